@@ -1,0 +1,49 @@
+"""Pure-Python loop version of the block forward, for tiny shapes only (test
+infrastructure).  Written element by element, without NumPy, so that it shares
+no vectorised indexing with ``oracle.block``; the tests compare the two and
+differentiate this one by central differences."""
+from __future__ import annotations
+
+import math
+from typing import List
+
+
+def silu(v: float) -> float:
+    return v / (1.0 + math.exp(-v))
+
+
+def block_fwd_loops(x: List[List[float]], gamma: List[float], A: List[List[float]],
+                    B: List[List[List[float]]], r: int, g: int, act: str, eps: float,
+                    D: int = 0) -> List[List[List[float]]]:
+    T, d = len(x), len(x[0])
+    D = D or d
+    ys = []
+    n_up = 1 if act == "swiglu" else g
+    for i in range(n_up):
+        ys.append([[0.0] * d for _ in range(T)])
+    for t in range(T):
+        acc = 0.0
+        for j in range(d):
+            acc += x[t][j] * x[t][j]
+        rstd = 1.0 / math.sqrt(acc / D + eps)
+        xn = [x[t][j] * rstd * gamma[j] for j in range(d)]
+        h = []
+        for c in range(g * r):
+            s = 0.0
+            for j in range(d):
+                s += xn[j] * A[j][c]
+            h.append(s)
+        zs = []
+        if act == "identity":
+            zs = [h[i * r:(i + 1) * r] for i in range(g)]
+        elif act == "silu":
+            zs = [[silu(v) for v in h[i * r:(i + 1) * r]] for i in range(g)]
+        elif act == "swiglu":
+            zs = [[silu(h[k]) * h[r + k] for k in range(r)]]
+        for i in range(n_up):
+            for j in range(d):
+                s = 0.0
+                for k in range(r):
+                    s += zs[i][k] * B[i][k][j]
+                ys[i][t][j] = s
+    return ys
