@@ -1,0 +1,140 @@
+/*
+ * lr_block.h -- C ABI of the fused low-rank bottleneck block for AMD MI355X (gfx950).
+ *
+ * The operation is the low-rank layer of BOOST ("BOOST: BOttleneck-Optimized
+ * Scalable Training Framework for Low-Rank Large Language Models"): a d x d
+ * weight replaced by a d x r "down" factor and an r x d "up" factor with a
+ * pointwise operation between them (technical summary, §1 and §2.1), preceded by
+ * RMSNorm whose statistic is computed locally and applied late (§2.2,
+ * Online-RMSNorm), with the down-projections that share one input concatenated
+ * into one weight and the up-projections run as a batch (§2.2, linear layer
+ * grouping), and a backward pass that keeps only the rank-r pre-activation and
+ * recomputes the pointwise operation from it (§2.2, low-rank activation
+ * checkpointing).
+ *
+ * Forward, for tokens t < T, hidden index j < d, rank index c < r:
+ *   rstd_t = (sum_j x_tj^2 / D + eps)^(-1/2)          D = d_norm, or d when d_norm == 0
+ *   h      = diag(rstd) . x . diag(gamma) . A          A = [A_0 | ... | A_{g-1}], [d, g*r]
+ *   z_i    = sigma(h_i)                                h_i = columns [i*r, (i+1)*r) of h
+ *            identity: z_i = h_i ; SiLU: z_i = h_i * sigmoid(h_i)
+ *            SwiGLU (g == 2): z_0 = SiLU(h_0) * h_1
+ *   y_i    = z_i . B_i                                 n_up = 1 for SwiGLU, else g
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major, dense, 16-byte aligned.
+ *     Arrays of pointers (B, y, dy, dB) are HOST arrays of n_up device pointers.
+ *   - The element type of x, gamma, A, B_i, y_i, h, dy_i and dx is dims->dtype
+ *     (LR_BF16: bfloat16 storage, fp32 accumulation; LR_F32: fp32).  sumsq,
+ *     rstd, the shard partial and all weight gradients are fp32.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no pointer after a call returns and holds no mutable global state.
+ *     Scratch space is the caller's workspace `ws` of at least
+ *     lr_block_workspace_size() bytes (256-byte aligned).
+ *   - All work is enqueued on `stream`; nothing synchronises.  Buffers must stay
+ *     alive until the stream has passed the call.
+ *   - Outputs must not alias inputs.  Gradients are overwritten, not accumulated.
+ *   - Shape and argument checks run on the host before any launch: a bad call
+ *     returns LR_EINVAL / LR_EUNSUPPORTED / LR_EWORKSPACE and launches nothing.
+ *     A failed launch returns LR_EHIP.  After an error the outputs are
+ *     undefined.  Nothing else crosses the ABI (no exceptions, no aborts).
+ *   - Supported shapes: T >= 0 (any value, ragged tails included); d and r
+ *     positive multiples of 64; 1 <= g <= 8; SwiGLU needs g == 2.
+ *   - Results are deterministic for a given device, shape and input (no
+ *     floating-point atomics).
+ */
+#ifndef LR_BLOCK_H
+#define LR_BLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LR_OK = 0,
+  LR_EINVAL = 1,        /* null / misaligned pointer, negative size, bad enum */
+  LR_EUNSUPPORTED = 2,  /* valid but unsupported shape or combination        */
+  LR_EWORKSPACE = 3,    /* workspace missing or smaller than required        */
+  LR_EHIP = 4           /* a HIP launch failed                               */
+} lr_status;
+
+typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
+
+typedef enum { LR_ACT_IDENTITY = 0, LR_ACT_SILU = 1, LR_ACT_SWIGLU = 2 } lr_act;
+
+typedef struct {
+  int64_t T;        /* tokens (b*s)                                              */
+  int64_t d;        /* hidden width held by this call (a shard's slice under TP) */
+  int64_t r;        /* rank                                                      */
+  int64_t g;        /* grouped down-projection branches                          */
+  int64_t d_norm;   /* width the RMS mean is taken over; 0 -> d                  */
+  float eps;        /* RMSNorm epsilon, inside the square root                   */
+  int32_t dtype;    /* lr_dtype                                                  */
+  int32_t act;      /* lr_act                                                    */
+} lr_dims;
+
+/* RMSNorm with the statistic computed in one pass (Online-RMSNorm, §2.2).
+ *   x [T, d], gamma [d] (dtype).  Each output may be NULL:
+ *   y [T, d] (dtype)  = x_tj * rstd_t * gamma_j
+ *   sumsq [T] (fp32)  = sum_j x_tj^2      (the additive local statistic)
+ *   rstd [T] (fp32)   = (sumsq_t / D + eps)^(-1/2)
+ * gamma may be NULL when y is NULL.  d must be a multiple of 8. */
+lr_status rmsnorm_online(const lr_dims* dims, const void* x, const void* gamma, void* y,
+                         float* sumsq, float* rstd, hipStream_t stream);
+
+/* Forward of the block.
+ *   x [T, d], gamma [d], A [d, g*r], B[i] [r, d]            (dtype)
+ *   y[i] [T, d]  for i < n_up                                (dtype)
+ *   h_save [T, g*r] (dtype): the rank-r pre-activation h, the only activation the
+ *   backward needs besides x (low-rank activation checkpointing, §2.2).  NULL for
+ *   inference. */
+lr_status lr_block_fwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                       const void* const* B, void* const* y, void* h_save,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the block from the saved pre-activation.
+ *   inputs : x, gamma, A, B[i] as in the forward; h_saved [T, g*r] (dtype), the
+ *            forward's h_save; dy[i] [T, d] (dtype), the upstream gradients.
+ *   outputs: dx [T, d] (dtype); dgamma [d], dA [d, g*r], dB[i] [r, d] (fp32).
+ * sigma is recomputed from h_saved; rstd is recomputed from x. */
+lr_status lr_block_bwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                       const void* const* B, const void* h_saved, const void* const* dy,
+                       void* dx, float* dgamma, float* dA, float* const* dB,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Shard seam of bottleneck-aware tensor parallelism (§2.1: the d x r factor runs
+ * row-parallel over this call's slice of d; §2.2: Online-RMSNorm keeps the local
+ * statistic and defers normalisation).  On one GPU the all-reduce of the partial
+ * and of sumsq that would sit between the two calls is the identity.
+ *   x [T, d] (this shard's columns), gamma [d], A [d, g*r] (this shard's rows)
+ *   partial [T, g*r] (fp32) = (x . diag(gamma)) . A        -- not normalised
+ *   sumsq [T] (fp32)        = sum_j x_tj^2 over this shard's columns */
+lr_status lr_down_partial(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                          float* partial, float* sumsq, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Second half of the seam: h = partial * (sumsq / D + eps)^(-1/2) with D =
+ * d_norm (the unsharded width), z = sigma(h), y[i] = z_i . B[i].
+ *   partial [T, g*r], sumsq [T] (fp32); B[i] [r, d] (this shard's columns);
+ *   y[i] [T, d]; h_save [T, g*r] or NULL (dtype). */
+lr_status lr_up_finish(const lr_dims* dims, const float* partial, const float* sumsq,
+                       const void* const* B, void* const* y, void* h_save,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes the calls above need for these dims:
+ *   backward == 0: lr_block_fwd, lr_down_partial and lr_up_finish;
+ *   backward != 0: lr_block_bwd.
+ * Returns 0 for dims that the calls would reject. */
+size_t lr_block_workspace_size(const lr_dims* dims, int backward);
+
+/* Static, NUL-terminated name of a status code. */
+const char* lr_status_str(lr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LR_BLOCK_H */

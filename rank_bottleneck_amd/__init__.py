@@ -1,0 +1,197 @@
+"""Python binding of the low-rank bottleneck block's HIP library (liblrblock.so).
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels; torch supplies device memory and the current stream.  There is no CPU
+or PyTorch fallback: if the library is missing or no GPU is present, the calls
+raise.
+
+The functions carry the C entry points' names (rmsnorm_online, lr_block_fwd,
+lr_block_bwd, lr_down_partial, lr_up_finish, lr_block_workspace_size,
+lr_status_str) and take torch tensors; ``fwd``/``bwd``/``down_partial``/
+``up_finish`` additionally allocate the outputs and the workspace.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch  # loads the HIP runtime first, so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblrblock.so")
+
+LR_OK, LR_EINVAL, LR_EUNSUPPORTED, LR_EWORKSPACE, LR_EHIP = range(5)
+LR_F32, LR_BF16 = 0, 1
+ACTS = {"identity": 0, "silu": 1, "swiglu": 2}
+DTYPES = {"f32": LR_F32, "bf16": LR_BF16}
+TORCH_DTYPE = {LR_F32: torch.float32, LR_BF16: torch.bfloat16}
+
+
+class LrDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("r", ctypes.c_int64), ("g", ctypes.c_int64),
+                ("d_norm", ctypes.c_int64), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("act", ctypes.c_int32)]
+
+
+class LrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {lr_status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_partial", "lr_up_finish",
+                "lr_block_workspace_size", "lr_status_str")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblrblock.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m rank_bottleneck_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32p, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
+    dims = ctypes.POINTER(LrDims)
+    lib.rmsnorm_online.argtypes = [dims, vp, vp, vp, vp, vp, vp]
+    lib.lr_block_fwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_bwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_down_partial.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_up_finish.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_partial", "lr_up_finish"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.lr_block_workspace_size.argtypes = [dims, ctypes.c_int]
+    lib.lr_block_workspace_size.restype = sz
+    lib.lr_status_str.argtypes = [ctypes.c_int]
+    lib.lr_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def lr_status_str(status: int) -> str:
+    return load().lr_status_str(int(status)).decode()
+
+
+def make_dims(T: int, d: int, r: int, g: int, act: str = "silu", dtype: str = "bf16", eps: float = 1e-6,
+              d_norm: int = 0) -> LrDims:
+    return LrDims(T, d, r, g, d_norm, eps, DTYPES[dtype], ACTS[act])
+
+
+def n_up(dims: LrDims) -> int:
+    return 1 if dims.act == ACTS["swiglu"] else dims.g
+
+
+def lr_block_workspace_size(dims: LrDims, backward: bool) -> int:
+    return int(load().lr_block_workspace_size(ctypes.byref(dims), 1 if backward else 0))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor is not on a GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_array(ts: Sequence[torch.Tensor]):
+    arr = (ctypes.c_void_p * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _stream(stream) -> Optional[int]:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn: str, st: int):
+    if st != LR_OK:
+        raise LrError(fn, st)
+
+
+def _ws_nbytes(ws: Optional[torch.Tensor]) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+# ----------------------------------------------------------------------- raw entry points
+def rmsnorm_online(dims: LrDims, x, gamma=None, y=None, sumsq=None, rstd=None, stream=None) -> None:
+    _check("rmsnorm_online", load().rmsnorm_online(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(y), _ptr(sumsq),
+                                                    _ptr(rstd), _stream(stream)))
+
+
+def lr_block_fwd(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, ws, stream=None) -> None:
+    _check("lr_block_fwd", load().lr_block_fwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
+                                                _ptr_array(y), _ptr(h_save), _ptr(ws), _ws_nbytes(ws),
+                                                _stream(stream)))
+
+
+def lr_block_bwd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, dy: Sequence, dx, dgamma, dA, dB: Sequence, ws,
+                 stream=None) -> None:
+    _check("lr_block_bwd", load().lr_block_bwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
+                                                _ptr(h_saved), _ptr_array(dy), _ptr(dx), _ptr(dgamma), _ptr(dA),
+                                                _ptr_array(dB), _ptr(ws), _ws_nbytes(ws), _stream(stream)))
+
+
+def lr_down_partial(dims: LrDims, x, gamma, A, partial, sumsq, ws, stream=None) -> None:
+    _check("lr_down_partial", load().lr_down_partial(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A),
+                                                      _ptr(partial), _ptr(sumsq), _ptr(ws), _ws_nbytes(ws),
+                                                      _stream(stream)))
+
+
+def lr_up_finish(dims: LrDims, partial, sumsq, B: Sequence, y: Sequence, h_save, ws, stream=None) -> None:
+    _check("lr_up_finish", load().lr_up_finish(ctypes.byref(dims), _ptr(partial), _ptr(sumsq), _ptr_array(B),
+                                                _ptr_array(y), _ptr(h_save), _ptr(ws), _ws_nbytes(ws),
+                                                _stream(stream)))
+
+
+# ----------------------------------------------------------------------- allocating helpers
+def workspace(dims: LrDims, backward: bool, device="cuda") -> torch.Tensor:
+    n = lr_block_workspace_size(dims, backward)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def fwd(dims: LrDims, x, gamma, A, B: Sequence, save_h: bool = True, ws=None, stream=None):
+    """Allocating forward: returns (list of y_i, h or None)."""
+    dt = TORCH_DTYPE[dims.dtype]
+    y = [torch.empty((dims.T, dims.d), dtype=dt, device=x.device) for _ in range(n_up(dims))]
+    h = torch.empty((dims.T, dims.g * dims.r), dtype=dt, device=x.device) if save_h else None
+    ws = workspace(dims, False, x.device) if ws is None else ws
+    lr_block_fwd(dims, x, gamma, A, B, y, h, ws, stream)
+    return y, h
+
+
+def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream=None):
+    """Allocating backward: returns dict(dx, dgamma, dA, dB)."""
+    dt = TORCH_DTYPE[dims.dtype]
+    dev = x.device
+    dx = torch.empty((dims.T, dims.d), dtype=dt, device=dev)
+    dgamma = torch.empty(dims.d, dtype=torch.float32, device=dev)
+    dA = torch.empty((dims.d, dims.g * dims.r), dtype=torch.float32, device=dev)
+    dB = [torch.empty((dims.r, dims.d), dtype=torch.float32, device=dev) for _ in range(n_up(dims))]
+    ws = workspace(dims, True, dev) if ws is None else ws
+    lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, ws, stream)
+    return {"dx": dx, "dgamma": dgamma, "dA": dA, "dB": dB}
+
+
+def down_partial(dims: LrDims, x, gamma, A, ws=None, stream=None):
+    dev = x.device
+    partial = torch.empty((dims.T, dims.g * dims.r), dtype=torch.float32, device=dev)
+    sumsq = torch.empty(dims.T, dtype=torch.float32, device=dev)
+    ws = workspace(dims, False, dev) if ws is None else ws
+    lr_down_partial(dims, x, gamma, A, partial, sumsq, ws, stream)
+    return partial, sumsq
+
+
+def up_finish(dims: LrDims, partial, sumsq, B: Sequence, save_h: bool = True, ws=None, stream=None):
+    dt = TORCH_DTYPE[dims.dtype]
+    dev = partial.device
+    y = [torch.empty((dims.T, dims.d), dtype=dt, device=dev) for _ in range(n_up(dims))]
+    h = torch.empty((dims.T, dims.g * dims.r), dtype=dt, device=dev) if save_h else None
+    ws = workspace(dims, False, dev) if ws is None else ws
+    lr_up_finish(dims, partial, sumsq, B, y, h, ws, stream)
+    return y, h

@@ -1,0 +1,266 @@
+// C ABI of the low-rank bottleneck block: host-side argument checks, workspace
+// carving and launch sequencing.  The operations are documented in lr_block.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/lr_block.h"
+#include "lr_kernels.h"
+
+namespace {
+
+using lr::bf16;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t esize(int32_t dt) { return dt == LR_BF16 ? 2 : 4; }
+inline int n_up_of(const lr_dims* d) { return d->act == LR_ACT_SWIGLU ? 1 : (int)d->g; }
+
+// Shape checks shared by every entry point.
+lr_status check_dims(const lr_dims* d) {
+  if (!d) return LR_EINVAL;
+  if (d->dtype != LR_F32 && d->dtype != LR_BF16) return LR_EINVAL;
+  if (d->act < LR_ACT_IDENTITY || d->act > LR_ACT_SWIGLU) return LR_EINVAL;
+  if (d->T < 0 || d->d <= 0 || d->r <= 0 || d->g <= 0 || d->d_norm < 0) return LR_EINVAL;
+  if (!(d->eps >= 0.f) || !isfinite(d->eps)) return LR_EINVAL;
+  if (d->d % 64 || d->r % 64) return LR_EUNSUPPORTED;
+  if (d->g > lr::MAX_G) return LR_EUNSUPPORTED;
+  if (d->act == LR_ACT_SWIGLU && d->g != 2) return LR_EUNSUPPORTED;
+  // every index below is formed in 64 bits; tile coordinates in 32 bits
+  if (d->T > (1ll << 30) || d->d > (1 << 20) || d->r * d->g > (1 << 20)) return LR_EUNSUPPORTED;
+  return LR_OK;
+}
+
+inline float inv_width(const lr_dims* d) { return 1.0f / (float)(d->d_norm ? d->d_norm : d->d); }
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = reinterpret_cast<P*>(base + off);
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+size_t fwd_ws(const lr_dims* d) {
+  const size_t es = esize(d->dtype), gr = (size_t)(d->g * d->r);
+  return align_up((size_t)d->d * gr * es) + align_up((size_t)d->T * gr * es);
+}
+
+template <typename E>
+size_t bwd_ws_t(const lr_dims* d) {
+  const size_t es = sizeof(E), gr = (size_t)(d->g * d->r), T = (size_t)d->T;
+  const int nsp = n_up_of(d) * lr::dz_nparts<E>((int)d->r);
+  const int ngp = lr::wgrad_nparts<E>((int)gr);
+  return align_up(T * 4) + align_up(T * gr * es) * 2 + align_up(T * nsp * 4) + align_up((size_t)d->d * ngp * 4);
+}
+
+size_t bwd_ws(const lr_dims* d) { return d->dtype == LR_BF16 ? bwd_ws_t<bf16>(d) : bwd_ws_t<float>(d); }
+
+inline lr_status hip_status(hipError_t e) { return e == hipSuccess ? LR_OK : LR_EHIP; }
+#define LR_TRY(expr)                              \
+  do {                                            \
+    hipError_t e_ = (expr);                       \
+    if (e_ != hipSuccess) return LR_EHIP;         \
+  } while (0)
+
+template <typename E>
+lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                   void* const* y, void* h_save, void* ws, hipStream_t s) {
+  const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
+  Carve cv{static_cast<char*>(ws)};
+  void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
+  void* z = cv.take<void>((size_t)T * gr * sizeof(E));
+  LR_TRY(lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
+  lr::DownArgs da{};
+  da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_BLOCK;
+  da.invD = inv_width(d); da.eps = d->eps; da.h = h_save; da.z = z;
+  LR_TRY(lr::launch_down<E>(da, s));
+  lr::UpArgs ua{};
+  const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
+  ua.z = z_is_h ? h_save : z;
+  ua.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
+  for (int i = 0; i < n_up; ++i) { ua.B[i] = B[i]; ua.y[i] = y[i]; }
+  ua.T = T; ua.d = D; ua.r = r;
+  LR_TRY(lr::launch_up<E>(ua, n_up, s));
+  return LR_OK;
+}
+
+template <typename E>
+lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                   const void* h, const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB,
+                   void* ws, hipStream_t s) {
+  const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
+  const int nsp = n_up * lr::dz_nparts<E>(r);
+  const int ngp = lr::wgrad_nparts<E>(gr);
+  Carve cv{static_cast<char*>(ws)};
+  float* rstd = cv.take<float>((size_t)T * 4);
+  void* dh = cv.take<void>((size_t)T * gr * sizeof(E));
+  void* z = cv.take<void>((size_t)T * gr * sizeof(E));
+  float* spart = cv.take<float>((size_t)T * nsp * 4);
+  float* gpart = cv.take<float>((size_t)D * ngp * 4);
+
+  LR_TRY(lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd, T, D, inv_width(d), d->eps, s));
+
+  lr::DzArgs za{};
+  for (int i = 0; i < n_up; ++i) { za.dy[i] = dy[i]; za.B[i] = B[i]; }
+  za.h = h; za.rstd = rstd; za.dh = dh; za.z = z; za.spart = spart; za.nspart = nsp;
+  za.T = T; za.d = D; za.r = r; za.g = g; za.act = d->act;
+  LR_TRY(lr::launch_dz<E>(za, n_up, s));
+
+  lr::WgradArgs wa{};
+  wa.z = d->act == LR_ACT_IDENTITY ? h : z;
+  wa.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
+  for (int i = 0; i < n_up; ++i) { wa.dy[i] = dy[i]; wa.dB[i] = dB[i]; }
+  wa.x = x; wa.dh = dh; wa.A = A; wa.gamma = gamma; wa.dA = dA; wa.gpart = gpart; wa.ngpart = ngp;
+  wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
+  LR_TRY(lr::launch_wgrad<E>(wa, s));
+  LR_TRY(lr::launch_sum_parts(gpart, dgamma, D, ngp, s));
+
+  lr::DxArgs xa{};
+  xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp;
+  xa.dx = dx; xa.T = T; xa.d = D; xa.r = r; xa.g = g; xa.invD = inv_width(d);
+  LR_TRY(lr::launch_dx<E>(xa, s));
+  return LR_OK;
+}
+
+template <typename E>
+lr_status partial_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, float* partial,
+                       float* sumsq, void* ws, hipStream_t s) {
+  const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r;
+  Carve cv{static_cast<char*>(ws)};
+  void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
+  LR_TRY(lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
+  lr::DownArgs da{};
+  da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_PARTIAL;
+  da.invD = inv_width(d); da.eps = d->eps; da.partial = partial; da.sumsq = sumsq;
+  LR_TRY(lr::launch_down<E>(da, s));
+  return LR_OK;
+}
+
+template <typename E>
+lr_status finish_impl(const lr_dims* d, const float* partial, const float* sumsq, const void* const* B,
+                      void* const* y, void* h_save, void* ws, hipStream_t s) {
+  const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
+  Carve cv{static_cast<char*>(ws)};
+  cv.take<void>((size_t)D * gr * sizeof(E));  // same layout as the forward
+  void* z = cv.take<void>((size_t)T * gr * sizeof(E));
+  LR_TRY(lr::launch_finish<E>(partial, sumsq, h_save, z, T, r, g, d->act, inv_width(d), d->eps, s));
+  lr::UpArgs ua{};
+  const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
+  ua.z = z_is_h ? h_save : z;
+  ua.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
+  for (int i = 0; i < n_up; ++i) { ua.B[i] = B[i]; ua.y[i] = y[i]; }
+  ua.T = T; ua.d = D; ua.r = r;
+  LR_TRY(lr::launch_up<E>(ua, n_up, s));
+  return LR_OK;
+}
+
+lr_status check_ptrs(const void* const* arr, int n) {
+  if (!arr) return LR_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (!arr[i] || !aligned16(arr[i])) return LR_EINVAL;
+  return LR_OK;
+}
+inline bool req(const void* p) { return p && aligned16(p); }
+inline bool opt(const void* p) { return !p || aligned16(p); }
+
+lr_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return LR_OK;
+  if (!ws || !aligned16(ws) || have < need) return LR_EWORKSPACE;
+  return LR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lr_status_str(lr_status st) {
+  switch (st) {
+    case LR_OK: return "LR_OK";
+    case LR_EINVAL: return "LR_EINVAL";
+    case LR_EUNSUPPORTED: return "LR_EUNSUPPORTED";
+    case LR_EWORKSPACE: return "LR_EWORKSPACE";
+    case LR_EHIP: return "LR_EHIP";
+  }
+  return "LR_UNKNOWN";
+}
+
+size_t lr_block_workspace_size(const lr_dims* d, int backward) {
+  if (check_dims(d) != LR_OK) return 0;
+  return backward ? bwd_ws(d) : fwd_ws(d);
+}
+
+lr_status rmsnorm_online(const lr_dims* d, const void* x, const void* gamma, void* y, float* sumsq, float* rstd,
+                         hipStream_t s) {
+  if (!d) return LR_EINVAL;
+  if (d->dtype != LR_F32 && d->dtype != LR_BF16) return LR_EINVAL;
+  if (d->T < 0 || d->d <= 0 || d->d_norm < 0 || !(d->eps >= 0.f) || !isfinite(d->eps)) return LR_EINVAL;
+  if (d->d % 8) return LR_EUNSUPPORTED;
+  if (d->T > (1ll << 30) || d->d > (1 << 24)) return LR_EUNSUPPORTED;
+  if (!req(x) || !opt(y) || !opt(sumsq) || !opt(rstd)) return LR_EINVAL;
+  if (y && !req(gamma)) return LR_EINVAL;
+  const int T = (int)d->T, D = (int)d->d;
+  hipError_t e = d->dtype == LR_BF16
+                     ? lr::launch_rms_stats<bf16>(x, gamma, y, sumsq, rstd, T, D, inv_width(d), d->eps, s)
+                     : lr::launch_rms_stats<float>(x, gamma, y, sumsq, rstd, T, D, inv_width(d), d->eps, s);
+  return hip_status(e);
+}
+
+lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                       void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req(x) || !req(gamma) || !req(A) || !opt(h_save)) return LR_EINVAL;
+  const int n_up = n_up_of(d);
+  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
+  if ((st = check_ptrs(reinterpret_cast<const void* const*>(y), n_up)) != LR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
+  return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, y, h_save, ws, s)
+                             : fwd_impl<float>(d, x, gamma, A, B, y, h_save, ws, s);
+}
+
+lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                       const void* h_saved, const void* const* dy, void* dx, float* dgamma, float* dA,
+                       float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req(x) || !req(gamma) || !req(A) || !req(h_saved) || !req(dx) || !req(dgamma) || !req(dA))
+    return LR_EINVAL;
+  const int n_up = n_up_of(d);
+  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
+  if ((st = check_ptrs(dy, n_up)) != LR_OK) return st;
+  if ((st = check_ptrs(reinterpret_cast<const void* const*>(dB), n_up)) != LR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, bwd_ws(d))) != LR_OK) return st;
+  return d->dtype == LR_BF16 ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, dy, dx, dgamma, dA, dB, ws, s)
+                             : bwd_impl<float>(d, x, gamma, A, B, h_saved, dy, dx, dgamma, dA, dB, ws, s);
+}
+
+lr_status lr_down_partial(const lr_dims* d, const void* x, const void* gamma, const void* A, float* partial,
+                          float* sumsq, void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req(x) || !req(gamma) || !req(A) || !req(partial) || !req(sumsq)) return LR_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
+  return d->dtype == LR_BF16 ? partial_impl<bf16>(d, x, gamma, A, partial, sumsq, ws, s)
+                             : partial_impl<float>(d, x, gamma, A, partial, sumsq, ws, s);
+}
+
+lr_status lr_up_finish(const lr_dims* d, const float* partial, const float* sumsq, const void* const* B,
+                       void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req(partial) || !req(sumsq) || !opt(h_save)) return LR_EINVAL;
+  const int n_up = n_up_of(d);
+  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
+  if ((st = check_ptrs(reinterpret_cast<const void* const*>(y), n_up)) != LR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
+  return d->dtype == LR_BF16 ? finish_impl<bf16>(d, partial, sumsq, B, y, h_save, ws, s)
+                             : finish_impl<float>(d, partial, sumsq, B, y, h_save, ws, s);
+}
+
+}  // extern "C"

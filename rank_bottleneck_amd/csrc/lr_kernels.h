@@ -1,0 +1,90 @@
+// Argument blocks and launchers shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lr {
+
+typedef __bf16 bf16;
+
+enum { ACT_IDENTITY = 0, ACT_SILU = 1, ACT_SWIGLU = 2 };
+enum { DOWN_BLOCK = 0, DOWN_PARTIAL = 1 };
+constexpr int MAX_G = 8;
+
+struct DownArgs {
+  const void* x;      // [T, d]
+  const void* Ap;     // [d, g*r], gamma folded in
+  int T, d, r, g, act, mode;
+  float invD, eps;
+  void* h;            // [T, g*r] or null
+  void* z;            // [T, g*r] (SwiGLU: [T, r]); identity: used only when h is null
+  float* partial;     // DOWN_PARTIAL: [T, g*r]
+  float* sumsq;       // DOWN_PARTIAL: [T]
+};
+
+struct UpArgs {
+  const void* z;      // A operand source; branch i starts at column i*r
+  int64_t ldz;
+  const void* B[MAX_G];
+  void* y[MAX_G];
+  int T, d, r;
+};
+
+struct DzArgs {
+  const void* dy[MAX_G];
+  const void* B[MAX_G];
+  const void* h;      // saved pre-activation [T, g*r]
+  const float* rstd;  // [T]
+  void* dh;           // [T, g*r]   rstd * dh
+  void* z;            // sigma(h): [T, g*r] (SiLU) or [T, r] (SwiGLU); unused for identity
+  float* spart;       // [T, nspart]
+  int nspart;
+  int T, d, r, g, act;
+};
+
+struct WgradArgs {
+  const void* z;      // sigma(h) source, branch i at column i*r, leading dim ldz
+  int64_t ldz;
+  const void* dy[MAX_G];
+  float* dB[MAX_G];
+  const void* x;
+  const void* dh;
+  const void* A;
+  const void* gamma;
+  float* dA;
+  float* gpart;       // [d, ngpart]
+  int ngpart;
+  int T, d, r, g, n_up;
+};
+
+struct DxArgs {
+  const void* dh;
+  const void* A;
+  const void* x;
+  const void* gamma;
+  const float* rstd;
+  const float* spart;
+  int nspart;
+  void* dx;
+  int T, d, r, g;
+  float invD;
+};
+
+template <typename E> hipError_t launch_rms_stats(const void* x, const void* gamma, void* y, float* sumsq,
+                                                  float* rstd, int T, int d, float invD, float eps, hipStream_t s);
+template <typename E> hipError_t launch_fold_gamma(const void* A, const void* gamma, void* Ap, int d, int n,
+                                                   hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+template <typename E> hipError_t launch_down(const DownArgs& a, hipStream_t s);
+template <typename E> hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s);
+template <typename E> hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, int T,
+                                               int r, int g, int act, float invD, float eps, hipStream_t s);
+template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
+template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
+template <typename E> hipError_t launch_dx(const DxArgs& a, hipStream_t s);
+hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, hipStream_t s);
+template <typename E> int dz_nparts(int r);
+template <typename E> int wgrad_nparts(int gr);
+
+}  // namespace lr

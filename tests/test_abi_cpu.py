@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/lr_block.h declares, sizes workspaces, and rejects bad arguments on the
+host (returning a status, launching nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_bottleneck_amd as rb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lr_block.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rb.LIB_PATH), reason="liblrblock.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(rb.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rb.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert rb.lr_status_str(rb.LR_OK) == "LR_OK"
+    assert rb.lr_status_str(rb.LR_EWORKSPACE) == "LR_EWORKSPACE"
+    assert rb.lr_status_str(99) == "LR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    d = rb.make_dims(16384, 4096, 1024, 3, "silu", "bf16")
+    f, b = rb.lr_block_workspace_size(d, False), rb.lr_block_workspace_size(d, True)
+    # forward: gamma-folded A plus sigma(h); backward: rstd, dh', sigma(h), row partials
+    assert f >= 4096 * 3072 * 2 + 16384 * 3072 * 2
+    assert b >= 16384 * 4 + 2 * 16384 * 3072 * 2
+    assert rb.lr_block_workspace_size(rb.make_dims(16, 100, 64, 1), False) == 0   # d % 64 != 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its host checks
+
+
+def _call_fwd(dims, x=FAKE, gamma=FAKE, A=FAKE, nB=None, h=None, ws=FAKE, ws_bytes=1 << 40):
+    lib = rb.load()
+    n = rb.n_up(dims) if nB is None else nB
+    B = (ctypes.c_void_p * max(n, 1))(*([FAKE] * n))
+    y = (ctypes.c_void_p * max(n, 1))(*([FAKE] * n))
+    return lib.lr_block_fwd(ctypes.byref(dims), x, gamma, A, B, y, h, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rb.LR_EINVAL),
+    (dict(d=100), rb.LR_EUNSUPPORTED),
+    (dict(r=96), rb.LR_EUNSUPPORTED),
+    (dict(g=9), rb.LR_EUNSUPPORTED),
+    (dict(g=3, act="swiglu"), rb.LR_EUNSUPPORTED),
+    (dict(eps=float("nan")), rb.LR_EINVAL),
+    (dict(eps=-1.0), rb.LR_EINVAL),
+])
+def test_bad_dims_rejected(kw, status):
+    args = dict(T=64, d=128, r=64, g=1, act="silu", dtype="bf16", eps=1e-6)
+    args.update(kw)
+    dims = rb.make_dims(**args)
+    assert _call_fwd(dims) == status
+
+
+def test_bad_enums_rejected():
+    dims = rb.make_dims(64, 128, 64, 1)
+    dims.dtype = 7
+    assert _call_fwd(dims) == rb.LR_EINVAL
+    dims = rb.make_dims(64, 128, 64, 1)
+    dims.act = 5
+    assert _call_fwd(dims) == rb.LR_EINVAL
+    assert rb.load().lr_block_fwd(None, FAKE, FAKE, FAKE, None, None, None, FAKE, 1, None) == rb.LR_EINVAL
+
+
+def test_bad_pointers_rejected():
+    dims = rb.make_dims(64, 128, 64, 2, "identity")
+    assert _call_fwd(dims, x=None) == rb.LR_EINVAL
+    assert _call_fwd(dims, A=FAKE + 2) == rb.LR_EINVAL           # misaligned
+    assert _call_fwd(dims, h=FAKE + 8) == rb.LR_EINVAL
+    assert _call_fwd(dims, nB=1) == rb.LR_EINVAL                 # second B pointer null
+
+
+def test_workspace_checked():
+    dims = rb.make_dims(64, 128, 64, 1)
+    need = rb.lr_block_workspace_size(dims, False)
+    assert _call_fwd(dims, ws=None) == rb.LR_EWORKSPACE
+    assert _call_fwd(dims, ws_bytes=need - 1) == rb.LR_EWORKSPACE
+    lib = rb.load()
+    z = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 1)(FAKE)
+    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, arr, FAKE, FAKE, FAKE, arr,
+                            FAKE, rb.lr_block_workspace_size(dims, True) - 1, None) == rb.LR_EWORKSPACE
+    assert lib.lr_down_partial(ctypes.byref(dims), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == rb.LR_EINVAL
+    assert lib.lr_up_finish(ctypes.byref(dims), FAKE, FAKE, arr, arr, None, None, 0, None) == rb.LR_EWORKSPACE
+
+
+def test_rmsnorm_arguments():
+    lib = rb.load()
+    dims = rb.make_dims(8, 12, 64, 1)
+    assert lib.rmsnorm_online(ctypes.byref(dims), FAKE, FAKE, None, None, None, None) == rb.LR_EUNSUPPORTED
+    dims = rb.make_dims(8, 16, 64, 1)
+    assert lib.rmsnorm_online(ctypes.byref(dims), None, FAKE, None, None, None, None) == rb.LR_EINVAL
+    assert lib.rmsnorm_online(ctypes.byref(dims), FAKE, None, FAKE, None, None, None) == rb.LR_EINVAL

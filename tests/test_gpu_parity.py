@@ -1,0 +1,266 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases run the oracle on everything and span several 256 x 256 tiles with
+ragged tails in T and in the rank dimension; full-size cases use the shapes and
+launch configuration the benchmark times and compare sampled rows (rows are
+independent in the forward and in dx) and, where affordable, whole gradients.
+Tolerances: bf16 max|e| <= 1e-2 max|ref| and ||e||_F <= 5e-3 ||ref||_F; fp32 1e-5.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_bottleneck_amd as rb
+from workloads import WORKLOADS, Workload, make_inputs
+
+from util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, file=sys.stderr, flush=True)
+
+
+def _dims(wl: Workload, T=None):
+    return rb.make_dims(wl.T if T is None else T, wl.d, wl.r, wl.g, wl.act, wl.dtype, wl.eps, wl.d_norm)
+
+
+def _run_fwd(wl, inp, save_h=True):
+    dims = _dims(wl, inp.x.shape[0])
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    y, h = rb.fwd(dims, x, gamma, A, B, save_h=save_h)
+    torch.cuda.synchronize()
+    return dims, (x, gamma, A, B), y, h
+
+
+SMALL = [
+    Workload("tiny_f32_silu", 128, 256, 64, 1, "silu", "f32"),
+    Workload("f32_ragged", 300, 320, 128, 3, "silu", "f32"),
+    Workload("f32_swiglu", 200, 256, 192, 2, "swiglu", "f32"),
+    Workload("bf16_identity", 700, 512, 320, 3, "identity", "bf16"),
+    Workload("bf16_silu", 555, 768, 192, 3, "silu", "bf16"),
+    Workload("bf16_swiglu", 777, 1024, 256, 2, "swiglu", "bf16"),
+    Workload("bf16_g1_r64", 1000, 512, 64, 1, "silu", "bf16"),
+    Workload("bf16_dnorm", 333, 384, 128, 2, "silu", "bf16", d_norm=1536),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_block_forward_backward_small(wl):
+    _say("small", wl)
+    inp = make_inputs(wl, seed=1)
+    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    for i, yi in enumerate(y):
+        assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+    dy = [dev(t) for t in inp.dy]
+    g = rb.bwd(dims, x, gamma, A, B, h, dy)
+    torch.cuda.synchronize()
+    rb_ = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(g["dx"]), rb_["dx"], wl.dtype, "dx")
+    assert_close(host(g["dgamma"]), rb_["dgamma"], wl.dtype, "dgamma")
+    assert_close(host(g["dA"]), rb_["dA"], wl.dtype, "dA")
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
+
+
+@pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5]], ids=lambda w: w.name)
+def test_inference_forward_without_checkpoint(wl):
+    inp = make_inputs(wl, seed=2, with_dy=False)
+    _, _, y, h = _run_fwd(wl, inp, save_h=False)
+    assert h is None
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    for i, yi in enumerate(y):
+        assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rmsnorm_online(dtype):
+    wl = Workload("rms", 1111, 4096, 64, 1, "silu", dtype)
+    inp = make_inputs(wl, seed=3, with_dy=False)
+    dims = _dims(wl)
+    x, gamma = dev(inp.x), dev(inp.gamma)
+    y = torch.empty_like(x)
+    ss = torch.empty(wl.T, dtype=torch.float32, device="cuda")
+    rs = torch.empty_like(ss)
+    rb.rmsnorm_online(dims, x, gamma, y, ss, rs)
+    torch.cuda.synchronize()
+    ry, rss, rrs = oracle.rmsnorm(inp.x.v, inp.gamma.v, wl.eps)
+    assert_close(host(ss), rss, "f32", "sumsq")
+    assert_close(host(rs), rrs, "f32", "rstd")
+    assert_close(host(y), ry, dtype, "y")
+
+
+@pytest.mark.parametrize("act,g", [("silu", 1), ("identity", 3), ("swiglu", 2)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shard_seam_small(act, g, dtype):
+    """Partial + finish on one shard equals the oracle's seam; summing four
+    shards' partials and finishing equals the unsharded block."""
+    T, dl, r, tp = 500, 256, 128, 4
+    wl = Workload("seam", T, dl * tp, r, g, act, dtype)
+    inp = make_inputs(wl, seed=4, with_dy=False)
+    full = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], r, g, act, wl.eps)
+    parts, sss = [], []
+    for s in range(tp):
+        c = slice(s * dl, (s + 1) * dl)
+        dims = rb.make_dims(T, dl, r, g, act, dtype, wl.eps, d_norm=dl * tp)
+        x = dev(inp.x.store[:, c].copy() if dtype == "bf16" else inp.x.store[:, c])
+        gm = dev(inp.gamma.store[c].copy())
+        As = dev(inp.A.store[c, :].copy())
+        p, ss = rb.down_partial(dims, x, gm, As)
+        torch.cuda.synchronize()
+        rp, rss = oracle.down_partial(inp.x.v[:, c], inp.gamma.v[c], inp.A.v[c, :])
+        assert_close(host(p), rp, dtype, "partial")
+        assert_close(host(ss), rss, "f32", "sumsq")
+        parts.append(p)
+        sss.append(ss)
+    P = torch.stack(parts).sum(0).contiguous()   # stands in for the all-reduce
+    SS = torch.stack(sss).sum(0).contiguous()
+    for s in range(tp):
+        c = slice(s * dl, (s + 1) * dl)
+        dims = rb.make_dims(T, dl, r, g, act, dtype, wl.eps, d_norm=dl * tp)
+        Bs = [dev(b.store[:, c].copy()) for b in inp.B]
+        y, h = rb.up_finish(dims, P, SS, Bs)
+        torch.cuda.synchronize()
+        ref = oracle.up_finish(host(P), host(SS), [b.v[:, c] for b in inp.B], r, g, act, wl.eps, dl * tp)
+        assert_close(host(h), ref["h"], dtype, "h")
+        for i, yi in enumerate(y):
+            assert_close(host(yi), ref["y"][i], dtype, "y (seam)")
+            assert_close(host(yi), full["y"][i][:, c], dtype, "y (vs unsharded)")
+
+
+def test_exact_selection_case_bitwise():
+    """x in {+-1}, eps = 0, gamma = 1, one-hot A, B = A^T: the GPU output is
+    exact (identity) and equals the rounded SiLU(+-1) (SiLU), in fp32 and bf16."""
+    T, d, r, g = 300, 256, 64, 2
+    rng = np.random.default_rng(0)
+    x = np.where(rng.random((T, d)) < 0.5, -1.0, 1.0)
+    sel = rng.permutation(d)[: g * r]
+    A = np.zeros((d, g * r))
+    A[sel, np.arange(g * r)] = 1.0
+    B = [A[:, i * r:(i + 1) * r].T.copy() for i in range(g)]
+    for dtype, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        for act in ("identity", "silu"):
+            dims = rb.make_dims(T, d, r, g, act, dtype, 0.0)
+            t = lambda a: torch.tensor(a, dtype=tdt, device="cuda").contiguous()
+            y, _ = rb.fwd(dims, t(x), t(np.ones(d)), t(A), [t(b) for b in B])
+            torch.cuda.synchronize()
+            ref = oracle.block_fwd(x, np.ones(d), A, B, r, g, act, 0.0)
+            for i in range(g):
+                exp = torch.tensor(ref["y"][i], dtype=tdt).double().numpy()  # rounded once to the storage type
+                got = host(y[i])
+                if act == "identity":
+                    assert np.array_equal(got, exp), (dtype, act, i)
+                else:
+                    # SiLU(+-1) through the device exp: within 2 ulp of fp32, exact after bf16 rounding
+                    tol = 0.0 if dtype == "bf16" else 2.5e-7
+                    assert np.max(np.abs(got - exp)) <= tol, (dtype, act, i, np.max(np.abs(got - exp)))
+
+
+def test_deterministic_rerun():
+    wl = SMALL[4]
+    inp = make_inputs(wl, seed=5)
+    dims, (x, gamma, A, B), y1, h1 = _run_fwd(wl, inp)
+    y2, h2 = rb.fwd(dims, x, gamma, A, B)
+    dy = [dev(t) for t in inp.dy]
+    g1 = rb.bwd(dims, x, gamma, A, B, h1, dy)
+    g2 = rb.bwd(dims, x, gamma, A, B, h1, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and all(torch.equal(a, b) for a, b in zip(y1, y2))
+    for k in ("dx", "dgamma", "dA"):
+        assert torch.equal(g1[k], g2[k]), k
+    assert all(torch.equal(a, b) for a, b in zip(g1["dB"], g2["dB"]))
+
+
+def test_empty_batch():
+    """T = 0: no rows to produce; the weight gradients are sums over no tokens, so zero."""
+    wl = Workload("empty", 0, 256, 64, 3, "silu", "bf16")
+    dims = _dims(wl)
+    dt = torch.bfloat16
+    x = torch.empty((0, 256), dtype=dt, device="cuda")
+    gamma = torch.ones(256, dtype=dt, device="cuda")
+    A = torch.randn(256, 192, device="cuda").to(dt)
+    B = [torch.randn(64, 256, device="cuda").to(dt) for _ in range(3)]
+    y, h = rb.fwd(dims, x, gamma, A, B)
+    g = rb.bwd(dims, x, gamma, A, B, h, [torch.empty((0, 256), dtype=dt, device="cuda")] * 3)
+    torch.cuda.synchronize()
+    assert y[0].shape == (0, 256) and h.shape == (0, 192)
+    assert float(g["dA"].abs().max()) == 0.0 and float(g["dgamma"].abs().max()) == 0.0
+    assert all(float(t.abs().max()) == 0.0 for t in g["dB"])
+
+
+def test_status_on_bad_call_launches_nothing():
+    dims = rb.make_dims(64, 100, 64, 1)
+    x = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rb.LrError) as e:
+        rb.lr_block_fwd(dims, x, x, x, [x], [x], None, x)
+    assert e.value.status == rb.LR_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ full-size shapes
+FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r256"]
+
+
+def _sample_rows(T, n=192, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(T, n - 8, replace=False), np.arange(T - 8, T)]))
+    return rows
+
+
+@pytest.mark.parametrize("name", FULL_FWD)
+def test_full_size_forward_sampled_rows(name):
+    wl = WORKLOADS[name]
+    _say("full fwd", wl)
+    inp = make_inputs(wl, seed=0, with_dy=False)
+    _, _, y, h = _run_fwd(wl, inp)
+    rows = _sample_rows(wl.T)
+    ref = oracle.block_fwd(inp.x.v[rows], inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act,
+                           wl.eps, wl.D)
+    assert_close(host(h[torch.as_tensor(rows, device="cuda")]), ref["h"], wl.dtype, "h rows")
+    for i, yi in enumerate(y):
+        assert_close(host(yi[torch.as_tensor(rows, device="cuda")]), ref["y"][i], wl.dtype, f"y{i} rows")
+
+
+def test_full_size_btp_shard_seam():
+    wl = WORKLOADS["btp_shard"]
+    _say("full seam", wl)
+    inp = make_inputs(wl, seed=0, with_dy=False)
+    dims = _dims(wl)
+    p, ss = rb.down_partial(dims, dev(inp.x), dev(inp.gamma), dev(inp.A))
+    y, h = rb.up_finish(dims, p, ss, [dev(b) for b in inp.B])
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl.T)
+    rp, rss = oracle.down_partial(inp.x.v[rows], inp.gamma.v, inp.A.v)
+    ri = torch.as_tensor(rows, device="cuda")
+    assert_close(host(p[ri]), rp, wl.dtype, "partial rows")
+    assert_close(host(ss[ri]), rss, "f32", "sumsq rows")
+    ref = oracle.up_finish(rp, rss, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(y[0][ri]), ref["y"][0], wl.dtype, "y rows")
+
+
+@pytest.mark.parametrize("name", ["qkv_silu_ckpt", "swiglu_mlp", "qkv_identity"])
+def test_full_size_backward(name):
+    """Whole-tensor comparison of every gradient at the full shape (the oracle's
+    float64 products over all T take seconds on the host)."""
+    wl = WORKLOADS[name]
+    _say("full bwd", wl)
+    inp = make_inputs(wl, seed=0)
+    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    del y
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy])
+    torch.cuda.synchronize()
+    ref = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(g["dx"]), ref["dx"], wl.dtype, "dx")
+    assert_close(host(g["dgamma"]), ref["dgamma"], wl.dtype, "dgamma")
+    assert_close(host(g["dA"]), ref["dA"], wl.dtype, "dA")
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), ref["dB"][i], wl.dtype, f"dB{i}")
