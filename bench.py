@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the low-rank bottleneck block on one MI355X.
+
+One step = one forward (with the rank-r checkpoint) + one backward of the block
+over one batch of synthetic, seeded input already resident in HBM, through the
+C ABI (the shard workload "btp_shard" times its two seam calls instead).  Prints
+ONE JSON line: block fwd+bwd TFLOP/s (algorithmic GEMM FLOPs, elementwise work
+not counted), tokens/s, % of the bf16 MFMA peak, the roofline of the dominant
+kernel (timed with HIP events on its launch stream over the timed region) and
+the CPU oracle timed on a bounded row sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "low-rank block fwd+bwd TFLOP/s (bf16) and % MFMA peak; tokens/s per block"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (published)
+PEAK_GBS = 8000.0                                # MI355X HBM3E (published)
+KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
+                  "rank_bottleneck_amd/csrc/lr_kernels.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_work(wl, name: str):
+    """Algorithmic (flops, HBM bytes) of one launch of kernel `name`: every
+    operand read once and every result written once; GEMM flops only."""
+    T, d, r, g, nu = wl.T, wl.d, wl.r, wl.g, wl.n_up
+    e = 2 if wl.dtype == "bf16" else 4
+    gr = g * r
+    zcols = 0 if wl.act == "identity" else (r if wl.act == "swiglu" else gr)
+    if name == "down":
+        if wl.seam:   # fp32 partial + sumsq
+            return 2.0 * T * d * gr, e * (T * d + d * gr) + 4 * (T * gr + T)
+        return 2.0 * T * d * gr, e * (T * d + d * gr + T * gr + T * zcols)
+    if name == "up":
+        return 2.0 * T * r * d * nu, e * (T * r * nu + nu * r * d + nu * T * d)
+    if name == "dz":
+        return 2.0 * T * d * r * nu, e * (nu * T * d + nu * r * d + T * gr + T * gr + T * zcols) + 4 * T
+    if name == "wgrad":
+        return (2.0 * T * r * d * nu + 2.0 * T * d * gr,
+                e * (T * (zcols or gr) + nu * T * d + T * d + T * gr + d * gr) + 4 * (d * gr + nu * r * d))
+    if name == "dx":
+        return 2.0 * T * gr * d, e * (T * gr + d * gr + 2 * T * d) + 4 * T
+    if name == "fold_gamma":
+        return 0.0, e * (2 * d * gr + d)
+    if name == "rms_stats":
+        return 0.0, e * T * d + 4 * T
+    if name == "finish":
+        return 0.0, 4 * (T * gr + T) + e * (T * gr + T * zcols)
+    return 0.0, 0.0
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """The oracle (float64 NumPy, as it stands) on a row sample of the same
+    workload, on the host cores; reported in the metric's unit."""
+    import oracle
+    from workloads import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+
+    def run(rows):
+        inp = make_inputs(wl, seed=0, rows=rows)
+        args = (inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B])
+        t0 = time.perf_counter()
+        if wl.seam:
+            p, ss = oracle.down_partial(*args[:3])
+            oracle.up_finish(p, ss, args[3], wl.r, wl.g, wl.act, wl.eps, wl.D)
+        else:
+            oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D)
+            oracle.block_bwd(*args, [t.v for t in inp.dy], wl.r, wl.g, wl.act, wl.eps, wl.D)
+        return time.perf_counter() - t0
+
+    probe = min(wl.T, 256)
+    tp = run(probe)
+    rows = int(min(wl.T, max(probe, probe * budget_s / max(tp, 1e-3))))
+    rows = max(probe, rows // 64 * 64) if rows < wl.T else wl.T
+    log(f"cpu oracle: probe {probe} rows {tp:.2f}s -> sample {rows} rows")
+    t = run(rows)
+    sub = wl.replace(T=rows)
+    flops = sub.fwd_flops() + (0 if wl.seam else sub.bwd_flops())
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy fwd+bwd, {t:.1f} s",
+            "tokens_per_s": rows / t}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qkv_identity")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work on the host")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the block's hot path runs on one GPU's shard and this build has no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_bottleneck_amd as rb
+    from workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    log("workload", wl)
+    torch.cuda.set_device(0)
+    inp = make_inputs(wl, seed=0, with_dy=not wl.seam)
+
+    def dev(t):
+        if t.dtype == "bf16":
+            return torch.from_numpy(t.store.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(t.store).cuda()
+
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    dy = None if wl.seam else [dev(t) for t in inp.dy]
+    del inp
+    dims = rb.make_dims(wl.T, wl.d, wl.r, wl.g, wl.act, wl.dtype, wl.eps, wl.d_norm)
+    dt = rb.TORCH_DTYPE[dims.dtype]
+    gr, nu = wl.g * wl.r, wl.n_up
+    y = [torch.empty((wl.T, wl.d), dtype=dt, device="cuda") for _ in range(nu)]
+    h = torch.empty((wl.T, gr), dtype=dt, device="cuda")
+    wsf = rb.workspace(dims, False)
+    if wl.seam:
+        partial = torch.empty((wl.T, gr), dtype=torch.float32, device="cuda")
+        sumsq = torch.empty(wl.T, dtype=torch.float32, device="cuda")
+
+        def step():
+            rb.lr_down_partial(dims, x, gamma, A, partial, sumsq, wsf)
+            rb.lr_up_finish(dims, partial, sumsq, B, y, h, wsf)
+        flops = wl.fwd_flops()
+    else:
+        wsb = rb.workspace(dims, True)
+        dx = torch.empty((wl.T, wl.d), dtype=dt, device="cuda")
+        dgamma = torch.empty(wl.d, dtype=torch.float32, device="cuda")
+        dA = torch.empty((wl.d, gr), dtype=torch.float32, device="cuda")
+        dB = [torch.empty((wl.r, wl.d), dtype=torch.float32, device="cuda") for _ in range(nu)]
+
+        def step():
+            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, wsf)
+            rb.lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, wsb)
+        flops = wl.fwd_flops() + wl.bwd_flops()
+
+    # warm-up; the last warm-up step is traced per kernel to find the dominant one
+    for i in range(max(args.warmup - 1, 0)):
+        step()
+    rb.lr_trace_begin(None, 64)
+    step()
+    per_kernel = {}
+    for i in range(rb.lr_trace_count()):
+        name, ms = rb.lr_trace_elapsed(i)
+        per_kernel[name] = per_kernel.get(name, 0.0) + ms
+    rb.lr_trace_end()
+    torch.cuda.synchronize()
+    dominant = max(per_kernel, key=per_kernel.get)
+    log("warm-up kernel ms:", {k: round(v, 4) for k, v in per_kernel.items()}, "dominant:", dominant)
+
+    # timed region: K steps; the dominant kernel is bracketed by HIP events on its stream
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rb.lr_trace_begin(dominant, args.steps * 8)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    dom_ms = [rb.lr_trace_elapsed(i)[1] for i in range(rb.lr_trace_count())]
+    rb.lr_trace_end()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)")
+
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    dom_avg = float(np.mean(dom_ms)) if dom_ms else float("nan")
+    kf, kb = kernel_work(wl, dominant)
+    ridge = PEAK_TFLOPS[wl.dtype] * 1e12 / (PEAK_GBS * 1e9)
+    if kf > 0 and kf / max(kb, 1) > ridge:
+        roof = {"bound": "mfma", "achieved": kf / (dom_avg * 1e-3) / 1e12, "peak": PEAK_TFLOPS[wl.dtype],
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kb / (dom_avg * 1e-3) / 1e9, "peak": PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dominant
+    roof["kernel_ms"] = dom_avg
+    roof["algorithmic_flops"] = kf
+    roof["algorithmic_bytes"] = kb
+    roof["traffic"] = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath)).get(f"{wl.name}/{dominant}")
+        if rec and rec.get("source_hash") == source_hash():
+            roof["traffic"] = rec["bytes_per_launch"]
+
+    out = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+           "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "r": wl.r, "g": wl.g, "act": wl.act,
+                      "d_norm": wl.D, "step": "seam fwd" if wl.seam else "fwd+bwd", "parallelism": "none (1 GPU)"},
+           "tokens_per_s": wl.T / (ms_step * 1e-3),
+           "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wl.dtype],
+           "kernel_ms_warmup_step": per_kernel,
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,6 +23,7 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers, row-major, dense, 16-byte aligned.
  *     Arrays of pointers (B, y, dy, dB) are HOST arrays of n_up device pointers.
+ *     Pointers to [T, ...] buffers may be NULL when T == 0.
  *   - The element type of x, gamma, A, B_i, y_i, h, dy_i and dx is dims->dtype
  *     (LR_BF16: bfloat16 storage, fp32 accumulation; LR_F32: fp32).  sumsq,
  *     rstd, the shard partial and all weight gradients are fp32.
@@ -129,6 +130,24 @@ lr_status lr_up_finish(const lr_dims* dims, const float* partial, const float* s
  *   backward != 0: lr_block_bwd.
  * Returns 0 for dims that the calls would reject. */
 size_t lr_block_workspace_size(const lr_dims* dims, int backward);
+
+/* Kernel timing for benchmarks (not part of the block's arithmetic).
+ * Between lr_trace_begin and lr_trace_end, every kernel that an entry point
+ * launches from the CALLING THREAD whose name matches `kernel` (NULL: all) is
+ * bracketed by two hipEvents recorded on the launch stream, up to
+ * `max_launches` launches.  Kernel names: "fold_gamma", "down", "up", "finish",
+ * "rms_stats", "dz", "wgrad", "sum_parts", "dx".  This per-thread trace is the
+ * only state the library keeps between calls; it owns its events.
+ *   lr_trace_begin: LR_EINVAL if max_launches < 1 or a trace is already active,
+ *                   LR_EHIP if events cannot be created.
+ *   lr_trace_count: launches recorded so far (0 when no trace is active).
+ *   lr_trace_elapsed: waits for launch i's end event; writes its kernel name
+ *                   (static string) and duration in milliseconds.
+ *   lr_trace_end:   destroys the events (the stream must have passed them). */
+lr_status lr_trace_begin(const char* kernel, int max_launches);
+int lr_trace_count(void);
+lr_status lr_trace_elapsed(int i, const char** kernel, float* ms);
+lr_status lr_trace_end(void);
 
 /* Static, NUL-terminated name of a status code. */
 const char* lr_status_str(lr_status status);

@@ -42,7 +42,8 @@ class LrError(RuntimeError):
 
 _lib = None
 ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_partial", "lr_up_finish",
-                "lr_block_workspace_size", "lr_status_str")
+                "lr_block_workspace_size", "lr_status_str", "lr_trace_begin", "lr_trace_count",
+                "lr_trace_elapsed", "lr_trace_end")
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -66,6 +67,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lr_block_workspace_size.restype = sz
     lib.lr_status_str.argtypes = [ctypes.c_int]
     lib.lr_status_str.restype = ctypes.c_char_p
+    lib.lr_trace_begin.argtypes = [ctypes.c_char_p, ctypes.c_int]
+    lib.lr_trace_begin.restype = ctypes.c_int
+    lib.lr_trace_count.argtypes = []
+    lib.lr_trace_count.restype = ctypes.c_int
+    lib.lr_trace_elapsed.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+    lib.lr_trace_elapsed.restype = ctypes.c_int
+    lib.lr_trace_end.argtypes = []
+    lib.lr_trace_end.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -147,6 +156,25 @@ def lr_up_finish(dims: LrDims, partial, sumsq, B: Sequence, y: Sequence, h_save,
     _check("lr_up_finish", load().lr_up_finish(ctypes.byref(dims), _ptr(partial), _ptr(sumsq), _ptr_array(B),
                                                 _ptr_array(y), _ptr(h_save), _ptr(ws), _ws_nbytes(ws),
                                                 _stream(stream)))
+
+
+def lr_trace_begin(kernel: Optional[str] = None, max_launches: int = 1024) -> None:
+    _check("lr_trace_begin", load().lr_trace_begin(None if kernel is None else kernel.encode(), max_launches))
+
+
+def lr_trace_count() -> int:
+    return int(load().lr_trace_count())
+
+
+def lr_trace_elapsed(i: int):
+    """(kernel name, milliseconds) of traced launch i; waits for it to finish."""
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    _check("lr_trace_elapsed", load().lr_trace_elapsed(i, ctypes.byref(name), ctypes.byref(ms)))
+    return name.value.decode(), float(ms.value)
+
+
+def lr_trace_end() -> None:
+    _check("lr_trace_end", load().lr_trace_end())
 
 
 # ----------------------------------------------------------------------- allocating helpers

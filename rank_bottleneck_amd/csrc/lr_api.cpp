@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <new>
+
 #include "../../include/lr_block.h"
 #include "lr_kernels.h"
 
@@ -62,10 +64,37 @@ size_t bwd_ws_t(const lr_dims* d) {
 size_t bwd_ws(const lr_dims* d) { return d->dtype == LR_BF16 ? bwd_ws_t<bf16>(d) : bwd_ws_t<float>(d); }
 
 inline lr_status hip_status(hipError_t e) { return e == hipSuccess ? LR_OK : LR_EHIP; }
-#define LR_TRY(expr)                              \
-  do {                                            \
-    hipError_t e_ = (expr);                       \
-    if (e_ != hipSuccess) return LR_EHIP;         \
+
+// Per-thread launch trace (lr_trace_*): event pairs around matching launches.
+struct Trace {
+  bool on = false;
+  char filter[32] = {0};
+  int cap = 0, n = 0;
+  hipEvent_t* ev = nullptr;
+  const char** names = nullptr;
+};
+thread_local Trace g_trace;
+
+struct TraceGuard {
+  hipStream_t s;
+  int slot = -1;
+  TraceGuard(const char* name, hipStream_t st) : s(st) {
+    Trace& t = g_trace;
+    if (!t.on || t.n >= t.cap || (t.filter[0] && strcmp(t.filter, name) != 0)) return;
+    slot = t.n++;
+    t.names[slot] = name;
+    hipEventRecord(t.ev[2 * slot], s);
+  }
+  ~TraceGuard() {
+    if (slot >= 0) hipEventRecord(g_trace.ev[2 * slot + 1], s);
+  }
+};
+
+#define LR_LAUNCH(name, s, expr)          \
+  do {                                    \
+    TraceGuard tg_(name, s);              \
+    hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return LR_EHIP; \
   } while (0)
 
 template <typename E>
@@ -75,18 +104,18 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  LR_TRY(lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
+  LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
   lr::DownArgs da{};
   da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_BLOCK;
   da.invD = inv_width(d); da.eps = d->eps; da.h = h_save; da.z = z;
-  LR_TRY(lr::launch_down<E>(da, s));
+  LR_LAUNCH("down", s, lr::launch_down<E>(da, s));
   lr::UpArgs ua{};
   const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
   ua.z = z_is_h ? h_save : z;
   ua.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
   for (int i = 0; i < n_up; ++i) { ua.B[i] = B[i]; ua.y[i] = y[i]; }
   ua.T = T; ua.d = D; ua.r = r;
-  LR_TRY(lr::launch_up<E>(ua, n_up, s));
+  LR_LAUNCH("up", s, lr::launch_up<E>(ua, n_up, s));
   return LR_OK;
 }
 
@@ -104,13 +133,13 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   float* spart = cv.take<float>((size_t)T * nsp * 4);
   float* gpart = cv.take<float>((size_t)D * ngp * 4);
 
-  LR_TRY(lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd, T, D, inv_width(d), d->eps, s));
+  LR_LAUNCH("rms_stats", s, lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd, T, D, inv_width(d), d->eps, s));
 
   lr::DzArgs za{};
   for (int i = 0; i < n_up; ++i) { za.dy[i] = dy[i]; za.B[i] = B[i]; }
   za.h = h; za.rstd = rstd; za.dh = dh; za.z = z; za.spart = spart; za.nspart = nsp;
   za.T = T; za.d = D; za.r = r; za.g = g; za.act = d->act;
-  LR_TRY(lr::launch_dz<E>(za, n_up, s));
+  LR_LAUNCH("dz", s, lr::launch_dz<E>(za, n_up, s));
 
   lr::WgradArgs wa{};
   wa.z = d->act == LR_ACT_IDENTITY ? h : z;
@@ -118,13 +147,13 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   for (int i = 0; i < n_up; ++i) { wa.dy[i] = dy[i]; wa.dB[i] = dB[i]; }
   wa.x = x; wa.dh = dh; wa.A = A; wa.gamma = gamma; wa.dA = dA; wa.gpart = gpart; wa.ngpart = ngp;
   wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
-  LR_TRY(lr::launch_wgrad<E>(wa, s));
-  LR_TRY(lr::launch_sum_parts(gpart, dgamma, D, ngp, s));
+  LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
+  LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, ngp, s));
 
   lr::DxArgs xa{};
   xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp;
   xa.dx = dx; xa.T = T; xa.d = D; xa.r = r; xa.g = g; xa.invD = inv_width(d);
-  LR_TRY(lr::launch_dx<E>(xa, s));
+  LR_LAUNCH("dx", s, lr::launch_dx<E>(xa, s));
   return LR_OK;
 }
 
@@ -134,11 +163,11 @@ lr_status partial_impl(const lr_dims* d, const void* x, const void* gamma, const
   const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r;
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
-  LR_TRY(lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
+  LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
   lr::DownArgs da{};
   da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_PARTIAL;
   da.invD = inv_width(d); da.eps = d->eps; da.partial = partial; da.sumsq = sumsq;
-  LR_TRY(lr::launch_down<E>(da, s));
+  LR_LAUNCH("down", s, lr::launch_down<E>(da, s));
   return LR_OK;
 }
 
@@ -149,14 +178,14 @@ lr_status finish_impl(const lr_dims* d, const float* partial, const float* sumsq
   Carve cv{static_cast<char*>(ws)};
   cv.take<void>((size_t)D * gr * sizeof(E));  // same layout as the forward
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  LR_TRY(lr::launch_finish<E>(partial, sumsq, h_save, z, T, r, g, d->act, inv_width(d), d->eps, s));
+  LR_LAUNCH("finish", s, lr::launch_finish<E>(partial, sumsq, h_save, z, T, r, g, d->act, inv_width(d), d->eps, s));
   lr::UpArgs ua{};
   const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
   ua.z = z_is_h ? h_save : z;
   ua.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
   for (int i = 0; i < n_up; ++i) { ua.B[i] = B[i]; ua.y[i] = y[i]; }
   ua.T = T; ua.d = D; ua.r = r;
-  LR_TRY(lr::launch_up<E>(ua, n_up, s));
+  LR_LAUNCH("up", s, lr::launch_up<E>(ua, n_up, s));
   return LR_OK;
 }
 
@@ -168,6 +197,14 @@ lr_status check_ptrs(const void* const* arr, int n) {
 }
 inline bool req(const void* p) { return p && aligned16(p); }
 inline bool opt(const void* p) { return !p || aligned16(p); }
+// a [T, ...] buffer: may be NULL when there are no rows
+inline bool req_rows(const void* p, int64_t T) { return T == 0 ? opt(p) : req(p); }
+lr_status check_rows_ptrs(const void* const* arr, int n, int64_t T) {
+  if (!arr) return LR_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (!req_rows(arr[i], T)) return LR_EINVAL;
+  return LR_OK;
+}
 
 lr_status check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return LR_OK;
@@ -202,23 +239,24 @@ lr_status rmsnorm_online(const lr_dims* d, const void* x, const void* gamma, voi
   if (d->T < 0 || d->d <= 0 || d->d_norm < 0 || !(d->eps >= 0.f) || !isfinite(d->eps)) return LR_EINVAL;
   if (d->d % 8) return LR_EUNSUPPORTED;
   if (d->T > (1ll << 30) || d->d > (1 << 24)) return LR_EUNSUPPORTED;
-  if (!req(x) || !opt(y) || !opt(sumsq) || !opt(rstd)) return LR_EINVAL;
+  if (!req_rows(x, d->T) || !opt(y) || !opt(sumsq) || !opt(rstd)) return LR_EINVAL;
   if (y && !req(gamma)) return LR_EINVAL;
   const int T = (int)d->T, D = (int)d->d;
-  hipError_t e = d->dtype == LR_BF16
-                     ? lr::launch_rms_stats<bf16>(x, gamma, y, sumsq, rstd, T, D, inv_width(d), d->eps, s)
-                     : lr::launch_rms_stats<float>(x, gamma, y, sumsq, rstd, T, D, inv_width(d), d->eps, s);
-  return hip_status(e);
+  if (d->dtype == LR_BF16)
+    LR_LAUNCH("rms_stats", s, lr::launch_rms_stats<bf16>(x, gamma, y, sumsq, rstd, T, D, inv_width(d), d->eps, s));
+  else
+    LR_LAUNCH("rms_stats", s, lr::launch_rms_stats<float>(x, gamma, y, sumsq, rstd, T, D, inv_width(d), d->eps, s));
+  return LR_OK;
 }
 
 lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
                        void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
-  if (!req(x) || !req(gamma) || !req(A) || !opt(h_save)) return LR_EINVAL;
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save)) return LR_EINVAL;
   const int n_up = n_up_of(d);
   if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
-  if ((st = check_ptrs(reinterpret_cast<const void* const*>(y), n_up)) != LR_OK) return st;
+  if ((st = check_rows_ptrs(reinterpret_cast<const void* const*>(y), n_up, d->T)) != LR_OK) return st;
   if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
   return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, y, h_save, ws, s)
                              : fwd_impl<float>(d, x, gamma, A, B, y, h_save, ws, s);
@@ -229,11 +267,12 @@ lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const
                        float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
-  if (!req(x) || !req(gamma) || !req(A) || !req(h_saved) || !req(dx) || !req(dgamma) || !req(dA))
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(h_saved, d->T) || !req_rows(dx, d->T) ||
+      !req(dgamma) || !req(dA))
     return LR_EINVAL;
   const int n_up = n_up_of(d);
   if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
-  if ((st = check_ptrs(dy, n_up)) != LR_OK) return st;
+  if ((st = check_rows_ptrs(dy, n_up, d->T)) != LR_OK) return st;
   if ((st = check_ptrs(reinterpret_cast<const void* const*>(dB), n_up)) != LR_OK) return st;
   if ((st = check_ws(ws, ws_bytes, bwd_ws(d))) != LR_OK) return st;
   return d->dtype == LR_BF16 ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, dy, dx, dgamma, dA, dB, ws, s)
@@ -244,7 +283,8 @@ lr_status lr_down_partial(const lr_dims* d, const void* x, const void* gamma, co
                           float* sumsq, void* ws, size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
-  if (!req(x) || !req(gamma) || !req(A) || !req(partial) || !req(sumsq)) return LR_EINVAL;
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(partial, d->T) || !req_rows(sumsq, d->T))
+    return LR_EINVAL;
   if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
   return d->dtype == LR_BF16 ? partial_impl<bf16>(d, x, gamma, A, partial, sumsq, ws, s)
                              : partial_impl<float>(d, x, gamma, A, partial, sumsq, ws, s);
@@ -254,13 +294,59 @@ lr_status lr_up_finish(const lr_dims* d, const float* partial, const float* sums
                        void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
-  if (!req(partial) || !req(sumsq) || !opt(h_save)) return LR_EINVAL;
+  if (!req_rows(partial, d->T) || !req_rows(sumsq, d->T) || !opt(h_save)) return LR_EINVAL;
   const int n_up = n_up_of(d);
   if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
-  if ((st = check_ptrs(reinterpret_cast<const void* const*>(y), n_up)) != LR_OK) return st;
+  if ((st = check_rows_ptrs(reinterpret_cast<const void* const*>(y), n_up, d->T)) != LR_OK) return st;
   if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
   return d->dtype == LR_BF16 ? finish_impl<bf16>(d, partial, sumsq, B, y, h_save, ws, s)
                              : finish_impl<float>(d, partial, sumsq, B, y, h_save, ws, s);
+}
+
+lr_status lr_trace_begin(const char* kernel, int max_launches) {
+  Trace& t = g_trace;
+  if (t.on || max_launches < 1) return LR_EINVAL;
+  t.ev = new hipEvent_t[2 * (size_t)max_launches];
+  t.names = new const char*[max_launches];
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    if (hipEventCreate(&t.ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(t.ev[j]);
+      delete[] t.ev;
+      delete[] t.names;
+      t = Trace{};
+      return LR_EHIP;
+    }
+  }
+  t.cap = max_launches;
+  t.n = 0;
+  t.filter[0] = 0;
+  if (kernel) {
+    strncpy(t.filter, kernel, sizeof(t.filter) - 1);
+    t.filter[sizeof(t.filter) - 1] = 0;
+  }
+  t.on = true;
+  return LR_OK;
+}
+
+int lr_trace_count(void) { return g_trace.on ? g_trace.n : 0; }
+
+lr_status lr_trace_elapsed(int i, const char** kernel, float* ms) {
+  Trace& t = g_trace;
+  if (!t.on || i < 0 || i >= t.n || !ms) return LR_EINVAL;
+  if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess) return LR_EHIP;
+  if (hipEventElapsedTime(ms, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) return LR_EHIP;
+  if (kernel) *kernel = t.names[i];
+  return LR_OK;
+}
+
+lr_status lr_trace_end(void) {
+  Trace& t = g_trace;
+  if (!t.on) return LR_EINVAL;
+  for (int i = 0; i < 2 * t.cap; ++i) hipEventDestroy(t.ev[i]);
+  delete[] t.ev;
+  delete[] t.names;
+  t = Trace{};
+  return LR_OK;
 }
 
 }  // extern "C"
