@@ -96,9 +96,16 @@ __device__ __forceinline__ void mfma_chunk(f32x16& acc, const uint4& a, const ui
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// LDS slot of 16-byte chunk `ch` of tile row `row`.  Rows are 128 bytes; the chunk
+// index is XORed with bits 1..3 of the row, so that 16 consecutive rows reading
+// the same chunk (one ds_read_b128 quarter-wave) and 2 rows written whole both
+// touch 16 distinct 16-byte slots of a 256-byte bank window.
+__device__ __forceinline__ int lds_slot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+
 template <typename E_, int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
   using E = E_;
+  static constexpr bool PIPE = false;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
   static constexpr int CH = 8;                      // chunks per LDS row
@@ -110,12 +117,15 @@ struct TileCfg {
   static constexpr int LDS_A = BM * CH, LDS_B = BN * CH;  // uint4 units per stage
   static constexpr int LDS_STAGE = LDS_A + LDS_B;
   static constexpr int LDS_GEMM_BYTES = 2 * LDS_STAGE * 16;
+  static constexpr int LDS_UINT4 = 2 * LDS_STAGE;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BM % VEC == 0 && BN % VEC == 0, "tile must be a multiple of VEC");
 };
 
 // One operand of a GEMM: base pointer, leading dimension (elements) and the valid
-// extents; loads outside [0, MN) x [0, K) read as zero.
+// extents.  Loads at K >= K read as zero (hardware range check of the buffer
+// resource); loads at M/N >= MN only feed output rows/columns that are never
+// stored, and never read past the operand's last element.
 struct Opnd {
   const void* p;
   int64_t ld;
@@ -145,18 +155,36 @@ struct MapGateUp {
   }
 };
 
+constexpr uint32_t kOffInvalid = 0x80000000u;  // beyond every resource's range -> reads 0
+constexpr int64_t kMaxRecords = 0x7fffffff;
+
+// Buffer resource (gfx9 raw buffer, no stride) over [p, p + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+
+// Global -> register -> LDS staging of one operand tile (ROWS x BK).
+// KC : unit = one 16-byte vector (row, chunk); MNC: unit = a VEC x VEC block.
+// Byte offsets are relative to the tile origin (row mn0 / k0 for KC, k0 / mn0 for
+// MNC) and fixed for the whole K loop; the resource is rebased every k step.
 template <class C, int ROWS, bool MNC>
 struct Loader {
   using E = typename C::E;
   static constexpr int VEC = C::VEC, CH = C::CH, NT = C::THREADS;
+  static constexpr int ES = (int)sizeof(E);
   static constexpr int UNITS = MNC ? (ROWS / VEC) * CH : ROWS * CH;
   static constexpr int PER = (UNITS + NT - 1) / NT;
   static constexpr int REGS = MNC ? PER * VEC : PER;
+  uint32_t off[PER];
   uint4 r[REGS];
 
   template <class Map>
-  __device__ __forceinline__ void load(const Opnd& o, const Map& map, int mn0, int k0, int tid) {
-    const E* base = static_cast<const E*>(o.p);
+  __device__ __forceinline__ void init(const Opnd& o, const Map& map, int mn0, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int u = tid + i * NT;
@@ -164,21 +192,39 @@ struct Loader {
       if (!MNC) {
         const int row = u / CH, ch = u % CH;
         const int gmn = map(mn0, row);
-        const int gk = k0 + ch * VEC;
-        const bool ok = in_tile && gmn >= 0 && gmn < o.MN && gk < o.K;
-        r[i] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)gmn * o.ld + gk)
-                  : make_uint4(0, 0, 0, 0);
+        const bool ok = in_tile && gmn >= 0;
+        off[i] = ok ? (uint32_t)(((int64_t)(gmn - mn0) * o.ld + ch * VEC) * ES) : kOffInvalid;
       } else {
         const int ch = u % CH, blk = u / CH;
         const int gmn = map(mn0, blk * VEC);
-        const int gk = k0 + ch * VEC;
-        const bool okmn = in_tile && gmn >= 0 && gmn < o.MN;
+        const bool ok = in_tile && gmn >= 0;
+        off[i] = ok ? (uint32_t)(((int64_t)(ch * VEC) * o.ld + (gmn - mn0)) * ES) : kOffInvalid;
+      }
+    }
+  }
+
+  // Resource for the k step starting at k0: KC rows mn0.., columns k0..; MNC rows k0.., columns mn0..
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const Opnd& o, int mn0, int k0) const {
+    const char* base = static_cast<const char*>(o.p);
+    if (!MNC) {
+      const int64_t rows = (int64_t)o.MN - mn0;
+      return make_rsrc(base + ((int64_t)mn0 * o.ld + k0) * ES, rows <= 0 ? 0 : ((rows - 1) * o.ld + (o.K - k0)) * ES);
+    } else {
+      const int64_t rows = (int64_t)o.K - k0;
+      return make_rsrc(base + ((int64_t)k0 * o.ld + mn0) * ES, rows <= 0 ? 0 : ((rows - 1) * o.ld + (o.MN - mn0)) * ES);
+    }
+  }
+
+  __device__ __forceinline__ void load(const Opnd& o, int mn0, int k0) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(o, mn0, k0);
+    const uint32_t rowb = (uint32_t)(o.ld * ES);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const bool ok = okmn && (gk + e) < o.K;
-          r[i * VEC + e] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)(gk + e) * o.ld + gmn)
-                              : make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < PER; ++i) {
+      if (!MNC) {
+        r[i] = buf_load16(rs, off[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) r[i * VEC + e] = buf_load16(rs, off[i] == kOffInvalid ? kOffInvalid : off[i] + e * rowb);
       }
     }
   }
@@ -197,15 +243,18 @@ struct Loader {
       if ((UNITS % NT != 0) && u >= UNITS) continue;
       if (!MNC) {
         const int row = u / CH, ch = u % CH;
-        lds[row * CH + (ch ^ (row & 7))] = r[i];
+        lds[lds_slot(row, ch)] = r[i];
       } else {
-        const int ch = u % CH, blk = u / CH;
+        // lanes of odd blocks store the rows of each pair in swapped order, so
+        // that the 16 lanes of one LDS cycle write rows of both parities
+        const int ch = u % CH, blk = u / CH, flip = blk & 1;
         uint4 t[VEC];
         transpose_block(&r[i * VEC], t, (E*)nullptr);
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
-          const int row = blk * VEC + j;
-          lds[row * CH + (ch ^ (row & 7))] = t[j];
+          const int jj = j ^ flip;
+          const int row = blk * VEC + jj;
+          lds[lds_slot(row, ch)] = flip ? t[j ^ 1] : t[j];
         }
       }
     }
@@ -213,30 +262,39 @@ struct Loader {
 };
 
 template <class C>
+__device__ __forceinline__ void load_frags(const uint4* ldsA, const uint4* ldsB, uint4 (&a)[C::MB], uint4 (&b)[C::NB],
+                                           int ks, int wm, int wn, int lane) {
+  const int lr = lane & 31, ch = 2 * ks + (lane >> 5);
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) a[mb] = ldsA[lds_slot(wm * C::WTM + mb * 32 + lr, ch)];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) b[nb] = ldsB[lds_slot(wn * C::WTN + nb * 32 + lr, ch)];
+}
+
+// MFMAs over one LDS stage; the fragments of sub-step ks+1 are read while the
+// MFMAs of sub-step ks run.
+template <class C>
 __device__ __forceinline__ void mma_stage(const uint4* ldsA, const uint4* ldsB,
                                           f32x16 (&acc)[C::MB][C::NB], int wm, int wn, int lane) {
-  const int lr = lane & 31, hi = lane >> 5, sw = lane & 7;
+  uint4 a[2][C::MB], b[2][C::NB];
+  load_frags<C>(ldsA, ldsB, a[0], b[0], 0, wm, wn, lane);
 #pragma unroll
   for (int ks = 0; ks < C::CH / 2; ++ks) {
-    const int ch = (2 * ks + hi) ^ sw;
-    uint4 a[C::MB], b[C::NB];
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) a[mb] = ldsA[(wm * C::WTM + mb * 32 + lr) * C::CH + ch];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) b[nb] = ldsB[(wn * C::WTN + nb * 32 + lr) * C::CH + ch];
+    if (ks + 1 < C::CH / 2) load_frags<C>(ldsA, ldsB, a[(ks + 1) & 1], b[(ks + 1) & 1], ks + 1, wm, wn, lane);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) mfma_chunk(acc[mb][nb], a[mb], b[nb], (typename C::E*)nullptr);
+      for (int nb = 0; nb < C::NB; ++nb)
+        mfma_chunk(acc[mb][nb], b[ks & 1][nb], a[ks & 1][mb], (typename C::E*)nullptr);
   }
 }
 
-// Double-buffered mainloop over K.  With ROWSTAT the K-contiguous A operand's
+// Double-buffered mainloop over k in [kbeg, kbeg + K).  With ROWSTAT the K-contiguous A operand's
 // per-row sum of squares is accumulated on the way through registers and left,
 // reduced, in rowss[0..BM) (LDS).
 template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB>
 __device__ __forceinline__ void gemm_tile(const Opnd& oa, const Opnd& ob, const MapA& ma,
-                                          const MapB& mbm, int m0, int n0, int K, uint4* lds,
+                                          const MapB& mbm, int m0, int n0, int kbeg, int K, uint4* lds,
                                           float* rowss, f32x16 (&acc)[C::MB][C::NB]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -255,8 +313,10 @@ __device__ __forceinline__ void gemm_tile(const Opnd& oa, const Opnd& ob, const 
 
   const int nk = (K + C::BK - 1) / C::BK;
   if (nk > 0) {
-    la.load(oa, ma, m0, 0, tid);
-    lb.load(ob, mbm, n0, 0, tid);
+    la.init(oa, ma, m0, tid);
+    lb.init(ob, mbm, n0, tid);
+    la.load(oa, m0, kbeg);
+    lb.load(ob, n0, kbeg);
     if constexpr (ROWSTAT) la.accum_sumsq(ss);
     la.store(lds, tid);
     lb.store(lds + C::LDS_A, tid);
@@ -266,8 +326,8 @@ __device__ __forceinline__ void gemm_tile(const Opnd& oa, const Opnd& ob, const 
       uint4* nxt = lds + ((kt + 1) & 1) * C::LDS_STAGE;
       const bool more = kt + 1 < nk;
       if (more) {
-        la.load(oa, ma, m0, (kt + 1) * C::BK, tid);
-        lb.load(ob, mbm, n0, (kt + 1) * C::BK, tid);
+        la.load(oa, m0, kbeg + (kt + 1) * C::BK);
+        lb.load(ob, n0, kbeg + (kt + 1) * C::BK);
       }
       mma_stage<C>(cur, cur + C::LDS_A, acc, wm, wn, lane);
       if (more) {
@@ -295,18 +355,58 @@ __device__ __forceinline__ void gemm_tile(const Opnd& oa, const Opnd& ob, const 
   }
 }
 
-// Global (row, col) of accumulator register v of block (mb, nb) for this lane.
+// Work-group scheduling.  The dispatcher hands consecutive work-group ids to the 8
+// XCDs in turn, and each XCD has its own L2.  xcd_remap() renumbers ids so that
+// every XCD receives one contiguous range of logical tiles, and grouped_tile()
+// walks each range in groups of GROUP_M row panels, so that the work-groups
+// resident on one XCD at a time share few operand panels.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  const int xcd = bid % kNumXcd, idx = bid / kNumXcd;
+  const int per = nblk / kNumXcd, extra = nblk % kNumXcd;
+  return xcd * per + (xcd < extra ? xcd : extra) + idx;
+}
+template <int GROUP_M>
+__device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (logical / in_group) * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int w = logical % in_group;
+  tm = first_m + w % gsz;
+  tn = w / gsz;
+}
+
+// Output position of this lane's accumulators.  The MFMA's first operand is the
+// B tile (so the 32x32 accumulator's "row" runs over N): block (mb, nb) of lane l
+// holds output row  m0 + wm*WTM + mb*32 + l%32  and, in registers 4q..4q+3, the
+// four consecutive output columns  n0 + wn*WTN + nb*32 + 8q + 4*(l/32) + 0..3.
 template <class C>
 struct FragPos {
   int row0, col0, lane;
   __device__ __forceinline__ FragPos(int m0, int n0) {
     const int tid = threadIdx.x, wave = tid >> 6;
     lane = tid & 63;
-    row0 = m0 + (wave / C::WN) * C::WTM + 4 * (lane >> 5);
-    col0 = n0 + (wave % C::WN) * C::WTN + (lane & 31);
+    row0 = m0 + (wave / C::WN) * C::WTM + (lane & 31);
+    col0 = n0 + (wave % C::WN) * C::WTN + 4 * (lane >> 5);
   }
-  __device__ __forceinline__ int row(int mb, int v) const { return row0 + mb * 32 + 8 * (v >> 2) + (v & 3); }
-  __device__ __forceinline__ int col(int nb) const { return col0 + nb * 32; }
+  __device__ __forceinline__ int row(int mb) const { return row0 + mb * 32; }
+  __device__ __forceinline__ int col(int nb, int q) const { return col0 + nb * 32 + 8 * q; }
 };
+
+// 4 consecutive values -> memory (8 bytes of bf16 / 16 bytes of fp32)
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ float4 load4(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 }  // namespace lr

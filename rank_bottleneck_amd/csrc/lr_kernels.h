@@ -56,6 +56,10 @@ struct WgradArgs {
   float* gpart;       // [d, ngpart]
   int ngpart;
   int T, d, r, g, n_up;
+  int nsplit, ksplit;       // token splits and tokens per split (a multiple of the k step)
+  float* wpart;             // nsplit x part_stride fp32 partial tiles (nsplit > 1)
+  int64_t part_stride;      // n_up*r*d + d*g*r
+  int64_t part_offA;        // n_up*r*d
 };
 
 struct DxArgs {
@@ -83,8 +87,11 @@ template <typename E> hipError_t launch_finish(const float* partial, const float
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 template <typename E> hipError_t launch_dx(const DxArgs& a, hipStream_t s);
-hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, hipStream_t s);
+hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, int stride, hipStream_t s);
 template <typename E> int dz_nparts(int r);
 template <typename E> int wgrad_nparts(int gr);
+template <typename E> int gemm_bk();
+template <typename E> int wgrad_nparts_used(int gr, int nsplit);
+template <typename E> int wgrad_splits(int T, int d, int r, int g, int n_up);
 
 }  // namespace lr

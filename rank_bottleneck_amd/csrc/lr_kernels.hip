@@ -24,9 +24,12 @@
 #include <stdint.h>
 
 #include "lr_device.h"
+#include "lr_pipe.h"
 #include "lr_kernels.h"
 
 namespace lr {
+
+constexpr int kGroupM = 4;  // row panels per scheduling group
 
 // ------------------------------------------------------------------ small kernels
 template <typename E>
@@ -112,12 +115,11 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
   }
 }
 
-template <int PARTS>
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ parts, float* __restrict__ out,
-                                                   int n, int nparts) {
+                                                   int n, int nparts, int stride) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const float* p = parts + (int64_t)i * nparts;
+  const float* p = parts + (int64_t)i * stride;
   float s = 0.f;
   for (int k = 0; k < nparts; ++k) s += p[k];
   out[i] = s;
@@ -129,129 +131,153 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
 template <class C, bool GATEUP>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_down(DownArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[2 * C::LDS_STAGE + C::BM / 4];
-  float* rowss = reinterpret_cast<float*>(lds + 2 * C::LDS_STAGE);
+  __shared__ uint4 lds[C::LDS_UINT4 + C::BM / 4];
+  float* rowss = reinterpret_cast<float*>(lds + C::LDS_UINT4);
   const int gr = a.g * a.r;
-  const int ncols_logical = GATEUP ? a.r : gr;  // columns walked by tiles
-  const int tiles_n = (ncols_logical + (GATEUP ? C::BN / 2 : C::BN) - 1) / (GATEUP ? C::BN / 2 : C::BN);
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * C::BM;
-  const int n0 = tn * (GATEUP ? C::BN / 2 : C::BN);
+  constexpr int TN = GATEUP ? C::BN / 2 : C::BN;  // logical columns per tile
+  const int tiles_n = ((GATEUP ? a.r : gr) + TN - 1) / TN;
+  const int tiles_m = (a.T + C::BM - 1) / C::BM;
+  int tm, tn;
+  grouped_tile<kGroupM>(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * TN;
 
   Opnd oa{a.x, a.d, a.T, a.d};
   Opnd ob{a.Ap, gr, gr, a.d};
   f32x16 acc[C::MB][C::NB];
   if constexpr (GATEUP) {
-    gemm_tile<C, false, true, true>(oa, ob, MapId{}, MapGateUp<C::WTN>{a.r}, m0, n0, a.d, lds, rowss, acc);
+    mainloop<C, false, true, true>(oa, ob, MapId{}, MapGateUp<C::WTN>{a.r}, m0, n0, 0, a.d, lds, rowss, acc);
   } else {
-    gemm_tile<C, false, true, true>(oa, ob, MapId{}, MapId{}, m0, n0, a.d, lds, rowss, acc);
+    mainloop<C, false, true, true>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, rowss, acc);
   }
 
-  FragPos<C> fp(m0, 0);
   const int wn = (threadIdx.x >> 6) % C::WN;
+  FragPos<C> fp(m0, 0);
+  // column of register block (nb, q) before any gate/up remapping
+  const int cbase = wn * C::WTN + 4 * (fp.lane >> 5);
   if (a.mode == DOWN_PARTIAL) {
     if (tn == 0 && threadIdx.x < C::BM && m0 + (int)threadIdx.x < a.T)
       a.sumsq[m0 + threadIdx.x] = rowss[threadIdx.x];
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int row = fp.row(mb);
+      if (row >= a.T) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = fp.row(mb, v);
-        if (row >= a.T) continue;
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
+        for (int q = 0; q < 4; ++q) {
           int col;
           if constexpr (GATEUP) {
-            MapGateUp<C::WTN> mp{a.r};
-            col = mp(n0, wn * C::WTN + nb * 32 + (fp.lane & 31));
+            col = MapGateUp<C::WTN>{a.r}(n0, cbase + nb * 32 + 8 * q);
           } else {
-            col = n0 + wn * C::WTN + nb * 32 + (fp.lane & 31);
+            col = n0 + cbase + nb * 32 + 8 * q;
           }
           if (col < 0 || col >= gr) continue;
-          a.partial[(int64_t)row * gr + col] = acc[mb][nb][v];
+          const f32x16& v = acc[mb][nb];
+          store4(a.partial + (int64_t)row * gr + col, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         }
-      }
+    }
     return;
   }
 
   E* h = static_cast<E*>(a.h);
   E* z = static_cast<E*>(a.z);
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int row = fp.row(mb);
+    if (row >= a.T) continue;
+    const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
+    if constexpr (GATEUP) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = fp.row(mb, v);
-      if (row >= a.T) continue;
-      const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
-      if constexpr (GATEUP) {
+      for (int nb = 0; nb < C::NB / 2; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB / 2; ++nb) {
-          const int logical = n0 + wn * (C::WTN / 2) + nb * 32 + (fp.lane & 31);
+        for (int q = 0; q < 4; ++q) {
+          const int logical = n0 + wn * (C::WTN / 2) + nb * 32 + 8 * q + 4 * (fp.lane >> 5);
           if (logical >= a.r) continue;
-          const float hg = acc[mb][nb][v] * rs, hu = acc[mb][nb + C::NB / 2][v] * rs;
-          if (h) {
-            h[(int64_t)row * gr + logical] = from_f32<E>(hg);
-            h[(int64_t)row * gr + a.r + logical] = from_f32<E>(hu);
-          }
-          z[(int64_t)row * a.r + logical] = from_f32<E>(hg * sigmoidf_(hg) * hu);
-        }
-      } else {
+          float hg[4], hu[4], zz[4];
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const int col = n0 + wn * C::WTN + nb * 32 + (fp.lane & 31);
-          if (col >= gr) continue;
-          const float hv = acc[mb][nb][v] * rs;
-          if (h) h[(int64_t)row * gr + col] = from_f32<E>(hv);
-          if (a.act == ACT_SILU) z[(int64_t)row * gr + col] = from_f32<E>(hv * sigmoidf_(hv));
-          else if (!h) z[(int64_t)row * gr + col] = from_f32<E>(hv);
+          for (int e = 0; e < 4; ++e) {
+            hg[e] = acc[mb][nb][4 * q + e] * rs;
+            hu[e] = acc[mb][nb + C::NB / 2][4 * q + e] * rs;
+            zz[e] = hg[e] * sigmoidf_(hg[e]) * hu[e];
+          }
+          if (h) {
+            store4(h + (int64_t)row * gr + logical, hg[0], hg[1], hg[2], hg[3]);
+            store4(h + (int64_t)row * gr + a.r + logical, hu[0], hu[1], hu[2], hu[3]);
+          }
+          store4(z + (int64_t)row * a.r + logical, zz[0], zz[1], zz[2], zz[3]);
         }
-      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + cbase + nb * 32 + 8 * q;
+          if (col >= gr) continue;
+          float hv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = acc[mb][nb][4 * q + e] * rs;
+          if (h) store4(h + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
+          if (a.act == ACT_SILU) {
+            store4(z + (int64_t)row * gr + col, hv[0] * sigmoidf_(hv[0]), hv[1] * sigmoidf_(hv[1]),
+                   hv[2] * sigmoidf_(hv[2]), hv[3] * sigmoidf_(hv[3]));
+          } else if (!h) {
+            store4(z + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
+          }
+        }
     }
+  }
 }
 
 // ------------------------------------------------------------------ up projection
-// y_i = z_i . B_i ; blockIdx.y = branch
+// y_i = z_i . B_i ; one launch over (branch, tile)
 template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_up(UpArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[2 * C::LDS_STAGE];
-  const int br = blockIdx.y;
+  __shared__ uint4 lds[C::LDS_UINT4];
   const int tiles_n = (a.d + C::BN - 1) / C::BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int tiles_m = (a.T + C::BM - 1) / C::BM;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int br = logical / (tiles_m * tiles_n);
+  int tm, tn;
+  grouped_tile<kGroupM>(logical % (tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   Opnd oa{static_cast<const E*>(a.z) + (int64_t)br * a.r, a.ldz, a.T, a.r};
   Opnd ob{a.B[br], a.d, a.d, a.r};
   f32x16 acc[C::MB][C::NB];
-  gemm_tile<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, a.r, lds, nullptr, acc);
+  mainloop<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.r, lds, nullptr, acc);
   E* y = static_cast<E*>(a.y[br]);
   FragPos<C> fp(m0, n0);
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int row = fp.row(mb);
+    if (row >= a.T) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = fp.row(mb, v);
-      if (row >= a.T) continue;
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int col = fp.col(nb);
-        if (col < a.d) y[(int64_t)row * a.d + col] = from_f32<E>(acc[mb][nb][v]);
+      for (int q = 0; q < 4; ++q) {
+        const int col = fp.col(nb, q);
+        const f32x16& v = acc[mb][nb];
+        if (col < a.d) store4(y + (int64_t)row * a.d + col, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       }
-    }
+  }
 }
 
 // ------------------------------------------------------------------ backward: dz -> dh'
 template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dz(DzArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[2 * C::LDS_STAGE];
-  const int br = blockIdx.y;
+  __shared__ uint4 lds[C::LDS_UINT4];
   const int tiles_n = (a.r + C::BN - 1) / C::BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int tiles_m = (a.T + C::BM - 1) / C::BM;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int br = logical / (tiles_m * tiles_n);
+  int tm, tn;
+  grouped_tile<kGroupM>(logical % (tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   Opnd oa{a.dy[br], a.d, a.T, a.d};
   Opnd ob{a.B[br], a.d, a.r, a.d};  // B_i^T: (n = c, k = j) at B_i[c*d + j]
   f32x16 acc[C::MB][C::NB];
-  gemm_tile<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, a.d, lds, nullptr, acc);
+  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc);
 
   const int gr = a.g * a.r;
   const E* h = static_cast<const E*>(a.h);
@@ -261,67 +287,90 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   const int wn = (threadIdx.x >> 6) % C::WN;
   const int part = (br * tiles_n + tn) * C::WN + wn;
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int row = fp.row(mb);
+    const bool rok = row < a.T;
+    const float rs = rok ? a.rstd[row] : 0.f;
+    const int64_t hrow = (int64_t)row * gr;
+    float srow = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = fp.row(mb, v);
-      const bool rok = row < a.T;
-      const float rs = rok ? a.rstd[row] : 0.f;
-      float srow = 0.f;
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int c = fp.col(nb);
+      for (int q = 0; q < 4; ++q) {
+        const int c = fp.col(nb, q);
         if (!rok || c >= a.r) continue;
-        const float dzv = acc[mb][nb][v];
-        const int64_t hrow = (int64_t)row * gr;
-        if (a.act == ACT_IDENTITY) {
-          const float hv = to_f32(h[hrow + br * a.r + c]);
-          const float d1 = rs * dzv;
-          dh[hrow + br * a.r + c] = from_f32<E>(d1);
-          srow += d1 * hv;
-        } else if (a.act == ACT_SILU) {
-          const float hv = to_f32(h[hrow + br * a.r + c]);
-          const float s = sigmoidf_(hv);
-          const float d1 = rs * dzv * s * (1.0f + hv * (1.0f - s));
-          dh[hrow + br * a.r + c] = from_f32<E>(d1);
-          z[hrow + br * a.r + c] = from_f32<E>(hv * s);
-          srow += d1 * hv;
-        } else {  // SwiGLU, one branch
-          const float hg = to_f32(h[hrow + c]), hu = to_f32(h[hrow + a.r + c]);
-          const float s = sigmoidf_(hg);
-          const float sg = hg * s;
-          const float dg = rs * dzv * hu * s * (1.0f + hg * (1.0f - s));
-          const float du = rs * dzv * sg;
-          dh[hrow + c] = from_f32<E>(dg);
-          dh[hrow + a.r + c] = from_f32<E>(du);
-          z[(int64_t)row * a.r + c] = from_f32<E>(sg * hu);
-          srow += dg * hg + du * hu;
+        const f32x16& v = acc[mb][nb];
+        const float dzv[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        if (a.act == ACT_SWIGLU) {
+          const float4 g4 = load4(h + hrow + c), u4 = load4(h + hrow + a.r + c);
+          const float hg[4] = {g4.x, g4.y, g4.z, g4.w}, hu[4] = {u4.x, u4.y, u4.z, u4.w};
+          float dg[4], du[4], zz[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float s = sigmoidf_(hg[e]);
+            const float sg = hg[e] * s;
+            dg[e] = rs * dzv[e] * hu[e] * s * (1.0f + hg[e] * (1.0f - s));
+            du[e] = rs * dzv[e] * sg;
+            zz[e] = sg * hu[e];
+            srow += dg[e] * hg[e] + du[e] * hu[e];
+          }
+          store4(dh + hrow + c, dg[0], dg[1], dg[2], dg[3]);
+          store4(dh + hrow + a.r + c, du[0], du[1], du[2], du[3]);
+          store4(z + (int64_t)row * a.r + c, zz[0], zz[1], zz[2], zz[3]);
+        } else {
+          const int64_t idx = hrow + br * a.r + c;
+          const float4 h4 = load4(h + idx);
+          const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+          float d1[4];
+          if (a.act == ACT_SILU) {
+            float zz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float s = sigmoidf_(hv[e]);
+              d1[e] = rs * dzv[e] * s * (1.0f + hv[e] * (1.0f - s));
+              zz[e] = hv[e] * s;
+            }
+            store4(z + idx, zz[0], zz[1], zz[2], zz[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d1[e] = rs * dzv[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) srow += d1[e] * hv[e];
+          store4(dh + idx, d1[0], d1[1], d1[2], d1[3]);
         }
       }
-      // reduce over the 32 columns held by lanes with the same lane>>5
-      srow += __shfl_xor(srow, 1);
-      srow += __shfl_xor(srow, 2);
-      srow += __shfl_xor(srow, 4);
-      srow += __shfl_xor(srow, 8);
-      srow += __shfl_xor(srow, 16);
-      if ((fp.lane & 31) == 0 && rok) a.spart[(int64_t)row * a.nspart + part] = srow;
-    }
+    // lanes l and l+32 hold the same row
+    srow += __shfl_xor(srow, 32);
+    if (fp.lane < 32 && rok) a.spart[(int64_t)row * a.nspart + part] = srow;
+  }
 }
 
 // ------------------------------------------------------------------ backward: weight gradients
-// blockIdx.y < n_up: dB_i = z_i^T . dy_i ; blockIdx.y == n_up: M = x^T . dh' -> dA, dgamma partials
+// Jobs: j < n_up: dB_j = z_j^T . dy_j ; j == n_up: M = x^T . dh'; one launch over (split, job, tile).
+// Each split covers a token range; with more than one split the fp32 tile
+// goes to the partial buffer [split][job-major M x N] and k_wgrad_reduce finishes.
 template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_wgrad(WgradArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[2 * C::LDS_STAGE];
-  const int job = blockIdx.y;
+  __shared__ uint4 lds[C::LDS_UINT4];
   const int gr = a.g * a.r;
+  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+  const int tmA = (a.d + C::BM - 1) / C::BM, tnA = (gr + C::BN - 1) / C::BN;
+  const int per_split = a.n_up * tmB * tnB + tmA * tnA;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = logical / per_split;
+  int w = logical % per_split;
+  const int job = w < a.n_up * tmB * tnB ? w / (tmB * tnB) : a.n_up;
+  w = job < a.n_up ? w % (tmB * tnB) : w - a.n_up * tmB * tnB;
   const bool isA = job == a.n_up;
   const int M = isA ? a.d : a.r, N = isA ? gr : a.d;
-  const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
-  if ((int)blockIdx.x >= tiles_m * tiles_n) return;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int tiles_m = isA ? tmA : tmB, tiles_n = isA ? tnA : tnB;
+  int tm, tn;
+  grouped_tile<kGroupM>(w, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int kbeg = split * a.ksplit;
+  const int klen = min(a.ksplit, a.T - kbeg);
   Opnd oa, ob;
   if (isA) {
     oa = Opnd{a.x, a.d, a.d, a.T};   // x^T: (m = j, k = t) at x[t*d + j]
@@ -331,68 +380,103 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
     ob = Opnd{a.dy[job], a.d, a.d, a.T};
   }
   f32x16 acc[C::MB][C::NB];
-  gemm_tile<C, true, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, a.T, lds, nullptr, acc);
+  mainloop<C, true, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, kbeg, klen > 0 ? klen : 0, lds, nullptr, acc);
 
   FragPos<C> fp(m0, n0);
-  if (!isA) {
-    float* dB = a.dB[job];
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = fp.row(mb, v);
-        if (row >= M) continue;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const int col = fp.col(nb);
-          if (col < N) dB[(int64_t)row * N + col] = acc[mb][nb][v];
-        }
-      }
-    return;
+  float* out;
+  int64_t ldo = N;
+  if (a.nsplit > 1) {
+    out = a.wpart + (int64_t)split * a.part_stride + (isA ? a.part_offA : (int64_t)job * a.r * a.d);
+  } else {
+    out = isA ? a.dA : a.dB[job];
   }
+  const bool finalA = isA && a.nsplit == 1;
   const E* Aw = static_cast<const E*>(a.A);
   const E* gamma = static_cast<const E*>(a.gamma);
   const int wn = (threadIdx.x >> 6) % C::WN;
-  const int part = tn * C::WN + wn;
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int row = fp.row(mb);
+    if (row >= M) continue;
+    const float gj = finalA ? to_f32(gamma[row]) : 1.0f;
+    float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = fp.row(mb, v);  // j
-      const bool rok = row < M;
-      const float gj = rok ? to_f32(gamma[row]) : 0.f;
-      float s = 0.f;
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int col = fp.col(nb);
-        if (!rok || col >= N) continue;
-        const float m = acc[mb][nb][v];
-        a.dA[(int64_t)row * gr + col] = gj * m;
-        s += to_f32(Aw[(int64_t)row * gr + col]) * m;
+      for (int q = 0; q < 4; ++q) {
+        const int col = fp.col(nb, q);
+        if (col >= N) continue;
+        const f32x16& v = acc[mb][nb];
+        if (finalA) {
+          const float4 a4 = load4(Aw + (int64_t)row * gr + col);
+          s += a4.x * v[4 * q] + a4.y * v[4 * q + 1] + a4.z * v[4 * q + 2] + a4.w * v[4 * q + 3];
+        }
+        store4(out + (int64_t)row * ldo + col, gj * v[4 * q], gj * v[4 * q + 1], gj * v[4 * q + 2],
+               gj * v[4 * q + 3]);
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      s += __shfl_xor(s, 16);
-      if ((fp.lane & 31) == 0 && rok) a.gpart[(int64_t)row * a.ngpart + part] = s;
+    if (finalA) {
+      s += __shfl_xor(s, 32);
+      if (fp.lane < 32) a.gpart[(int64_t)row * a.ngpart + tn * C::WN + wn] = s;
     }
+  }
+}
+
+// Sum the split partials in split order.  Elements [0, nB) are the dB tensors
+// (job-major), the rest dA; one thread per 4 consecutive outputs.  dA rows get
+// gamma_j and the row partial sum_c A_jc M_jc (one partial per 64-column group).
+template <typename E>
+__global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
+  const int gr = a.g * a.r;
+  const int64_t nB = (int64_t)a.n_up * a.r * a.d, nA = (int64_t)a.d * gr;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const bool active = i < nB + nA;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (active) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float4 p = *reinterpret_cast<const float4*>(a.wpart + (int64_t)s * a.part_stride + i);
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+  }
+  if (active && i < nB) {
+    const int job = (int)(i / ((int64_t)a.r * a.d));
+    const int64_t k = i % ((int64_t)a.r * a.d);
+    *reinterpret_cast<float4*>(a.dB[job] + k) = acc;
+    return;
+  }
+  // dA part: 16 threads share one 64-column group of a row (gr is a multiple of 64)
+  const int64_t k = active ? i - nB : 0;
+  const int row = (int)(k / gr), col = (int)(k % gr);
+  float s = 0.f;
+  if (active) {
+    const E* Aw = static_cast<const E*>(a.A);
+    const float gj = to_f32(static_cast<const E*>(a.gamma)[row]);
+    const float4 a4 = load4(Aw + k);
+    s = a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
+    *reinterpret_cast<float4*>(a.dA + k) = make_float4(gj * acc.x, gj * acc.y, gj * acc.z, gj * acc.w);
+  }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 8);
+  if (active && (threadIdx.x & 15) == 0) a.gpart[(int64_t)row * a.ngpart + col / 64] = s;
 }
 
 // ------------------------------------------------------------------ backward: dx
 template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(DxArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[2 * C::LDS_STAGE + C::BM / 4];
-  float* srow = reinterpret_cast<float*>(lds + 2 * C::LDS_STAGE);  // [BM] : rstd*S'/D
+  __shared__ uint4 lds[C::LDS_UINT4 + C::BM / 4];
+  float* srow = reinterpret_cast<float*>(lds + C::LDS_UINT4);  // [BM] : rstd*S'/D
   const int gr = a.g * a.r;
   const int tiles_n = (a.d + C::BN - 1) / C::BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int tiles_m = (a.T + C::BM - 1) / C::BM;
+  int tm, tn;
+  grouped_tile<kGroupM>(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   Opnd oa{a.dh, gr, a.T, gr};   // dh' [T, gr]
   Opnd ob{a.A, gr, a.d, gr};    // A^T: (n = j, k = c) at A[j*gr + c]
   f32x16 acc[C::MB][C::NB];
-  gemm_tile<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, gr, lds, nullptr, acc);
+  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc);
   for (int i = threadIdx.x; i < C::BM; i += C::THREADS) {
     const int t = m0 + i;
     float s = 0.f;
@@ -409,18 +493,21 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   E* dx = static_cast<E*>(a.dx);
   FragPos<C> fp(m0, n0);
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    const int col = fp.col(nb);
-    if (col >= a.d) continue;
-    const float gj = to_f32(gamma[col]);
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int row = fp.row(mb);
+    if (row >= a.T) continue;
+    const float sr = srow[row - m0];
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = fp.row(mb, v);
-        if (row >= a.T) continue;
+      for (int q = 0; q < 4; ++q) {
+        const int col = fp.col(nb, q);
+        if (col >= a.d) continue;
         const int64_t idx = (int64_t)row * a.d + col;
-        dx[idx] = from_f32<E>(gj * acc[mb][nb][v] - to_f32(x[idx]) * srow[row - m0]);
+        const float4 g4 = load4(gamma + col), x4 = load4(x + idx);
+        const f32x16& v = acc[mb][nb];
+        store4(dx + idx, g4.x * v[4 * q] - x4.x * sr, g4.y * v[4 * q + 1] - x4.y * sr,
+               g4.z * v[4 * q + 2] - x4.z * sr, g4.w * v[4 * q + 3] - x4.w * sr);
       }
   }
 }
@@ -430,7 +517,7 @@ template <typename E>
 struct Cfgs;
 template <>
 struct Cfgs<bf16> {
-  using Main = TileCfg<bf16, 256, 256, 2, 2>;
+  using Main = PipeCfg<256, 256, 32, 2, 2, 4>;
 };
 template <>
 struct Cfgs<float> {
@@ -484,7 +571,7 @@ hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s) {
   using C = typename Cfgs<E>::Main;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
-  hipLaunchKernelGGL((k_up<C>), dim3(tiles, n_up), dim3(C::THREADS), 0, s, a);
+  hipLaunchKernelGGL((k_up<C>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -504,9 +591,26 @@ int dz_nparts(int r) {
   return cdiv(r, C::BN) * C::WN;
 }
 template <typename E>
-int wgrad_nparts(int gr) {
+int gemm_bk() {
+  return Cfgs<E>::Main::BK;
+}
+template int gemm_bk<bf16>();
+template int gemm_bk<float>();
+
+template <typename E>
+int wgrad_nparts_used(int gr, int nsplit) {
   using C = typename Cfgs<E>::Main;
-  return cdiv(gr, C::BN) * C::WN;
+  return nsplit > 1 ? gr / 64 : cdiv(gr, C::BN) * C::WN;
+}
+template int wgrad_nparts_used<bf16>(int, int);
+template int wgrad_nparts_used<float>(int, int);
+
+template <typename E>
+int wgrad_nparts(int gr) {
+  // one partial per (column tile, wave column) without splits, one per 64 columns with
+  using C = typename Cfgs<E>::Main;
+  const int a = cdiv(gr, C::BN) * C::WN, b = gr / 64;
+  return a > b ? a : b;
 }
 
 template <typename E>
@@ -514,8 +618,20 @@ hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
   using C = typename Cfgs<E>::Main;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN);
-  hipLaunchKernelGGL((k_dz<C>), dim3(tiles, n_up), dim3(C::THREADS), 0, s, a);
+  hipLaunchKernelGGL((k_dz<C>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename E>
+int wgrad_splits(int T, int d, int r, int g, int n_up) {
+  using C = typename Cfgs<E>::Main;
+  const int gr = g * r;
+  const int tiles = n_up * cdiv(r, C::BM) * cdiv(d, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
+  // aim for at least two waves of work-groups on 256 CUs, with >= 16 k steps per split
+  const int ksteps = cdiv(T, C::BK);
+  int s = 1;
+  while (tiles * s < 512 && ksteps / (2 * s) >= 16 && s < 16) s *= 2;
+  return s;
 }
 
 template <typename E>
@@ -524,8 +640,12 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   const int gr = a.g * a.r;
   const int tilesB = cdiv(a.r, C::BM) * cdiv(a.d, C::BN);
   const int tilesA = cdiv(a.d, C::BM) * cdiv(gr, C::BN);
-  const int tiles = tilesA > tilesB ? tilesA : tilesB;
-  hipLaunchKernelGGL((k_wgrad<C>), dim3(tiles, a.n_up + 1), dim3(C::THREADS), 0, s, a);
+  const int total = (a.n_up * tilesB + tilesA) * a.nsplit;
+  hipLaunchKernelGGL((k_wgrad<C>), dim3(total), dim3(C::THREADS), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const int64_t n4 = ((int64_t)a.n_up * a.r * a.d + (int64_t)a.d * gr) / 4;
+  hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -538,9 +658,9 @@ hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, hipStream_t s) {
+hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, int stride, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_sum_parts<0>, dim3(cdiv(n, 256)), dim3(256), 0, s, parts, out, n, nparts);
+  hipLaunchKernelGGL(k_sum_parts, dim3(cdiv(n, 256)), dim3(256), 0, s, parts, out, n, nparts, stride);
   return hipGetLastError();
 }
 
@@ -564,5 +684,7 @@ template int dz_nparts<bf16>(int);
 template int dz_nparts<float>(int);
 template int wgrad_nparts<bf16>(int);
 template int wgrad_nparts<float>(int);
+template int wgrad_splits<bf16>(int, int, int, int, int);
+template int wgrad_splits<float>(int, int, int, int, int);
 
 }  // namespace lr

@@ -1,0 +1,255 @@
+// bf16 GEMM mainloop with direct global->LDS loads (gfx950).
+//
+// Operand tiles go from HBM straight into a ring of STAGES LDS buffers with
+// `buffer_load_dwordx4 ... lds` (each lane's 16 bytes land at M0 + 16*lane, an
+// out-of-range lane writes zeros), STAGES-1 stages ahead of the MFMAs, so no
+// register staging and no VALU transposes are needed.  The LDS layout depends on
+// how the operand is stored in memory:
+//   KC  (K contiguous): [rows][BK] rows of BK*2 bytes, 16-byte chunks XOR-swizzled;
+//                       MFMA fragments come from ds_read_b128.
+//   MNC (M/N contiguous): [BK][rows] rows of rows*2 bytes, 32-byte granules
+//                       XOR-swizzled; fragments come from two ds_read_b64_tr_b16.
+//                       That instruction treats each 16-lane group's 16 addresses
+//                       as a 4 x 16 block (lane j names row j/4, columns 4*(j%4)..+3)
+//                       and hands lane i column i of it, which is exactly the
+//                       K-packed operand layout of v_mfma_f32_32x32x16_bf16.
+// Both swizzles make a quarter/half-wave's reads hit distinct banks of a 256-byte
+// window; the DMA writes are 1 KiB contiguous per instruction.
+//
+// One barrier per k step: wait for this wave's loads of stage kt, barrier (all
+// waves' loads visible, all waves done reading stage kt-1), issue the loads of
+// stage kt+STAGES-1 into stage kt-1's buffer, then the MFMAs of stage kt.  The
+// loads are inline assembly, so the compiler neither tracks them nor inserts
+// waits for them; the waits are explicit (vmcnt counts this wave's own loads,
+// which complete in order).
+#pragma once
+
+#include "lr_device.h"
+
+namespace lr {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#define LR_LDS __attribute__((address_space(3)))
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+struct PipeCfg {
+  using E = bf16;
+  static constexpr bool PIPE = true;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int VEC = 8;
+  static constexpr int NWAVES = WM * WN, THREADS = NWAVES * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, MB = WTM / 32, NB = WTN / 32;
+  static constexpr int KS = BK / 16;                       // MFMA k sub-steps per stage
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LPS_A = A_BYTES / (1024 * NWAVES), LPS_B = B_BYTES / (1024 * NWAVES);
+  static constexpr int LPS = LPS_A + LPS_B;                // DMA instructions per stage per wave
+  static constexpr int LDS_UINT4 = STAGES * STAGE_BYTES / 16;
+  static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "tile / wave mismatch");
+  static_assert(BK % 16 == 0 && (BK * 2 == 64 || BK * 2 == 128), "BK must be 32 or 64");
+  static_assert((STAGES - 2) * LPS <= 63, "vmcnt range");
+};
+
+// 16-byte chunk swizzle of a KC tile row (RB = row bytes, 64 or 128)
+template <int RB>
+__device__ __forceinline__ int kc_swz(int row) {
+  constexpr int RPW = 256 / RB, CPR = RB / 16;
+  return (row / RPW) % CPR;
+}
+// 32-byte granule swizzle of an MNC tile row (k index)
+__device__ __forceinline__ int mnc_swz(int krow) { return 2 * (krow & 3); }
+
+struct Rsrc4 {
+  int x, y, z, w;
+};
+__device__ __forceinline__ Rsrc4 rsrc4(const void* p, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
+  return Rsrc4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)n, 0x00020000};
+}
+
+__device__ __forceinline__ void dma16(const Rsrc4& r, uint32_t voff, uint32_t lds_byte) {
+  typedef int int4v __attribute__((ext_vector_type(4)));
+  const int4v rs = {r.x, r.y, r.z, r.w};
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_byte)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Per-lane DMA offsets of one operand tile (relative to the tile origin at k0).
+template <class C, int ROWS, bool MNC>
+struct DmaTile {
+  static constexpr int BYTES = ROWS * C::BK * 2;
+  static constexpr int Q = BYTES / (1024 * C::NWAVES);  // instructions per wave per stage
+  uint32_t off[Q];
+
+  template <class Map>
+  __device__ __forceinline__ void init(const Opnd& o, const Map& map, int mn0, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int p = (q * C::NWAVES + wave) * 1024 + 16 * lane;  // LDS byte within the tile
+      if (!MNC) {
+        constexpr int RB = C::BK * 2;
+        const int row = p / RB, ch = ((p % RB) / 16) ^ kc_swz<RB>(row);
+        const int gmn = map(mn0, row);
+        off[q] = gmn >= 0 ? (uint32_t)(((int64_t)(gmn - mn0) * o.ld + ch * 8) * 2) : kOffInvalid;
+      } else {
+        constexpr int RB = ROWS * 2;
+        const int krow = p / RB, b = p % RB;
+        const int g = (b / 32) ^ mnc_swz(krow);
+        const int mn = g * 16 + ((b % 32) / 16) * 8;
+        const int gmn = map(mn0, mn);
+        off[q] = gmn >= 0 ? (uint32_t)(((int64_t)krow * o.ld + (gmn - mn0)) * 2) : kOffInvalid;
+      }
+    }
+  }
+
+  __device__ __forceinline__ Rsrc4 rsrc(const Opnd& o, int mn0, int k0) const {
+    const char* base = static_cast<const char*>(o.p);
+    if (!MNC) {
+      const int64_t rows = (int64_t)o.MN - mn0;
+      return rsrc4(base + ((int64_t)mn0 * o.ld + k0) * 2, rows <= 0 ? 0 : ((rows - 1) * o.ld + (o.K - k0)) * 2);
+    } else {
+      const int64_t rows = (int64_t)o.K - k0;
+      return rsrc4(base + ((int64_t)k0 * o.ld + mn0) * 2, rows <= 0 ? 0 : ((rows - 1) * o.ld + (o.MN - mn0)) * 2);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const Rsrc4& r, uint32_t lds_tile, int wave) const {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) dma16(r, off[q], lds_tile + (q * C::NWAVES + wave) * 1024);
+  }
+};
+
+// one MFMA operand fragment (32 rows x 16 k) of the tile whose LDS image starts at `t`
+template <class C, int ROWS, bool MNC>
+__device__ __forceinline__ uint4 frag(const char LR_LDS* t, int rbase, int s, int lane) {
+  if (!MNC) {
+    constexpr int RB = C::BK * 2;
+    const int row = rbase + (lane & 31);
+    const int ch = (2 * s + (lane >> 5)) ^ kc_swz<RB>(row);
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4 LR_LDS*>(t + row * RB + ch * 16));
+  } else {
+    constexpr int RB = ROWS * 2;
+    const int G = lane >> 4, j = lane & 15;
+    const int mn = rbase + 16 * (G & 1) + 4 * (j & 3);
+    const int kr0 = 16 * s + 8 * (G >> 1) + (j >> 2);
+    const int kr1 = kr0 + 4;
+    const bf16x4 LR_LDS* p0 =
+        reinterpret_cast<const bf16x4 LR_LDS*>(t + kr0 * RB + (((mn >> 4) ^ mnc_swz(kr0)) * 32) + (mn & 15) * 2);
+    const bf16x4 LR_LDS* p1 =
+        reinterpret_cast<const bf16x4 LR_LDS*>(t + kr1 * RB + (((mn >> 4) ^ mnc_swz(kr1)) * 32) + (mn & 15) * 2);
+    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<bf16x4 LR_LDS*>(p0));
+    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<bf16x4 LR_LDS*>(p1));
+    const uint2 u0 = __builtin_bit_cast(uint2, v0), u1 = __builtin_bit_cast(uint2, v1);
+    return make_uint4(u0.x, u0.y, u1.x, u1.y);
+  }
+}
+
+// sum of squares of the 8 bf16 values of a fragment register
+__device__ __forceinline__ float frag_sumsq(const uint4& q) { return sumsq_vec(q, (bf16*)nullptr); }
+
+// Mainloop over k in [kbeg, kbeg + K); same contract as gemm_tile (accumulator
+// layout, ROWSTAT result in rowss[0..BM)).
+template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB>
+__device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
+                                          int n0, int kbeg, int K, uint4* lds, float* rowss,
+                                          f32x16 (&acc)[C::MB][C::NB]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  float ss[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) ss[mb] = 0.f;
+
+  DmaTile<C, C::BM, A_MNC> da;
+  DmaTile<C, C::BN, B_MNC> db;
+  da.init(oa, ma, m0, wave, lane);
+  db.init(ob, mbm, n0, wave, lane);
+  const char LR_LDS* ldsp = (const char LR_LDS*)(lds);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
+  const int nk = (K + C::BK - 1) / C::BK;
+
+  auto issue_stage = [&](int st) {
+    // stages past the end read nothing (empty resource) and fill an unused buffer with zeros
+    const int k0 = kbeg + st * C::BK;
+    const bool live = st < nk;
+    const uint32_t buf = lds0 + (st % C::STAGES) * C::STAGE_BYTES;
+    da.issue(live ? da.rsrc(oa, m0, k0) : rsrc4(oa.p, 0), buf, wave);
+    db.issue(live ? db.rsrc(ob, n0, k0) : rsrc4(ob.p, 0), buf + C::A_BYTES, wave);
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int st = 0; st < C::STAGES - 1; ++st) issue_stage(st);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<(C::STAGES - 2) * C::LPS>();
+      block_barrier();
+      issue_stage(kt + C::STAGES - 1);
+      const char LR_LDS* ta = ldsp + (kt % C::STAGES) * C::STAGE_BYTES;
+      const char LR_LDS* tb = ta + C::A_BYTES;
+      uint4 a[2][C::MB], b[2][C::NB];
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) a[0][mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, 0, lane);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) b[0][nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, 0, lane);
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        if (s + 1 < C::KS) {
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb)
+            a[(s + 1) & 1][mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, s + 1, lane);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            b[(s + 1) & 1][nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, s + 1, lane);
+        }
+        if constexpr (ROWSTAT) {
+          if (wn == 0) {
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) ss[mb] += frag_sumsq(a[s & 1][mb]);
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) mfma_chunk(acc[mb][nb], b[s & 1][nb], a[s & 1][mb], (bf16*)nullptr);
+      }
+    }
+    wait_vmcnt<0>();
+  }
+  if constexpr (ROWSTAT) {
+    static_assert(!A_MNC, "row statistics need a K-contiguous A");
+    if (wn == 0) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const float s = ss[mb] + __shfl_xor(ss[mb], 32);
+        if (lane < 32) rowss[wm * C::WTM + mb * 32 + lane] = s;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB>
+__device__ __forceinline__ void mainloop(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
+                                         int n0, int kbeg, int K, uint4* lds, float* rowss,
+                                         f32x16 (&acc)[C::MB][C::NB]) {
+  if constexpr (C::PIPE)
+    gemm_pipe<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc);
+  else
+    gemm_tile<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc);
+}
+
+}  // namespace lr
