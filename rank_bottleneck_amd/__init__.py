@@ -46,11 +46,13 @@ ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_parti
                 "lr_trace_elapsed", "lr_trace_end")
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load liblrblock.so (once).  Raises if it has not been built."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load liblrblock.so (once): the in-tree build, or the file named by the
+    LR_BLOCK_LIBRARY environment variable.  Raises if it does not exist."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("LR_BLOCK_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m rank_bottleneck_amd.build`")
     lib = ctypes.CDLL(path)

@@ -7,7 +7,7 @@
 
 #include <new>
 
-#include "../../include/lr_block.h"
+#include "lr_block.h"
 #include "lr_kernels.h"
 
 namespace {
@@ -86,10 +86,10 @@ struct TraceGuard {
     if (!t.on || t.n >= t.cap || (t.filter[0] && strcmp(t.filter, name) != 0)) return;
     slot = t.n++;
     t.names[slot] = name;
-    hipEventRecord(t.ev[2 * slot], s);
+    (void)hipEventRecord(t.ev[2 * slot], s);
   }
   ~TraceGuard() {
-    if (slot >= 0) hipEventRecord(g_trace.ev[2 * slot + 1], s);
+    if (slot >= 0) (void)hipEventRecord(g_trace.ev[2 * slot + 1], s);
   }
 };
 
@@ -322,7 +322,7 @@ lr_status lr_trace_begin(const char* kernel, int max_launches) {
   t.names = new const char*[max_launches];
   for (int i = 0; i < 2 * max_launches; ++i) {
     if (hipEventCreate(&t.ev[i]) != hipSuccess) {
-      for (int j = 0; j < i; ++j) hipEventDestroy(t.ev[j]);
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(t.ev[j]);
       delete[] t.ev;
       delete[] t.names;
       t = Trace{};
@@ -354,7 +354,7 @@ lr_status lr_trace_elapsed(int i, const char** kernel, float* ms) {
 lr_status lr_trace_end(void) {
   Trace& t = g_trace;
   if (!t.on) return LR_EINVAL;
-  for (int i = 0; i < 2 * t.cap; ++i) hipEventDestroy(t.ev[i]);
+  for (int i = 0; i < 2 * t.cap; ++i) (void)hipEventDestroy(t.ev[i]);
   delete[] t.ev;
   delete[] t.names;
   t = Trace{};

@@ -106,6 +106,7 @@ template <typename E_, int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
   using E = E_;
   static constexpr bool PIPE = false;
+  static constexpr int WPE = 1;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
   static constexpr int CH = 8;                      // chunks per LDS row
@@ -392,6 +393,86 @@ struct FragPos {
   __device__ __forceinline__ int row(int mb) const { return row0 + mb * 32; }
   __device__ __forceinline__ int col(int nb, int q) const { return col0 + nb * 32 + 8 * q; }
 };
+
+#define LR_LDS __attribute__((address_space(3)))
+
+// Row-sweep epilogue.  A wave's WTM x WTN fp32 accumulators are staged through
+// its own LDS region one 32-row block at a time (rows padded by 16 bytes, so the
+// column-major writes of 16 lanes hit distinct banks); lanes then sweep the block
+// row by row, each taking 4 consecutive columns, so every global access of the
+// epilogue is a contiguous run of whole cache lines.
+template <class C>
+struct RowStage {
+  static constexpr int PITCH = C::WTN * 4 + 16;  // bytes per staged row
+  static constexpr int REGION = 32 * PITCH;      // bytes per wave
+  static constexpr int UINT4 = C::NWAVES * REGION / 16;
+};
+
+template <class C>
+__device__ __forceinline__ char LR_LDS* stage_region(uint4* lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return (char LR_LDS*)(lds) + wave * RowStage<C>::REGION;
+}
+
+template <class C>
+__device__ __forceinline__ void stage_block(const f32x16 (&acc)[C::MB][C::NB], int mb, char LR_LDS* region) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  char LR_LDS* rowp = region + (lane & 31) * RowStage<C>::PITCH + 16 * (lane >> 5);
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+      *reinterpret_cast<f4 LR_LDS*>(rowp + (nb * 32 + 8 * q) * 4) = v;
+    }
+}
+
+__device__ __forceinline__ float4 lds_f4(const char LR_LDS* p) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 v = *reinterpret_cast<const f4 LR_LDS*>(p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Sweep the staged block: COLS leading columns of each of the 32 rows; f(rl, cl,
+// row pointer) is called with the block-local row, the wave-local column (a
+// multiple of 4) and the staged row.  LPR = COLS/4 lanes share one row.
+template <class C, int COLS, class F>
+__device__ __forceinline__ void sweep_block(const char LR_LDS* region, F&& f) {
+  constexpr int LPR = COLS / 4, RPI = 64 / LPR;
+  static_assert(LPR <= 64 && 64 % LPR == 0, "row sweep width");
+  const int lane = threadIdx.x & 63;
+#pragma unroll 4
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rl = it * RPI + lane / LPR, cl = (lane % LPR) * 4;
+    f(rl, cl, region + rl * RowStage<C>::PITCH);
+  }
+}
+
+// Same sweep in two phases: load(it, rl, cl, in[it]) for every iteration first
+// (global loads of epilogue inputs, all in flight together), then
+// f(it, rl, cl, row pointer, in[it]).
+template <class C, int COLS, int NL, class FL, class F>
+__device__ __forceinline__ void sweep_block_pre(const char LR_LDS* region, FL&& load, F&& f) {
+  constexpr int LPR = COLS / 4, RPI = 64 / LPR, IT = 32 / RPI;
+  const int lane = threadIdx.x & 63;
+  float4 in[IT][NL];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) load(it * RPI + lane / LPR, (lane % LPR) * 4, in[it]);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int rl = it * RPI + lane / LPR, cl = (lane % LPR) * 4;
+    f(rl, cl, region + rl * RowStage<C>::PITCH, in[it]);
+  }
+}
+
+// sum over the LPR lanes that share a row in sweep_block
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 
 // 4 consecutive values -> memory (8 bytes of bf16 / 16 bytes of fp32)
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {

@@ -125,14 +125,22 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   out[i] = s;
 }
 
+// LDS words a GEMM kernel needs: the mainloop ring or the epilogue staging,
+// whichever is larger, plus BM floats of per-row values.
+template <class C>
+struct KernLds {
+  static constexpr int MAIN = C::LDS_UINT4 > RowStage<C>::UINT4 ? C::LDS_UINT4 : RowStage<C>::UINT4;
+  static constexpr int TOTAL = MAIN + C::BM / 4;
+};
+
 // ------------------------------------------------------------------ down projection
 // acc = x . A' over K = d; mode DOWN_BLOCK: h = rstd*acc, z = sigma(h);
 // mode DOWN_PARTIAL: fp32 partial = acc and sumsq (tile column 0 writes it).
 template <class C, bool GATEUP>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_down(DownArgs a) {
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_down(DownArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[C::LDS_UINT4 + C::BM / 4];
-  float* rowss = reinterpret_cast<float*>(lds + C::LDS_UINT4);
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  float* rowss = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);
   const int gr = a.g * a.r;
   constexpr int TN = GATEUP ? C::BN / 2 : C::BN;  // logical columns per tile
   const int tiles_n = ((GATEUP ? a.r : gr) + TN - 1) / TN;
@@ -150,80 +158,54 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
     mainloop<C, false, true, true>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, rowss, acc);
   }
 
-  const int wn = (threadIdx.x >> 6) % C::WN;
-  FragPos<C> fp(m0, 0);
-  // column of register block (nb, q) before any gate/up remapping
-  const int cbase = wn * C::WTN + 4 * (fp.lane >> 5);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  char LR_LDS* reg = stage_region<C>(lds);
+  E* h = static_cast<E*>(a.h);
+  E* z = static_cast<E*>(a.z);
   if (a.mode == DOWN_PARTIAL) {
     if (tn == 0 && threadIdx.x < C::BM && m0 + (int)threadIdx.x < a.T)
       a.sumsq[m0 + threadIdx.x] = rowss[threadIdx.x];
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-      const int row = fp.row(mb);
-      if (row >= a.T) continue;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int col;
-          if constexpr (GATEUP) {
-            col = MapGateUp<C::WTN>{a.r}(n0, cbase + nb * 32 + 8 * q);
-          } else {
-            col = n0 + cbase + nb * 32 + 8 * q;
-          }
-          if (col < 0 || col >= gr) continue;
-          const f32x16& v = acc[mb][nb];
-          store4(a.partial + (int64_t)row * gr + col, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
-    }
-    return;
   }
-
-  E* h = static_cast<E*>(a.h);
-  E* z = static_cast<E*>(a.z);
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
-    const int row = fp.row(mb);
-    if (row >= a.T) continue;
-    const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
+    stage_block<C>(acc, mb, reg);
+    const int rbase = m0 + wm * C::WTM + mb * 32;
     if constexpr (GATEUP) {
-#pragma unroll
-      for (int nb = 0; nb < C::NB / 2; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int logical = n0 + wn * (C::WTN / 2) + nb * 32 + 8 * q + 4 * (fp.lane >> 5);
-          if (logical >= a.r) continue;
-          float hg[4], hu[4], zz[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hg[e] = acc[mb][nb][4 * q + e] * rs;
-            hu[e] = acc[mb][nb + C::NB / 2][4 * q + e] * rs;
-            zz[e] = hg[e] * sigmoidf_(hg[e]) * hu[e];
-          }
-          if (h) {
-            store4(h + (int64_t)row * gr + logical, hg[0], hg[1], hg[2], hg[3]);
-            store4(h + (int64_t)row * gr + a.r + logical, hu[0], hu[1], hu[2], hu[3]);
-          }
-          store4(z + (int64_t)row * a.r + logical, zz[0], zz[1], zz[2], zz[3]);
+      sweep_block<C, C::WTN / 2>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+        const int row = rbase + rl;
+        const int logical = n0 + wn * (C::WTN / 2) + cl;
+        if (row >= a.T || logical >= a.r) return;
+        const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
+        const float4 g4 = lds_f4(rp + cl * 4), u4 = lds_f4(rp + (cl + C::WTN / 2) * 4);
+        const float hg[4] = {g4.x * rs, g4.y * rs, g4.z * rs, g4.w * rs};
+        const float hu[4] = {u4.x * rs, u4.y * rs, u4.z * rs, u4.w * rs};
+        if (h) {
+          store4(h + (int64_t)row * gr + logical, hg[0], hg[1], hg[2], hg[3]);
+          store4(h + (int64_t)row * gr + a.r + logical, hu[0], hu[1], hu[2], hu[3]);
         }
+        store4(z + (int64_t)row * a.r + logical, hg[0] * sigmoidf_(hg[0]) * hu[0], hg[1] * sigmoidf_(hg[1]) * hu[1],
+               hg[2] * sigmoidf_(hg[2]) * hu[2], hg[3] * sigmoidf_(hg[3]) * hu[3]);
+      });
     } else {
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + cbase + nb * 32 + 8 * q;
-          if (col >= gr) continue;
-          float hv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hv[e] = acc[mb][nb][4 * q + e] * rs;
-          if (h) store4(h + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
-          if (a.act == ACT_SILU) {
-            store4(z + (int64_t)row * gr + col, hv[0] * sigmoidf_(hv[0]), hv[1] * sigmoidf_(hv[1]),
-                   hv[2] * sigmoidf_(hv[2]), hv[3] * sigmoidf_(hv[3]));
-          } else if (!h) {
-            store4(z + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
-          }
+      sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+        const int row = rbase + rl;
+        const int col = n0 + wn * C::WTN + cl;
+        if (row >= a.T || col >= gr) return;
+        const float4 v = lds_f4(rp + cl * 4);
+        if (a.mode == DOWN_PARTIAL) {
+          store4(a.partial + (int64_t)row * gr + col, v.x, v.y, v.z, v.w);
+          return;
         }
+        const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
+        const float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
+        if (h) store4(h + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
+        if (a.act == ACT_SILU) {
+          store4(z + (int64_t)row * gr + col, hv[0] * sigmoidf_(hv[0]), hv[1] * sigmoidf_(hv[1]),
+                 hv[2] * sigmoidf_(hv[2]), hv[3] * sigmoidf_(hv[3]));
+        } else if (!h) {
+          store4(z + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
+        }
+      });
     }
   }
 }
@@ -231,9 +213,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
 // ------------------------------------------------------------------ up projection
 // y_i = z_i . B_i ; one launch over (branch, tile)
 template <class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_up(UpArgs a) {
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_up(UpArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[C::LDS_UINT4];
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
   const int tiles_n = (a.d + C::BN - 1) / C::BN;
   const int tiles_m = (a.T + C::BM - 1) / C::BM;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -246,27 +228,27 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   f32x16 acc[C::MB][C::NB];
   mainloop<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.r, lds, nullptr, acc);
   E* y = static_cast<E*>(a.y[br]);
-  FragPos<C> fp(m0, n0);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  char LR_LDS* reg = stage_region<C>(lds);
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
-    const int row = fp.row(mb);
-    if (row >= a.T) continue;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = fp.col(nb, q);
-        const f32x16& v = acc[mb][nb];
-        if (col < a.d) store4(y + (int64_t)row * a.d + col, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      }
+    stage_block<C>(acc, mb, reg);
+    const int rbase = m0 + wm * C::WTM + mb * 32;
+    sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+      const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+      if (row >= a.T || col >= a.d) return;
+      const float4 v = lds_f4(rp + cl * 4);
+      store4(y + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
+    });
   }
 }
 
 // ------------------------------------------------------------------ backward: dz -> dh'
-template <class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dz(DzArgs a) {
+template <class C, int ACT>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dz(DzArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[C::LDS_UINT4];
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  float* rs_tile = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] rstd of the tile's rows
   const int tiles_n = (a.r + C::BN - 1) / C::BN;
   const int tiles_m = (a.T + C::BM - 1) / C::BM;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -278,6 +260,8 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   Opnd ob{a.B[br], a.d, a.r, a.d};  // B_i^T: (n = c, k = j) at B_i[c*d + j]
   f32x16 acc[C::MB][C::NB];
   mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc);
+  for (int i = threadIdx.x; i < C::BM; i += C::THREADS) rs_tile[i] = m0 + i < a.T ? a.rstd[m0 + i] : 0.f;
+  __syncthreads();
 
   const int gr = a.g * a.r;
   const E* h = static_cast<const E*>(a.h);
@@ -301,7 +285,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
         if (!rok || c >= a.r) continue;
         const f32x16& v = acc[mb][nb];
         const float dzv[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-        if (a.act == ACT_SWIGLU) {
+        if constexpr (ACT == ACT_SWIGLU) {
           const float4 g4 = load4(h + hrow + c), u4 = load4(h + hrow + a.r + c);
           const float hg[4] = {g4.x, g4.y, g4.z, g4.w}, hu[4] = {u4.x, u4.y, u4.z, u4.w};
           float dg[4], du[4], zz[4];
@@ -322,7 +306,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
           const float4 h4 = load4(h + idx);
           const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
           float d1[4];
-          if (a.act == ACT_SILU) {
+          if constexpr (ACT == ACT_SILU) {
             float zz[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -351,9 +335,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
 // Each split covers a token range; with more than one split the fp32 tile
 // goes to the partial buffer [split][job-major M x N] and k_wgrad_reduce finishes.
 template <class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_wgrad(WgradArgs a) {
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_wgrad(WgradArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[C::LDS_UINT4];
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
   const int gr = a.g * a.r;
   const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
   const int tmA = (a.d + C::BM - 1) / C::BM, tnA = (gr + C::BN - 1) / C::BN;
@@ -382,9 +366,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   f32x16 acc[C::MB][C::NB];
   mainloop<C, true, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, kbeg, klen > 0 ? klen : 0, lds, nullptr, acc);
 
-  FragPos<C> fp(m0, n0);
   float* out;
-  int64_t ldo = N;
   if (a.nsplit > 1) {
     out = a.wpart + (int64_t)split * a.part_stride + (isA ? a.part_offA : (int64_t)job * a.r * a.d);
   } else {
@@ -393,31 +375,38 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   const bool finalA = isA && a.nsplit == 1;
   const E* Aw = static_cast<const E*>(a.A);
   const E* gamma = static_cast<const E*>(a.gamma);
-  const int wn = (threadIdx.x >> 6) % C::WN;
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  constexpr int LPR = C::WTN / 4;
+  char LR_LDS* reg = stage_region<C>(lds);
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
-    const int row = fp.row(mb);
-    if (row >= M) continue;
-    const float gj = finalA ? to_f32(gamma[row]) : 1.0f;
-    float s = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = fp.col(nb, q);
-        if (col >= N) continue;
-        const f32x16& v = acc[mb][nb];
-        if (finalA) {
-          const float4 a4 = load4(Aw + (int64_t)row * gr + col);
-          s += a4.x * v[4 * q] + a4.y * v[4 * q + 1] + a4.z * v[4 * q + 2] + a4.w * v[4 * q + 3];
-        }
-        store4(out + (int64_t)row * ldo + col, gj * v[4 * q], gj * v[4 * q + 1], gj * v[4 * q + 2],
-               gj * v[4 * q + 3]);
-      }
-    if (finalA) {
-      s += __shfl_xor(s, 32);
-      if (fp.lane < 32) a.gpart[(int64_t)row * a.ngpart + tn * C::WN + wn] = s;
-    }
+    stage_block<C>(acc, mb, reg);
+    const int rbase = m0 + wm * C::WTM + mb * 32;
+    // in[0] = A row segment, in[1].x = gamma_j (final dA only)
+    sweep_block_pre<C, C::WTN, 2>(
+        reg,
+        [&](int rl, int cl, float4* in) {
+          const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+          in[0] = in[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (finalA && row < M && col < N) {
+            in[0] = load4(Aw + (int64_t)row * gr + col);
+            in[1].x = to_f32(gamma[row]);
+          }
+        },
+        [&](int rl, int cl, const char LR_LDS* rp, const float4* in) {
+          const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+          float s = 0.f;
+          if (row < M && col < N) {
+            const float4 v = lds_f4(rp + cl * 4);
+            const float gj = finalA ? in[1].x : 1.0f;
+            if (finalA) s = in[0].x * v.x + in[0].y * v.y + in[0].z * v.z + in[0].w * v.w;
+            store4(out + (int64_t)row * N + col, gj * v.x, gj * v.y, gj * v.z, gj * v.w);
+          }
+          if (finalA) {
+            s = row_sum<LPR>(s);
+            if (row < M && (threadIdx.x & (LPR - 1)) == 0) a.gpart[(int64_t)row * a.ngpart + tn * C::WN + wn] = s;
+          }
+        });
   }
 }
 
@@ -463,10 +452,10 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
 
 // ------------------------------------------------------------------ backward: dx
 template <class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dx(DxArgs a) {
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dx(DxArgs a) {
   using E = typename C::E;
-  __shared__ uint4 lds[C::LDS_UINT4 + C::BM / 4];
-  float* srow = reinterpret_cast<float*>(lds + C::LDS_UINT4);  // [BM] : rstd*S'/D
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  float* srow = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] : rstd*S'/D
   const int gr = a.g * a.r;
   const int tiles_n = (a.d + C::BN - 1) / C::BN;
   const int tiles_m = (a.T + C::BM - 1) / C::BM;
@@ -618,7 +607,12 @@ hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
   using C = typename Cfgs<E>::Main;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN);
-  hipLaunchKernelGGL((k_dz<C>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  if (a.act == ACT_SWIGLU)
+    hipLaunchKernelGGL((k_dz<C, ACT_SWIGLU>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  else if (a.act == ACT_SILU)
+    hipLaunchKernelGGL((k_dz<C, ACT_SILU>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_dz<C, ACT_IDENTITY>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

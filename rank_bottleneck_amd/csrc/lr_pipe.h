@@ -16,12 +16,13 @@
 // Both swizzles make a quarter/half-wave's reads hit distinct banks of a 256-byte
 // window; the DMA writes are 1 KiB contiguous per instruction.
 //
-// One barrier per k step: wait for this wave's loads of stage kt, barrier (all
-// waves' loads visible, all waves done reading stage kt-1), issue the loads of
-// stage kt+STAGES-1 into stage kt-1's buffer, then the MFMAs of stage kt.  The
-// loads are inline assembly, so the compiler neither tracks them nor inserts
-// waits for them; the waits are explicit (vmcnt counts this wave's own loads,
-// which complete in order).
+// One barrier per k step, placed once the last fragments of stage kt are in
+// registers: wait for this wave's loads of stage kt+1, barrier (all waves' loads
+// visible, all waves done reading stage kt), refill stage kt's buffer with stage
+// kt+STAGES, read the first fragments of stage kt+1, then run the last MFMAs of
+// stage kt.  The loads are inline assembly, so the compiler neither tracks them
+// nor inserts waits for them; the waits are explicit (vmcnt counts this wave's
+// own loads, which complete in order).
 #pragma once
 
 #include "lr_device.h"
@@ -29,12 +30,12 @@
 namespace lr {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-#define LR_LDS __attribute__((address_space(3)))
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int WPE_ = 1>
 struct PipeCfg {
   using E = bf16;
   static constexpr bool PIPE = true;
+  static constexpr int WPE = WPE_;  // waves per SIMD the kernels are built for
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr int VEC = 8;
   static constexpr int NWAVES = WM * WN, THREADS = NWAVES * 64;
@@ -47,7 +48,8 @@ struct PipeCfg {
   static constexpr int LDS_UINT4 = STAGES * STAGE_BYTES / 16;
   static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "tile / wave mismatch");
   static_assert(BK % 16 == 0 && (BK * 2 == 64 || BK * 2 == 128), "BK must be 32 or 64");
-  static_assert((STAGES - 2) * LPS <= 63, "vmcnt range");
+  static_assert((STAGES - 1) * LPS <= 63, "vmcnt range");
+  static_assert(KS % 2 == 0, "fragment double buffer assumes an even number of sub-steps");
 };
 
 // 16-byte chunk swizzle of a KC tile row (RB = row bytes, 64 or 128)
@@ -109,15 +111,28 @@ struct DmaTile {
     }
   }
 
-  __device__ __forceinline__ Rsrc4 rsrc(const Opnd& o, int mn0, int k0) const {
-    const char* base = static_cast<const char*>(o.p);
+  // Resource of the stage starting at kbeg + st*BK: base0 + st*step, with the bytes
+  // left to the operand's last element (bytes0 - st*step, clamped); `live == false`
+  // gives an empty range (reads zeros).  All scalar arithmetic.
+  const char* base0;
+  int64_t bytes0, step;
+  __device__ __forceinline__ void init_range(const Opnd& o, int mn0, int kbeg) {
     if (!MNC) {
-      const int64_t rows = (int64_t)o.MN - mn0;
-      return rsrc4(base + ((int64_t)mn0 * o.ld + k0) * 2, rows <= 0 ? 0 : ((rows - 1) * o.ld + (o.K - k0)) * 2);
+      base0 = static_cast<const char*>(o.p) + ((int64_t)mn0 * o.ld + kbeg) * 2;
+      bytes0 = ((int64_t)(o.MN - mn0 - 1) * o.ld + (o.K - kbeg)) * 2;
+      step = (int64_t)C::BK * 2;
+      if (o.MN - mn0 <= 0) bytes0 = -(int64_t)1 << 62;
     } else {
-      const int64_t rows = (int64_t)o.K - k0;
-      return rsrc4(base + ((int64_t)k0 * o.ld + mn0) * 2, rows <= 0 ? 0 : ((rows - 1) * o.ld + (o.MN - mn0)) * 2);
+      base0 = static_cast<const char*>(o.p) + ((int64_t)kbeg * o.ld + mn0) * 2;
+      bytes0 = ((int64_t)(o.K - kbeg - 1) * o.ld + (o.MN - mn0)) * 2;
+      step = (int64_t)C::BK * o.ld * 2;
     }
+  }
+  __device__ __forceinline__ Rsrc4 rsrc(int st, bool live) const {
+    int64_t b = bytes0 - (int64_t)st * step;
+    b = b < 0 ? 0 : (b > kMaxRecords ? kMaxRecords : b);
+    const uint64_t a = reinterpret_cast<uint64_t>(base0) + (uint64_t)((int64_t)st * step);
+    return Rsrc4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), live ? (int)b : 0, 0x00020000};
   }
 
   __device__ __forceinline__ void issue(const Rsrc4& r, uint32_t lds_tile, int wave) const {
@@ -178,53 +193,73 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
   DmaTile<C, C::BN, B_MNC> db;
   da.init(oa, ma, m0, wave, lane);
   db.init(ob, mbm, n0, wave, lane);
+  da.init_range(oa, m0, kbeg);
+  db.init_range(ob, n0, kbeg);
   const char LR_LDS* ldsp = (const char LR_LDS*)(lds);
   const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
   const int nk = (K + C::BK - 1) / C::BK;
 
   auto issue_stage = [&](int st) {
-    // stages past the end read nothing (empty resource) and fill an unused buffer with zeros
-    const int k0 = kbeg + st * C::BK;
+    // stages past the end read nothing (empty resource) and fill a buffer no one reads with zeros
     const bool live = st < nk;
     const uint32_t buf = lds0 + (st % C::STAGES) * C::STAGE_BYTES;
-    da.issue(live ? da.rsrc(oa, m0, k0) : rsrc4(oa.p, 0), buf, wave);
-    db.issue(live ? db.rsrc(ob, n0, k0) : rsrc4(ob.p, 0), buf + C::A_BYTES, wave);
+    da.issue(da.rsrc(st, live), buf, wave);
+    db.issue(db.rsrc(st, live), buf + C::A_BYTES, wave);
+  };
+  auto read_frags = [&](int st, int s, uint4 (&fa)[C::MB], uint4 (&fb)[C::NB]) {
+    const char LR_LDS* ta = ldsp + (st % C::STAGES) * C::STAGE_BYTES;
+    const char LR_LDS* tb = ta + C::A_BYTES;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, s, lane);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, s, lane);
+  };
+  // LDS reads of the next fragments interleaved one-for-one with this sub-step's MFMAs
+  auto interleave = [&]() {
+    constexpr int NREAD = C::MB * (A_MNC ? 2 : 1) + C::NB * (B_MNC ? 2 : 1);
+    constexpr int NMFMA = C::MB * C::NB;
+#pragma unroll
+    for (int i = 0; i < (NREAD < NMFMA ? NREAD : NMFMA); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    if constexpr (NMFMA > NREAD) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
   };
 
   if (nk > 0) {
+    // prefetch distance: STAGES stages; the buffer of stage kt is refilled with stage
+    // kt+STAGES as soon as every wave holds its last fragments of stage kt
 #pragma unroll
-    for (int st = 0; st < C::STAGES - 1; ++st) issue_stage(st);
+    for (int st = 0; st < C::STAGES; ++st) issue_stage(st);
+    wait_vmcnt<(C::STAGES - 1) * C::LPS>();
+    block_barrier();
+    uint4 a[2][C::MB], b[2][C::NB];
+    read_frags(0, 0, a[0], b[0]);
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<(C::STAGES - 2) * C::LPS>();
-      block_barrier();
-      issue_stage(kt + C::STAGES - 1);
-      const char LR_LDS* ta = ldsp + (kt % C::STAGES) * C::STAGE_BYTES;
-      const char LR_LDS* tb = ta + C::A_BYTES;
-      uint4 a[2][C::MB], b[2][C::NB];
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) a[0][mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, 0, lane);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) b[0][nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, 0, lane);
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
+        const int cur = s & 1, nxt = cur ^ 1;
         if (s + 1 < C::KS) {
-#pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb)
-            a[(s + 1) & 1][mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, s + 1, lane);
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-            b[(s + 1) & 1][nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, s + 1, lane);
+          read_frags(kt, s + 1, a[nxt], b[nxt]);
+        } else {
+          // all of stage kt is in registers: wait for stage kt+1, refill stage kt's buffer
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_vmcnt<(C::STAGES - 2) * C::LPS>();
+          block_barrier();
+          issue_stage(kt + C::STAGES);
+          read_frags(kt + 1, 0, a[nxt], b[nxt]);  // past the end: unused reads of a zero-filled buffer
         }
         if constexpr (ROWSTAT) {
           if (wn == 0) {
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) ss[mb] += frag_sumsq(a[s & 1][mb]);
+            for (int mb = 0; mb < C::MB; ++mb) ss[mb] += frag_sumsq(a[cur][mb]);
           }
         }
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) mfma_chunk(acc[mb][nb], b[s & 1][nb], a[s & 1][mb], (bf16*)nullptr);
+          for (int nb = 0; nb < C::NB; ++nb) mfma_chunk(acc[mb][nb], b[cur][nb], a[cur][mb], (bf16*)nullptr);
+        interleave();
       }
     }
     wait_vmcnt<0>();
