@@ -27,7 +27,7 @@ METRIC = "low-rank block fwd+bwd TFLOP/s (bf16) and % MFMA peak; tokens/s per bl
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (published)
 PEAK_GBS = 8000.0                                # MI355X HBM3E (published)
 KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
-                  "rank_bottleneck_amd/csrc/lr_kernels.h"]
+                  "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h"]
 
 
 def log(*a):
@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--workload", default="qkv_identity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work on the host")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the steps, copy a 256 MiB buffer once (a plain copy kernel of known size, "
+                         "used to scale the HBM byte counters of a profiling run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the block's hot path runs on one GPU's shard and this build has no "
@@ -163,6 +166,14 @@ def main():
             rb.lr_block_fwd(dims, x, gamma, A, B, y, h, wsf)
             rb.lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, wsb)
         flops = wl.fwd_flops() + wl.bwd_flops()
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # warm-up; the last warm-up step is traced per kernel to find the dominant one
     for i in range(max(args.warmup - 1, 0)):

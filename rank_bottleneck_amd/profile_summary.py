@@ -1,0 +1,104 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+    python -m rank_bottleneck_amd.profile_summary stats  <kernel_stats.csv> <out.md> --title T --command C
+    python -m rank_bottleneck_amd.profile_summary traffic <fetch_counter_collection.csv> <write_counter_collection.csv>
+           --workload W --out profiles/traffic.json --command C
+
+`traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel into
+HBM bytes per launch.  Each counter is scaled by the factor that makes the same
+counter read exactly right for the plain 256 MiB copy that
+`bench.py --copy-calibration` runs first (read 256 MiB, write 256 MiB), and the
+entry records a hash of the kernel sources so that stale figures are ignored.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
+                  "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h"]
+COPY_BYTES = 256 << 20
+SHORT = [("k_wgrad_reduce", "wgrad_reduce"), ("k_wgrad", "wgrad"), ("k_down", "down"), ("k_up", "up"),
+         ("k_dz", "dz"), ("k_dx", "dx"), ("k_rms_stats", "rms_stats"), ("k_fold_gamma", "fold_gamma"),
+         ("k_sum_parts", "sum_parts"), ("k_finish", "finish")]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    k = kernel.replace("_ZN2lr", "")
+    for needle, short in SHORT:
+        if needle[2:] in k:
+            return short
+    return kernel
+
+
+def stats(csv_path: str, out: str, title: str, command: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    with open(out, "w") as f:
+        f.write(f"# {title}\n\nCommand (repository root, one MI355X):\n\n```\n{command}\n```\n\n")
+        f.write("| kernel | name | calls | average us | share % |\n|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {short_name(r['Name'])} | `{r['Name'][:70]}` | {r['Calls']} | "
+                    f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |\n")
+
+
+def _per_kernel(csv_path: str, counter: str):
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_csv: str, write_csv: str, workload: str, out: str, command: str) -> dict:
+    fetch, write = _per_kernel(fetch_csv, "FETCH_SIZE"), _per_kernel(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy:
+        raise SystemExit("no calibration copy kernel in the fetch run")
+    ck = max(copy, key=lambda k: max(fetch[k]))
+    f_scale = COPY_BYTES / (max(fetch[ck]) * 1024.0)
+    w_scale = COPY_BYTES / (max(write[ck]) * 1024.0)
+    rec = json.load(open(out)) if os.path.exists(out) else {}
+    h = source_hash()
+    summary = {}
+    for k in fetch:
+        name = short_name(k)
+        if name == k:
+            continue
+        fb = statistics.median(fetch[k]) * 1024.0 * f_scale
+        wb = statistics.median(write.get(k, [0.0])) * 1024.0 * w_scale
+        rec[f"{workload}/{name}"] = {"bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+                                     "fetch_scale": f_scale, "write_scale": w_scale, "source_hash": h,
+                                     "command": command}
+        summary[name] = (fb, wb)
+    json.dump(rec, open(out, "w"), indent=1, sort_keys=True)
+    return summary
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", choices=["stats", "traffic"])
+    ap.add_argument("inputs", nargs="+")
+    ap.add_argument("--title", default="kernel statistics")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--workload", default="")
+    ap.add_argument("--out", default="")
+    a = ap.parse_args()
+    if a.mode == "stats":
+        stats(a.inputs[0], a.inputs[1], a.title, a.command)
+    else:
+        s = traffic(a.inputs[0], a.inputs[1], a.workload, a.out, a.command)
+        for k, (fb, wb) in sorted(s.items()):
+            print(f"{k:14s} fetch {fb / 1e6:10.1f} MB  write {wb / 1e6:10.1f} MB")
