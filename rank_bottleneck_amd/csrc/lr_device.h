@@ -341,6 +341,7 @@ __device__ __forceinline__ void gemm_tile(const Opnd& oa, const Opnd& ob, const 
   }
   if constexpr (ROWSTAT) {
     static_assert(!A_MNC, "row statistics need a K-contiguous A");
+    __syncthreads();  // rowss may alias the staging buffers
     constexpr int PER = Loader<C, C::BM, A_MNC>::PER;
     constexpr int UNITS = Loader<C, C::BM, A_MNC>::UNITS;
 #pragma unroll
@@ -489,5 +490,24 @@ __device__ __forceinline__ float4 load4(const bf16* p) {
                      __uint_as_float(u.y & 0xffff0000u));
 }
 __device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// Raw 4-element loads, converted to fp32 later, so that an epilogue can issue all
+// of its input loads before the first use.
+template <typename E> struct Raw4;
+template <> struct Raw4<bf16> {
+  typedef uint2 T;
+  static __device__ __forceinline__ T load(const bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+  static __device__ __forceinline__ T zero() { return make_uint2(0u, 0u); }
+  static __device__ __forceinline__ float4 f4(const T& u) {
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+template <> struct Raw4<float> {
+  typedef float4 T;
+  static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ __forceinline__ float4 f4(const T& u) { return u; }
+};
 
 }  // namespace lr

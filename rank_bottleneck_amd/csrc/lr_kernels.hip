@@ -127,10 +127,14 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
 
 // LDS words a GEMM kernel needs: the mainloop ring or the epilogue staging,
 // whichever is larger, plus BM floats of per-row values.
+// The BM per-row floats live in the last BM*4 bytes: inside the mainloop ring when
+// the ring is the larger of the two (they are written only after the mainloop's
+// final barrier), and past the epilogue staging regions either way.
 template <class C>
 struct KernLds {
-  static constexpr int MAIN = C::LDS_UINT4 > RowStage<C>::UINT4 ? C::LDS_UINT4 : RowStage<C>::UINT4;
-  static constexpr int TOTAL = MAIN + C::BM / 4;
+  static constexpr int STAGE_PLUS_ROWS = RowStage<C>::UINT4 + C::BM / 4;
+  static constexpr int TOTAL = C::LDS_UINT4 > STAGE_PLUS_ROWS ? C::LDS_UINT4 : STAGE_PLUS_ROWS;
+  static constexpr int MAIN = TOTAL - C::BM / 4;   // offset of the per-row floats
 };
 
 // ------------------------------------------------------------------ down projection
@@ -243,6 +247,153 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   }
 }
 
+// dz epilogue in the accumulator layout: for two 32-row blocks at a time, every
+// input load (h) is issued before the first use, then dh' = rstd*dz*sigma'(h),
+// z = sigma(h) and the row partials of S' are formed and stored.  The restrict
+// qualifiers let the loads run ahead of the stores.
+template <class C, int ACT, typename E>
+__device__ __forceinline__ void dz_epilogue(const f32x16 (&acc)[C::MB][C::NB], const DzArgs& a,
+                                            const E* __restrict__ h, E* __restrict__ dh, E* __restrict__ z,
+                                            float* __restrict__ spart, const float* rs_tile, int m0, int n0, int br,
+                                            int part) {
+  using R = Raw4<E>;
+  constexpr int MBH = C::MB >= 2 ? 2 : 1;
+  constexpr int NL = ACT == ACT_SWIGLU ? 2 : 1;
+  const int gr = a.g * a.r;
+  FragPos<C> fp(m0, n0);
+#pragma unroll
+  for (int mb0 = 0; mb0 < C::MB; mb0 += MBH) {
+    typename R::T in[MBH][C::NB][4][NL];
+#pragma unroll
+    for (int j = 0; j < MBH; ++j) {
+      const int row = fp.row(mb0 + j);
+      const int64_t hrow = (int64_t)row * gr;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = fp.col(nb, q);
+          const bool ok = row < a.T && c < a.r;
+#pragma unroll
+          for (int k = 0; k < NL; ++k) {
+            const int64_t off = ACT == ACT_SWIGLU ? hrow + k * a.r + c : hrow + br * a.r + c;
+            in[j][nb][q][k] = ok ? R::load(h + off) : R::zero();
+          }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < MBH; ++j) {
+      const int mb = mb0 + j;
+      const int row = fp.row(mb);
+      const bool rok = row < a.T;
+      const float rs = rok ? rs_tile[row - m0] : 0.f;
+      const int64_t hrow = (int64_t)row * gr;
+      float srow = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = fp.col(nb, q);
+          if (!rok || c >= a.r) continue;
+          const f32x16& v = acc[mb][nb];
+          const float dzv[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+          if constexpr (ACT == ACT_SWIGLU) {
+            const float4 g4 = R::f4(in[j][nb][q][0]), u4 = R::f4(in[j][nb][q][NL - 1]);
+            const float hg[4] = {g4.x, g4.y, g4.z, g4.w}, hu[4] = {u4.x, u4.y, u4.z, u4.w};
+            float dg[4], du[4], zz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float s = sigmoidf_(hg[e]);
+              const float sg = hg[e] * s;
+              dg[e] = rs * dzv[e] * hu[e] * s * (1.0f + hg[e] * (1.0f - s));
+              du[e] = rs * dzv[e] * sg;
+              zz[e] = sg * hu[e];
+              srow += dg[e] * hg[e] + du[e] * hu[e];
+            }
+            store4(dh + hrow + c, dg[0], dg[1], dg[2], dg[3]);
+            store4(dh + hrow + a.r + c, du[0], du[1], du[2], du[3]);
+            store4(z + (int64_t)row * a.r + c, zz[0], zz[1], zz[2], zz[3]);
+          } else {
+            const int64_t idx = hrow + br * a.r + c;
+            const float4 h4 = R::f4(in[j][nb][q][0]);
+            const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+            float d1[4];
+            if constexpr (ACT == ACT_SILU) {
+              float zz[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float s = sigmoidf_(hv[e]);
+                d1[e] = rs * dzv[e] * s * (1.0f + hv[e] * (1.0f - s));
+                zz[e] = hv[e] * s;
+              }
+              store4(z + idx, zz[0], zz[1], zz[2], zz[3]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) d1[e] = rs * dzv[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) srow += d1[e] * hv[e];
+            store4(dh + idx, d1[0], d1[1], d1[2], d1[3]);
+          }
+        }
+      srow += __shfl_xor(srow, 32);  // lanes l and l+32 hold the same row
+      if (fp.lane < 32 && rok) spart[(int64_t)row * a.nspart + part] = srow;
+    }
+  }
+}
+
+// dx epilogue in the accumulator layout: x and gamma for two 32-row blocks are
+// loaded before the first use, then dx = gamma*(dh'.A^T) - x*rstd*S'/D.
+template <class C, typename E>
+__device__ __forceinline__ void dx_epilogue(const f32x16 (&acc)[C::MB][C::NB], int T, int d,
+                                            const E* __restrict__ x, const E* __restrict__ gamma,
+                                            E* __restrict__ dx, const float* srow, int m0, int n0) {
+  using R = Raw4<E>;
+  constexpr int MBH = C::MB >= 2 ? 2 : 1;
+  FragPos<C> fp(m0, n0);
+  typename R::T g[C::NB][4];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = fp.col(nb, q);
+      g[nb][q] = col < d ? R::load(gamma + col) : R::zero();
+    }
+#pragma unroll
+  for (int mb0 = 0; mb0 < C::MB; mb0 += MBH) {
+    typename R::T xin[MBH][C::NB][4];
+#pragma unroll
+    for (int j = 0; j < MBH; ++j) {
+      const int row = fp.row(mb0 + j);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = fp.col(nb, q);
+          xin[j][nb][q] = row < T && col < d ? R::load(x + (int64_t)row * d + col) : R::zero();
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < MBH; ++j) {
+      const int mb = mb0 + j;
+      const int row = fp.row(mb);
+      if (row >= T) continue;
+      const float sr = srow[row - m0];
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = fp.col(nb, q);
+          if (col >= d) continue;
+          const float4 g4 = R::f4(g[nb][q]), x4 = R::f4(xin[j][nb][q]);
+          const f32x16& v = acc[mb][nb];
+          store4(dx + (int64_t)row * d + col, g4.x * v[4 * q] - x4.x * sr, g4.y * v[4 * q + 1] - x4.y * sr,
+                 g4.z * v[4 * q + 2] - x4.z * sr, g4.w * v[4 * q + 3] - x4.w * sr);
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ backward: dz -> dh'
 template <class C, int ACT>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dz(DzArgs a) {
@@ -263,71 +414,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   for (int i = threadIdx.x; i < C::BM; i += C::THREADS) rs_tile[i] = m0 + i < a.T ? a.rstd[m0 + i] : 0.f;
   __syncthreads();
 
-  const int gr = a.g * a.r;
-  const E* h = static_cast<const E*>(a.h);
-  E* dh = static_cast<E*>(a.dh);
-  E* z = static_cast<E*>(a.z);
-  FragPos<C> fp(m0, n0);
   const int wn = (threadIdx.x >> 6) % C::WN;
-  const int part = (br * tiles_n + tn) * C::WN + wn;
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) {
-    const int row = fp.row(mb);
-    const bool rok = row < a.T;
-    const float rs = rok ? a.rstd[row] : 0.f;
-    const int64_t hrow = (int64_t)row * gr;
-    float srow = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = fp.col(nb, q);
-        if (!rok || c >= a.r) continue;
-        const f32x16& v = acc[mb][nb];
-        const float dzv[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-        if constexpr (ACT == ACT_SWIGLU) {
-          const float4 g4 = load4(h + hrow + c), u4 = load4(h + hrow + a.r + c);
-          const float hg[4] = {g4.x, g4.y, g4.z, g4.w}, hu[4] = {u4.x, u4.y, u4.z, u4.w};
-          float dg[4], du[4], zz[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float s = sigmoidf_(hg[e]);
-            const float sg = hg[e] * s;
-            dg[e] = rs * dzv[e] * hu[e] * s * (1.0f + hg[e] * (1.0f - s));
-            du[e] = rs * dzv[e] * sg;
-            zz[e] = sg * hu[e];
-            srow += dg[e] * hg[e] + du[e] * hu[e];
-          }
-          store4(dh + hrow + c, dg[0], dg[1], dg[2], dg[3]);
-          store4(dh + hrow + a.r + c, du[0], du[1], du[2], du[3]);
-          store4(z + (int64_t)row * a.r + c, zz[0], zz[1], zz[2], zz[3]);
-        } else {
-          const int64_t idx = hrow + br * a.r + c;
-          const float4 h4 = load4(h + idx);
-          const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
-          float d1[4];
-          if constexpr (ACT == ACT_SILU) {
-            float zz[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float s = sigmoidf_(hv[e]);
-              d1[e] = rs * dzv[e] * s * (1.0f + hv[e] * (1.0f - s));
-              zz[e] = hv[e] * s;
-            }
-            store4(z + idx, zz[0], zz[1], zz[2], zz[3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d1[e] = rs * dzv[e];
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) srow += d1[e] * hv[e];
-          store4(dh + idx, d1[0], d1[1], d1[2], d1[3]);
-        }
-      }
-    // lanes l and l+32 hold the same row
-    srow += __shfl_xor(srow, 32);
-    if (fp.lane < 32 && rok) a.spart[(int64_t)row * a.nspart + part] = srow;
-  }
+  dz_epilogue<C, ACT>(acc, a, static_cast<const E*>(a.h), static_cast<E*>(a.dh), static_cast<E*>(a.z), a.spart,
+                      rs_tile, m0, n0, br, (br * tiles_n + tn) * C::WN + wn);
 }
 
 // ------------------------------------------------------------------ backward: weight gradients
@@ -477,28 +566,8 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
     srow[i] = s;
   }
   __syncthreads();
-  const E* x = static_cast<const E*>(a.x);
-  const E* gamma = static_cast<const E*>(a.gamma);
-  E* dx = static_cast<E*>(a.dx);
-  FragPos<C> fp(m0, n0);
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) {
-    const int row = fp.row(mb);
-    if (row >= a.T) continue;
-    const float sr = srow[row - m0];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = fp.col(nb, q);
-        if (col >= a.d) continue;
-        const int64_t idx = (int64_t)row * a.d + col;
-        const float4 g4 = load4(gamma + col), x4 = load4(x + idx);
-        const f32x16& v = acc[mb][nb];
-        store4(dx + idx, g4.x * v[4 * q] - x4.x * sr, g4.y * v[4 * q + 1] - x4.y * sr,
-               g4.z * v[4 * q + 2] - x4.z * sr, g4.w * v[4 * q + 3] - x4.w * sr);
-      }
-  }
+  dx_epilogue<C>(acc, a.T, a.d, static_cast<const E*>(a.x), static_cast<const E*>(a.gamma), static_cast<E*>(a.dx),
+                 srow, m0, n0);
 }
 
 // ------------------------------------------------------------------ launchers

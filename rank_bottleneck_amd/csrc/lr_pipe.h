@@ -139,6 +139,9 @@ struct DmaTile {
 #pragma unroll
     for (int q = 0; q < Q; ++q) dma16(r, off[q], lds_tile + (q * C::NWAVES + wave) * 1024);
   }
+  __device__ __forceinline__ void issue_one(int q, const Rsrc4& r, uint32_t lds_tile, int wave) const {
+    dma16(r, off[q], lds_tile + (q * C::NWAVES + wave) * 1024);
+  }
 };
 
 // one MFMA operand fragment (32 rows x 16 k) of the tile whose LDS image starts at `t`
@@ -227,11 +230,30 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
   };
 
   if (nk > 0) {
-    // prefetch distance: STAGES stages; the buffer of stage kt is refilled with stage
-    // kt+STAGES as soon as every wave holds its last fragments of stage kt
+    // Prefetch distance: STAGES stages.  Once every wave holds its last fragments of
+    // stage kt, stage kt's buffer is refilled with stage kt+STAGES: the first half
+    // of those loads goes out during the last MFMA sub-step of stage kt, the second
+    // half during the first sub-step of stage kt+1, one load per few MFMAs, so that
+    // this in-order wave never stalls on a burst of load issues while the MFMA pipe
+    // runs dry.  Fragment reads of the next sub-step are interleaved the same way.
+    constexpr int QA = DmaTile<C, C::BM, A_MNC>::Q, QB = DmaTile<C, C::BN, B_MNC>::Q;
+    constexpr int HALF = (QA + QB) / 2;
+    constexpr int NMF = C::MB * C::NB;
+    constexpr int NF = C::MB + C::NB;
+    static_assert((QA + QB) % 2 == 0 && HALF <= NMF, "load spreading");
+    auto issue_q = [&](int q, const Rsrc4& ra, const Rsrc4& rb, uint32_t buf) {
+      if (q < QA)
+        da.issue_one(q, ra, buf, wave);
+      else
+        db.issue_one(q - QA, rb, buf + C::A_BYTES, wave);
+    };
 #pragma unroll
-    for (int st = 0; st < C::STAGES; ++st) issue_stage(st);
-    wait_vmcnt<(C::STAGES - 1) * C::LPS>();
+    for (int st = 0; st < C::STAGES - 1; ++st) issue_stage(st);
+    Rsrc4 pra = da.rsrc(C::STAGES - 1, C::STAGES - 1 < nk), prb = db.rsrc(C::STAGES - 1, C::STAGES - 1 < nk);
+    uint32_t pbuf = lds0 + ((C::STAGES - 1) % C::STAGES) * C::STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < HALF; ++q) issue_q(q, pra, prb, pbuf);
+    wait_vmcnt<(C::STAGES - 2) * C::LPS + HALF>();
     block_barrier();
     uint4 a[2][C::MB], b[2][C::NB];
     read_frags(0, 0, a[0], b[0]);
@@ -239,16 +261,29 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
         const int cur = s & 1, nxt = cur ^ 1;
-        if (s + 1 < C::KS) {
-          read_frags(kt, s + 1, a[nxt], b[nxt]);
-        } else {
-          // all of stage kt is in registers: wait for stage kt+1, refill stage kt's buffer
+        const bool last = s + 1 == C::KS;
+        Rsrc4 ra = pra, rb = prb;
+        uint32_t buf = pbuf;
+        int qbase = HALF;               // first sub-step: second half of the pending refill
+        int fst = kt, fs = s + 1;       // source of the next fragments
+        if (last) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           wait_vmcnt<(C::STAGES - 2) * C::LPS>();
           block_barrier();
-          issue_stage(kt + C::STAGES);
-          read_frags(kt + 1, 0, a[nxt], b[nxt]);  // past the end: unused reads of a zero-filled buffer
+          const int st = kt + C::STAGES;
+          ra = da.rsrc(st, st < nk);
+          rb = db.rsrc(st, st < nk);
+          buf = lds0 + (st % C::STAGES) * C::STAGE_BYTES;
+          pra = ra;
+          prb = rb;
+          pbuf = buf;
+          qbase = 0;
+          fst = kt + 1;                 // past the end: unused reads of a zero-filled buffer
+          fs = 0;
         }
+        const bool loads_here = last || s == 0;
+        const char LR_LDS* fa = ldsp + (fst % C::STAGES) * C::STAGE_BYTES;
+        const char LR_LDS* fb = fa + C::A_BYTES;
         if constexpr (ROWSTAT) {
           if (wn == 0) {
 #pragma unroll
@@ -256,16 +291,25 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
           }
         }
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) mfma_chunk(acc[mb][nb], b[cur][nb], a[cur][mb], (bf16*)nullptr);
-        interleave();
+        for (int i = 0; i < NMF; ++i) {
+          mfma_chunk(acc[i / C::NB][i % C::NB], b[cur][i % C::NB], a[cur][i / C::NB], (bf16*)nullptr);
+          if (i < NF) {
+            if (i < C::MB)
+              a[nxt][i] = frag<C, C::BM, A_MNC>(fa, wm * C::WTM + i * 32, fs, lane);
+            else
+              b[nxt][i - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (i - C::MB) * 32, fs, lane);
+          }
+          constexpr int EVERY = NMF / HALF;
+          if (loads_here && (i % EVERY) == EVERY - 1) issue_q(qbase + i / EVERY, ra, rb, buf);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     wait_vmcnt<0>();
   }
   if constexpr (ROWSTAT) {
     static_assert(!A_MNC, "row statistics need a K-contiguous A");
+    __syncthreads();  // rowss may alias the ring: every wave is past its last fragment read
     if (wn == 0) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
