@@ -59,6 +59,8 @@ def kernel_work(wl, name: str):
     if name == "wgrad":
         return (2.0 * T * r * d * nu + 2.0 * T * d * gr,
                 e * (T * (zcols or gr) + nu * T * d + T * d + T * gr + d * gr) + 4 * (d * gr + nu * r * d))
+    if name == "wgrad_reduce":   # the split-K sum: only its fp32 results count
+        return 0.0, 4 * (d * gr + nu * r * d)
     if name == "dx":
         return 2.0 * T * gr * d, e * (T * gr + d * gr + 2 * T * d) + 4 * T
     if name == "fold_gamma":

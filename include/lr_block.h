@@ -136,8 +136,9 @@ size_t lr_block_workspace_size(const lr_dims* dims, int backward);
  * launches from the CALLING THREAD whose name matches `kernel` (NULL: all) is
  * bracketed by two hipEvents recorded on the launch stream, up to
  * `max_launches` launches.  Kernel names: "fold_gamma", "down", "up", "finish",
- * "rms_stats", "dz", "wgrad", "sum_parts", "dx".  This per-thread trace is the
- * only state the library keeps between calls; it owns its events.
+ * "rms_stats", "dz", "wgrad", "wgrad_reduce", "sum_parts", "dx".  This
+ * per-thread trace is the only state the library keeps between calls; it owns
+ * its events.
  *   lr_trace_begin: LR_EINVAL if max_launches < 1 or a trace is already active,
  *                   LR_EHIP if events cannot be created.
  *   lr_trace_count: launches recorded so far (0 when no trace is active).

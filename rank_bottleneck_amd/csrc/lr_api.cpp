@@ -160,6 +160,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
     wa.ksplit = ((ksteps + ns - 1) / ns) * BK;
   }
   LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
+  if (ns > 1) LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
   LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, ns), ngp, s));
 
   lr::DxArgs xa{};

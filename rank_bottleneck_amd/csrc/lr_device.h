@@ -467,12 +467,48 @@ __device__ __forceinline__ void sweep_block_pre(const char LR_LDS* region, FL&& 
   }
 }
 
-// sum over the LPR lanes that share a row in sweep_block
+// Lane geometry of a row sweep over COLS staged columns, for kernels that
+// interleave their own loads with it: iteration it covers block row rl(it) and
+// the 4 columns from cl.
+template <class C, int COLS>
+struct Sweep {
+  static constexpr int LPR = COLS / 4, RPI = 64 / LPR, IT = 32 / RPI;
+  static_assert(LPR <= 64 && 64 % LPR == 0, "row sweep width");
+  int r0, cl;
+  __device__ __forceinline__ Sweep() {
+    const int lane = threadIdx.x & 63;
+    r0 = lane / LPR;
+    cl = (lane % LPR) * 4;
+  }
+  __device__ __forceinline__ int rl(int it) const { return it * RPI + r0; }
+};
+
+// DPP lane move of x (ISA data-parallel primitives); lanes of rows outside
+// ROWMASK read 0.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xF,
+                                                               false));
+}
+
+// Sum over the LPR consecutive lanes that share a row in a sweep (LPR a power of
+// two up to 32), with DPP moves instead of LDS shuffles: pair and quad swaps,
+// the mirrors within 8 and 16 lanes, then for 32 lanes a broadcast of lane 15 of
+// each 16-lane row into the next.  The sum is complete in the group's last lane
+// (row_sum_lane), and in every lane of the group when LPR <= 16.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  static_assert(LPR >= 1 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "row width");
+  if constexpr (LPR >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
+  if constexpr (LPR >= 16) v += dpp_mov<0x140>(v);  // row_mirror
+  if constexpr (LPR == 32) v += dpp_mov<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
   return v;
+}
+template <int LPR>
+__device__ __forceinline__ bool row_sum_lane() {
+  return (threadIdx.x & (LPR - 1)) == LPR - 1;
 }
 
 // 4 consecutive values -> memory (8 bytes of bf16 / 16 bytes of fp32)

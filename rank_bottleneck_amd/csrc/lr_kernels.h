@@ -86,6 +86,8 @@ template <typename E> hipError_t launch_finish(const float* partial, const float
                                                int r, int g, int act, float invD, float eps, hipStream_t s);
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
+// sums the split partials of launch_wgrad (nothing to do when nsplit == 1)
+template <typename E> hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s);
 template <typename E> hipError_t launch_dx(const DxArgs& a, hipStream_t s);
 hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, int stride, hipStream_t s);
 template <typename E> int dz_nparts(int r);

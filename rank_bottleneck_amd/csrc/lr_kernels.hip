@@ -127,14 +127,16 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
 
 // LDS words a GEMM kernel needs: the mainloop ring or the epilogue staging,
 // whichever is larger, plus BM floats of per-row values.
-// The BM per-row floats live in the last BM*4 bytes: inside the mainloop ring when
-// the ring is the larger of the two (they are written only after the mainloop's
-// final barrier), and past the epilogue staging regions either way.
+// LDS of a GEMM kernel: the mainloop's tiles, then (after the mainloop) the
+// waves' epilogue staging regions followed by BM per-row floats.  The per-row
+// floats are written only after the mainloop's final barrier, when every load of
+// a real stage has landed (loads of stages past the end go to the sink, which
+// lies beyond them).
 template <class C>
 struct KernLds {
-  static constexpr int STAGE_PLUS_ROWS = RowStage<C>::UINT4 + C::BM / 4;
+  static constexpr int MAIN = RowStage<C>::UINT4;   // offset of the per-row floats
+  static constexpr int STAGE_PLUS_ROWS = MAIN + C::BM / 4;
   static constexpr int TOTAL = C::LDS_UINT4 > STAGE_PLUS_ROWS ? C::LDS_UINT4 : STAGE_PLUS_ROWS;
-  static constexpr int MAIN = TOTAL - C::BM / 4;   // offset of the per-row floats
 };
 
 // ------------------------------------------------------------------ down projection
@@ -166,10 +168,16 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   char LR_LDS* reg = stage_region<C>(lds);
   E* h = static_cast<E*>(a.h);
   E* z = static_cast<E*>(a.z);
-  if (a.mode == DOWN_PARTIAL) {
-    if (tn == 0 && threadIdx.x < C::BM && m0 + (int)threadIdx.x < a.T)
-      a.sumsq[m0 + threadIdx.x] = rowss[threadIdx.x];
+  // per-row sum of squares -> rstd, once per row (in place)
+  for (int i = threadIdx.x; i < C::BM; i += C::THREADS) {
+    const float ssv = rowss[i];
+    if (a.mode == DOWN_PARTIAL) {
+      if (tn == 0 && m0 + i < a.T) a.sumsq[m0 + i] = ssv;
+    } else {
+      rowss[i] = __builtin_amdgcn_rsqf(ssv * a.invD + a.eps);
+    }
   }
+  __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
     stage_block<C>(acc, mb, reg);
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
         const int row = rbase + rl;
         const int logical = n0 + wn * (C::WTN / 2) + cl;
         if (row >= a.T || logical >= a.r) return;
-        const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
+        const float rs = rowss[row - m0];
         const float4 g4 = lds_f4(rp + cl * 4), u4 = lds_f4(rp + (cl + C::WTN / 2) * 4);
         const float hg[4] = {g4.x * rs, g4.y * rs, g4.z * rs, g4.w * rs};
         const float hu[4] = {u4.x * rs, u4.y * rs, u4.z * rs, u4.w * rs};
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
           store4(a.partial + (int64_t)row * gr + col, v.x, v.y, v.z, v.w);
           return;
         }
-        const float rs = 1.0f / sqrtf(rowss[row - m0] * a.invD + a.eps);
+        const float rs = rowss[row - m0];
         const float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
         if (h) store4(h + (int64_t)row * gr + col, hv[0], hv[1], hv[2], hv[3]);
         if (a.act == ACT_SILU) {
@@ -247,157 +255,40 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   }
 }
 
-// dz epilogue in the accumulator layout: for two 32-row blocks at a time, every
-// input load (h) is issued before the first use, then dh' = rstd*dz*sigma'(h),
-// z = sigma(h) and the row partials of S' are formed and stored.  The restrict
-// qualifiers let the loads run ahead of the stores.
-template <class C, int ACT, typename E>
-__device__ __forceinline__ void dz_epilogue(const f32x16 (&acc)[C::MB][C::NB], const DzArgs& a,
-                                            const E* __restrict__ h, E* __restrict__ dh, E* __restrict__ z,
-                                            float* __restrict__ spart, const float* rs_tile, int m0, int n0, int br,
-                                            int part) {
-  using R = Raw4<E>;
-  constexpr int MBH = C::MB >= 2 ? 2 : 1;
-  constexpr int NL = ACT == ACT_SWIGLU ? 2 : 1;
-  const int gr = a.g * a.r;
-  FragPos<C> fp(m0, n0);
+// Per-row values a kernel loads at its last k step and publishes in LDS after
+// the mainloop: thread tid holds rows tid, tid + THREADS, ...
+template <class C>
+struct RowVals {
+  static constexpr int N = (C::BM + C::THREADS - 1) / C::THREADS;
+  float v[N];
+  template <class F>
+  __device__ __forceinline__ void load(F&& f) {
 #pragma unroll
-  for (int mb0 = 0; mb0 < C::MB; mb0 += MBH) {
-    typename R::T in[MBH][C::NB][4][NL];
-#pragma unroll
-    for (int j = 0; j < MBH; ++j) {
-      const int row = fp.row(mb0 + j);
-      const int64_t hrow = (int64_t)row * gr;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = fp.col(nb, q);
-          const bool ok = row < a.T && c < a.r;
-#pragma unroll
-          for (int k = 0; k < NL; ++k) {
-            const int64_t off = ACT == ACT_SWIGLU ? hrow + k * a.r + c : hrow + br * a.r + c;
-            in[j][nb][q][k] = ok ? R::load(h + off) : R::zero();
-          }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < MBH; ++j) {
-      const int mb = mb0 + j;
-      const int row = fp.row(mb);
-      const bool rok = row < a.T;
-      const float rs = rok ? rs_tile[row - m0] : 0.f;
-      const int64_t hrow = (int64_t)row * gr;
-      float srow = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = fp.col(nb, q);
-          if (!rok || c >= a.r) continue;
-          const f32x16& v = acc[mb][nb];
-          const float dzv[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-          if constexpr (ACT == ACT_SWIGLU) {
-            const float4 g4 = R::f4(in[j][nb][q][0]), u4 = R::f4(in[j][nb][q][NL - 1]);
-            const float hg[4] = {g4.x, g4.y, g4.z, g4.w}, hu[4] = {u4.x, u4.y, u4.z, u4.w};
-            float dg[4], du[4], zz[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float s = sigmoidf_(hg[e]);
-              const float sg = hg[e] * s;
-              dg[e] = rs * dzv[e] * hu[e] * s * (1.0f + hg[e] * (1.0f - s));
-              du[e] = rs * dzv[e] * sg;
-              zz[e] = sg * hu[e];
-              srow += dg[e] * hg[e] + du[e] * hu[e];
-            }
-            store4(dh + hrow + c, dg[0], dg[1], dg[2], dg[3]);
-            store4(dh + hrow + a.r + c, du[0], du[1], du[2], du[3]);
-            store4(z + (int64_t)row * a.r + c, zz[0], zz[1], zz[2], zz[3]);
-          } else {
-            const int64_t idx = hrow + br * a.r + c;
-            const float4 h4 = R::f4(in[j][nb][q][0]);
-            const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
-            float d1[4];
-            if constexpr (ACT == ACT_SILU) {
-              float zz[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float s = sigmoidf_(hv[e]);
-                d1[e] = rs * dzv[e] * s * (1.0f + hv[e] * (1.0f - s));
-                zz[e] = hv[e] * s;
-              }
-              store4(z + idx, zz[0], zz[1], zz[2], zz[3]);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) d1[e] = rs * dzv[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) srow += d1[e] * hv[e];
-            store4(dh + idx, d1[0], d1[1], d1[2], d1[3]);
-          }
-        }
-      srow += __shfl_xor(srow, 32);  // lanes l and l+32 hold the same row
-      if (fp.lane < 32 && rok) spart[(int64_t)row * a.nspart + part] = srow;
+    for (int j = 0; j < N; ++j) {
+      const int i = threadIdx.x + j * C::THREADS;
+      v[j] = i < C::BM ? f(i) : 0.f;
     }
   }
-}
-
-// dx epilogue in the accumulator layout: x and gamma for two 32-row blocks are
-// loaded before the first use, then dx = gamma*(dh'.A^T) - x*rstd*S'/D.
-template <class C, typename E>
-__device__ __forceinline__ void dx_epilogue(const f32x16 (&acc)[C::MB][C::NB], int T, int d,
-                                            const E* __restrict__ x, const E* __restrict__ gamma,
-                                            E* __restrict__ dx, const float* srow, int m0, int n0) {
-  using R = Raw4<E>;
-  constexpr int MBH = C::MB >= 2 ? 2 : 1;
-  FragPos<C> fp(m0, n0);
-  typename R::T g[C::NB][4];
+  __device__ __forceinline__ void publish(float* dst) const {
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = fp.col(nb, q);
-      g[nb][q] = col < d ? R::load(gamma + col) : R::zero();
-    }
-#pragma unroll
-  for (int mb0 = 0; mb0 < C::MB; mb0 += MBH) {
-    typename R::T xin[MBH][C::NB][4];
-#pragma unroll
-    for (int j = 0; j < MBH; ++j) {
-      const int row = fp.row(mb0 + j);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = fp.col(nb, q);
-          xin[j][nb][q] = row < T && col < d ? R::load(x + (int64_t)row * d + col) : R::zero();
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < MBH; ++j) {
-      const int mb = mb0 + j;
-      const int row = fp.row(mb);
-      if (row >= T) continue;
-      const float sr = srow[row - m0];
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = fp.col(nb, q);
-          if (col >= d) continue;
-          const float4 g4 = R::f4(g[nb][q]), x4 = R::f4(xin[j][nb][q]);
-          const f32x16& v = acc[mb][nb];
-          store4(dx + (int64_t)row * d + col, g4.x * v[4 * q] - x4.x * sr, g4.y * v[4 * q + 1] - x4.y * sr,
-                 g4.z * v[4 * q + 2] - x4.z * sr, g4.w * v[4 * q + 3] - x4.w * sr);
-        }
+    for (int j = 0; j < N; ++j) {
+      const int i = threadIdx.x + j * C::THREADS;
+      if (i < C::BM) dst[i] = v[j];
     }
   }
-}
+};
 
 // ------------------------------------------------------------------ backward: dz -> dh'
+// acc = dy_i . B_i^T over K = d.  Row-sweep epilogue: dh' = rstd*dz*sigma'(h),
+// z = sigma(h) (SiLU/SwiGLU) and one partial of S' = sum_c dh'*h per (row, wave).
+// The h rows of 32-row block mb+1 are loaded while block mb is computed; those of
+// block 0 and the rows' rstd are loaded at the start of the last k step.
 template <class C, int ACT>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dz(DzArgs a) {
   using E = typename C::E;
+  using R = Raw4<E>;
+  using SW = Sweep<C, C::WTN>;
+  constexpr int NL = ACT == ACT_SWIGLU ? 2 : 1;
   __shared__ uint4 lds[KernLds<C>::TOTAL];
   float* rs_tile = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] rstd of the tile's rows
   const int tiles_n = (a.r + C::BN - 1) / C::BN;
@@ -407,16 +298,108 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   int tm, tn;
   grouped_tile<kGroupM>(logical % (tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int gr = a.g * a.r;
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const SW sw;
+  const int c = n0 + wn * C::WTN + sw.cl;   // rank index within the branch
+  const bool cok = c < a.r;
+  const E* __restrict__ h = static_cast<const E*>(a.h);
+  E* __restrict__ dh = static_cast<E*>(a.dh);
+  E* __restrict__ z = static_cast<E*>(a.z);
+  // SwiGLU reads gate (column c) and up (column r + c); otherwise branch br's column
+  const int hcol = ACT == ACT_SWIGLU ? c : br * a.r + c;
+
+  // two buffers of h values (SwiGLU: gate in `g`, up in `u`; otherwise `u` is unused)
+  typedef typename R::T Buf[SW::IT];
+  Buf g0, u0, g1, u1;
+  auto load_block = [&](int mb, Buf& bg, Buf& bu) {
+    const int rb = m0 + wm * C::WTM + mb * 32;
+#pragma unroll
+    for (int it = 0; it < SW::IT; ++it) {
+      const int row = rb + sw.rl(it);
+      const bool ok = row < a.T && cok;
+      const E* p = h + (int64_t)row * gr + hcol;
+      bg[it] = ok ? R::load(p) : R::zero();
+      if constexpr (NL == 2) bu[it] = ok ? R::load(p + a.r) : R::zero();
+    }
+  };
+  RowVals<C> rsv;
+  auto pre = [&]() {   // the row values first: they are needed first
+    rsv.load([&](int i) { return m0 + i < a.T ? a.rstd[m0 + i] : 0.f; });
+    load_block(0, g0, u0);
+  };
+
   Opnd oa{a.dy[br], a.d, a.T, a.d};
   Opnd ob{a.B[br], a.d, a.r, a.d};  // B_i^T: (n = c, k = j) at B_i[c*d + j]
   f32x16 acc[C::MB][C::NB];
-  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc);
-  for (int i = threadIdx.x; i < C::BM; i += C::THREADS) rs_tile[i] = m0 + i < a.T ? a.rstd[m0 + i] : 0.f;
+  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc, pre);
+  rsv.publish(rs_tile);
   __syncthreads();
 
-  const int wn = (threadIdx.x >> 6) % C::WN;
-  dz_epilogue<C, ACT>(acc, a, static_cast<const E*>(a.h), static_cast<E*>(a.dh), static_cast<E*>(a.z), a.spart,
-                      rs_tile, m0, n0, br, (br * tiles_n + tn) * C::WN + wn);
+  const int part = (br * tiles_n + tn) * C::WN + wn;
+  char LR_LDS* reg = stage_region<C>(lds);
+  // block mb computes from `cur` while block mb+1 loads into `nxt`
+  auto block = [&](int mb, const Buf& cg, const Buf& cu, Buf& ng, Buf& nu) {
+    if (mb + 1 < C::MB) load_block(mb + 1, ng, nu);
+    stage_block<C>(acc, mb, reg);
+    const int rb = m0 + wm * C::WTM + mb * 32;
+#pragma unroll
+    for (int it = 0; it < SW::IT; ++it) {
+      const int rl = sw.rl(it), row = rb + rl;
+      const bool ok = row < a.T && cok;
+      float srow = 0.f;
+      if (ok) {
+        const float4 v = lds_f4(reg + rl * RowStage<C>::PITCH + sw.cl * 4);
+        const float dzv[4] = {v.x, v.y, v.z, v.w};
+        const float rs = rs_tile[row - m0];
+        const int64_t hidx = (int64_t)row * gr + hcol;
+        if constexpr (ACT == ACT_SWIGLU) {
+          const float4 g4 = R::f4(cg[it]), u4 = R::f4(cu[it]);
+          const float hg[4] = {g4.x, g4.y, g4.z, g4.w}, hu[4] = {u4.x, u4.y, u4.z, u4.w};
+          float dg[4], du[4], zz[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = sigmoidf_(hg[e]);
+            const float sl = hg[e] * sg;
+            dg[e] = rs * dzv[e] * hu[e] * sg * (1.0f + hg[e] * (1.0f - sg));
+            du[e] = rs * dzv[e] * sl;
+            zz[e] = sl * hu[e];
+            srow += dg[e] * hg[e] + du[e] * hu[e];
+          }
+          store4(dh + hidx, dg[0], dg[1], dg[2], dg[3]);
+          store4(dh + hidx + a.r, du[0], du[1], du[2], du[3]);
+          store4(z + (int64_t)row * a.r + c, zz[0], zz[1], zz[2], zz[3]);
+        } else {
+          const float4 h4 = R::f4(cg[it]);
+          const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+          float d1[4];
+          if constexpr (ACT == ACT_SILU) {
+            float zz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = sigmoidf_(hv[e]);
+              d1[e] = rs * dzv[e] * sg * (1.0f + hv[e] * (1.0f - sg));
+              zz[e] = hv[e] * sg;
+            }
+            store4(z + hidx, zz[0], zz[1], zz[2], zz[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d1[e] = rs * dzv[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) srow += d1[e] * hv[e];
+          store4(dh + hidx, d1[0], d1[1], d1[2], d1[3]);
+        }
+      }
+      srow = row_sum<SW::LPR>(srow);
+      if (row < a.T && row_sum_lane<SW::LPR>()) a.spart[(int64_t)row * a.nspart + part] = srow;
+    }
+  };
+#pragma unroll
+  for (int mb = 0; mb < C::MB; mb += 2) {
+    block(mb, g0, u0, g1, u1);
+    if (mb + 1 < C::MB) block(mb + 1, g1, u1, g0, u0);
+  }
 }
 
 // ------------------------------------------------------------------ backward: weight gradients
@@ -493,7 +476,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
           }
           if (finalA) {
             s = row_sum<LPR>(s);
-            if (row < M && (threadIdx.x & (LPR - 1)) == 0) a.gpart[(int64_t)row * a.ngpart + tn * C::WN + wn] = s;
+            if (row < M && row_sum_lane<LPR>()) a.gpart[(int64_t)row * a.ngpart + tn * C::WN + wn] = s;
           }
         });
   }
@@ -540,9 +523,14 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
 }
 
 // ------------------------------------------------------------------ backward: dx
+// acc = dh' . A^T over K = g*r.  Row-sweep epilogue: dx = gamma*acc - x*rstd*S'/D,
+// with S' summed from the dz partials.  x rows of block mb+1 are loaded while
+// block mb is computed; block 0, gamma and the row statistic at the last k step.
 template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dx(DxArgs a) {
   using E = typename C::E;
+  using R = Raw4<E>;
+  using SW = Sweep<C, C::WTN>;
   __shared__ uint4 lds[KernLds<C>::TOTAL];
   float* srow = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] : rstd*S'/D
   const int gr = a.g * a.r;
@@ -551,23 +539,67 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   int tm, tn;
   grouped_tile<kGroupM>(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  const SW sw;
+  const int col = n0 + wn * C::WTN + sw.cl;
+  const bool cok = col < a.d;
+  const E* __restrict__ x = static_cast<const E*>(a.x);
+  E* __restrict__ dx = static_cast<E*>(a.dx);
+
+  typename R::T xin0[SW::IT], xin1[SW::IT];
+  auto load_block = [&](int mb, typename R::T (&buf)[SW::IT]) {
+    const int rb = m0 + wm * C::WTM + mb * 32;
+#pragma unroll
+    for (int it = 0; it < SW::IT; ++it) {
+      const int row = rb + sw.rl(it);
+      buf[it] = row < a.T && cok ? R::load(x + (int64_t)row * a.d + col) : R::zero();
+    }
+  };
+  typename R::T graw = R::zero();
+  RowVals<C> srv;
+  auto pre = [&]() {   // the row values first: they are needed first
+    srv.load([&](int i) {
+      const int t = m0 + i;
+      if (t >= a.T) return 0.f;
+      const float* p = a.spart + (int64_t)t * a.nspart;
+      float sum = 0.f;
+      for (int k = 0; k < a.nspart; ++k) sum += p[k];
+      return sum * a.rstd[t] * a.invD;
+    });
+    graw = cok ? R::load(static_cast<const E*>(a.gamma) + col) : R::zero();
+    load_block(0, xin0);
+  };
+
   Opnd oa{a.dh, gr, a.T, gr};   // dh' [T, gr]
   Opnd ob{a.A, gr, a.d, gr};    // A^T: (n = j, k = c) at A[j*gr + c]
   f32x16 acc[C::MB][C::NB];
-  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc);
-  for (int i = threadIdx.x; i < C::BM; i += C::THREADS) {
-    const int t = m0 + i;
-    float s = 0.f;
-    if (t < a.T) {
-      const float* p = a.spart + (int64_t)t * a.nspart;
-      for (int k = 0; k < a.nspart; ++k) s += p[k];
-      s *= a.rstd[t] * a.invD;
-    }
-    srow[i] = s;
-  }
+  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc, pre);
+  srv.publish(srow);
   __syncthreads();
-  dx_epilogue<C>(acc, a.T, a.d, static_cast<const E*>(a.x), static_cast<const E*>(a.gamma), static_cast<E*>(a.dx),
-                 srow, m0, n0);
+
+  const float4 g4 = R::f4(graw);
+  char LR_LDS* reg = stage_region<C>(lds);
+  // block mb computes from `cur` while block mb+1 loads into `nxt`
+  auto block = [&](int mb, const typename R::T (&cur)[SW::IT], typename R::T (&nxt)[SW::IT]) {
+    if (mb + 1 < C::MB) load_block(mb + 1, nxt);
+    stage_block<C>(acc, mb, reg);
+    const int rb = m0 + wm * C::WTM + mb * 32;
+#pragma unroll
+    for (int it = 0; it < SW::IT; ++it) {
+      const int rl = sw.rl(it), row = rb + rl;
+      if (row >= a.T || !cok) continue;
+      const float4 v = lds_f4(reg + rl * RowStage<C>::PITCH + sw.cl * 4);
+      const float4 x4 = R::f4(cur[it]);
+      const float sr = srow[row - m0];
+      store4(dx + (int64_t)row * a.d + col, g4.x * v.x - x4.x * sr, g4.y * v.y - x4.y * sr,
+             g4.z * v.z - x4.z * sr, g4.w * v.w - x4.w * sr);
+    }
+  };
+#pragma unroll
+  for (int mb = 0; mb < C::MB; mb += 2) {
+    block(mb, xin0, xin1);
+    if (mb + 1 < C::MB) block(mb + 1, xin1, xin0);
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -705,9 +737,13 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   const int tilesA = cdiv(a.d, C::BM) * cdiv(gr, C::BN);
   const int total = (a.n_up * tilesB + tilesA) * a.nsplit;
   hipLaunchKernelGGL((k_wgrad<C>), dim3(total), dim3(C::THREADS), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  const int64_t n4 = ((int64_t)a.n_up * a.r * a.d + (int64_t)a.d * gr) / 4;
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
+  if (a.nsplit == 1) return hipSuccess;
+  const int64_t n4 = ((int64_t)a.n_up * a.r * a.d + (int64_t)a.d * a.g * a.r) / 4;
   hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -741,6 +777,8 @@ template hipError_t launch_dz<bf16>(const DzArgs&, int, hipStream_t);
 template hipError_t launch_dz<float>(const DzArgs&, int, hipStream_t);
 template hipError_t launch_wgrad<bf16>(const WgradArgs&, hipStream_t);
 template hipError_t launch_wgrad<float>(const WgradArgs&, hipStream_t);
+template hipError_t launch_wgrad_reduce<bf16>(const WgradArgs&, hipStream_t);
+template hipError_t launch_wgrad_reduce<float>(const WgradArgs&, hipStream_t);
 template hipError_t launch_dx<bf16>(const DxArgs&, hipStream_t);
 template hipError_t launch_dx<float>(const DxArgs&, hipStream_t);
 template int dz_nparts<bf16>(int);

@@ -25,6 +25,8 @@
 // own loads, which complete in order).
 #pragma once
 
+#include <type_traits>
+
 #include "lr_device.h"
 
 namespace lr {
@@ -45,7 +47,10 @@ struct PipeCfg {
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LPS_A = A_BYTES / (1024 * NWAVES), LPS_B = B_BYTES / (1024 * NWAVES);
   static constexpr int LPS = LPS_A + LPS_B;                // DMA instructions per stage per wave
-  static constexpr int LDS_UINT4 = STAGES * STAGE_BYTES / 16;
+  // ring of STAGES stages, then a stage-sized sink that takes the (zero) loads of
+  // stages past the end of K, so that they never land on LDS the epilogue uses
+  static constexpr int SINK_BYTE = STAGES * STAGE_BYTES;
+  static constexpr int LDS_UINT4 = (STAGES + 1) * STAGE_BYTES / 16;
   static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "tile / wave mismatch");
   static_assert(BK % 16 == 0 && (BK * 2 == 64 || BK * 2 == 128), "BK must be 32 or 64");
   static_assert((STAGES - 1) * LPS <= 63, "vmcnt range");
@@ -72,7 +77,10 @@ __device__ __forceinline__ Rsrc4 rsrc4(const void* p, int64_t bytes) {
 
 __device__ __forceinline__ void dma16(const Rsrc4& r, uint32_t voff, uint32_t lds_byte) {
   typedef int int4v __attribute__((ext_vector_type(4)));
-  const int4v rs = {r.x, r.y, r.z, r.w};
+  // the resource is wave-uniform; readfirstlane keeps it in SGPRs where the
+  // compiler cannot prove that by itself
+  const int4v rs = {__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                    __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_byte)
                : "memory");
 }
@@ -173,12 +181,20 @@ __device__ __forceinline__ uint4 frag(const char LR_LDS* t, int rbase, int s, in
 // sum of squares of the 8 bf16 values of a fragment register
 __device__ __forceinline__ float frag_sumsq(const uint4& q) { return sumsq_vec(q, (bf16*)nullptr); }
 
+// pre() hook of kernels that load nothing ahead of their epilogue
+struct NoPre {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // Mainloop over k in [kbeg, kbeg + K); same contract as gemm_tile (accumulator
 // layout, ROWSTAT result in rowss[0..BM)).
-template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB>
+// `pre()` runs once, two k steps before the end (at the start when there are
+// fewer): kernels issue the global loads of their epilogue inputs there so that
+// they arrive while the last MFMAs run.
+template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB, class Pre>
 __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
                                           int n0, int kbeg, int K, uint4* lds, float* rowss,
-                                          f32x16 (&acc)[C::MB][C::NB]) {
+                                          f32x16 (&acc)[C::MB][C::NB], Pre&& pre) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -205,7 +221,7 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
   auto issue_stage = [&](int st) {
     // stages past the end read nothing (empty resource) and fill a buffer no one reads with zeros
     const bool live = st < nk;
-    const uint32_t buf = lds0 + (st % C::STAGES) * C::STAGE_BYTES;
+    const uint32_t buf = lds0 + (live ? (st % C::STAGES) * C::STAGE_BYTES : C::SINK_BYTE);
     da.issue(da.rsrc(st, live), buf, wave);
     db.issue(db.rsrc(st, live), buf + C::A_BYTES, wave);
   };
@@ -236,11 +252,15 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
     // half during the first sub-step of stage kt+1, one load per few MFMAs, so that
     // this in-order wave never stalls on a burst of load issues while the MFMA pipe
     // runs dry.  Fragment reads of the next sub-step are interleaved the same way.
+    // Stages past the end read an empty range into the sink, which keeps the load
+    // count of every k step the same.  pre() runs at the start of the last k step,
+    // which has no wait and no barrier, so its loads overlap the last MFMAs.
     constexpr int QA = DmaTile<C, C::BM, A_MNC>::Q, QB = DmaTile<C, C::BN, B_MNC>::Q;
     constexpr int HALF = (QA + QB) / 2;
     constexpr int NMF = C::MB * C::NB;
     constexpr int NF = C::MB + C::NB;
     static_assert((QA + QB) % 2 == 0 && HALF <= NMF, "load spreading");
+    static_assert(C::KS >= 2, "the refill is split over the first and the last sub-step");
     auto issue_q = [&](int q, const Rsrc4& ra, const Rsrc4& rb, uint32_t buf) {
       if (q < QA)
         da.issue_one(q, ra, buf, wave);
@@ -249,8 +269,9 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
     };
 #pragma unroll
     for (int st = 0; st < C::STAGES - 1; ++st) issue_stage(st);
-    Rsrc4 pra = da.rsrc(C::STAGES - 1, C::STAGES - 1 < nk), prb = db.rsrc(C::STAGES - 1, C::STAGES - 1 < nk);
-    uint32_t pbuf = lds0 + ((C::STAGES - 1) % C::STAGES) * C::STAGE_BYTES;
+    constexpr int ST0 = C::STAGES - 1;
+    Rsrc4 pra = da.rsrc(ST0, ST0 < nk), prb = db.rsrc(ST0, ST0 < nk);
+    uint32_t pbuf = lds0 + (ST0 < nk ? ST0 * C::STAGE_BYTES : C::SINK_BYTE);
 #pragma unroll
     for (int q = 0; q < HALF; ++q) issue_q(q, pra, prb, pbuf);
     wait_vmcnt<(C::STAGES - 2) * C::LPS + HALF>();
@@ -258,6 +279,8 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
     uint4 a[2][C::MB], b[2][C::NB];
     read_frags(0, 0, a[0], b[0]);
     for (int kt = 0; kt < nk; ++kt) {
+      const bool final_k = kt + 1 == nk;
+      if (final_k) pre();
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
         const int cur = s & 1, nxt = cur ^ 1;
@@ -267,18 +290,21 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
         int qbase = HALF;               // first sub-step: second half of the pending refill
         int fst = kt, fs = s + 1;       // source of the next fragments
         if (last) {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          wait_vmcnt<(C::STAGES - 2) * C::LPS>();
-          block_barrier();
+          if (!final_k) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            wait_vmcnt<(C::STAGES - 2) * C::LPS>();
+            block_barrier();
+          }
           const int st = kt + C::STAGES;
-          ra = da.rsrc(st, st < nk);
-          rb = db.rsrc(st, st < nk);
-          buf = lds0 + (st % C::STAGES) * C::STAGE_BYTES;
+          const bool live = st < nk;
+          ra = da.rsrc(st, live);
+          rb = db.rsrc(st, live);
+          buf = lds0 + (live ? (st % C::STAGES) * C::STAGE_BYTES : C::SINK_BYTE);
           pra = ra;
           prb = rb;
           pbuf = buf;
           qbase = 0;
-          fst = kt + 1;                 // past the end: unused reads of a zero-filled buffer
+          fst = kt + 1;                 // past the end: reads nobody uses
           fs = 0;
         }
         const bool loads_here = last || s == 0;
@@ -305,7 +331,11 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
         }
       }
     }
-    wait_vmcnt<0>();
+    // Every load of a real stage has landed.  Sink loads may still be in flight:
+    // without epilogue loads nothing else waits for them before the work-group ends.
+    if constexpr (std::is_same<std::decay_t<Pre>, NoPre>::value) wait_vmcnt<0>();
+  } else {
+    pre();
   }
   if constexpr (ROWSTAT) {
     static_assert(!A_MNC, "row statistics need a K-contiguous A");
@@ -321,14 +351,17 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
   __syncthreads();
 }
 
-template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB>
+
+template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB, class Pre = NoPre>
 __device__ __forceinline__ void mainloop(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
                                          int n0, int kbeg, int K, uint4* lds, float* rowss,
-                                         f32x16 (&acc)[C::MB][C::NB]) {
-  if constexpr (C::PIPE)
-    gemm_pipe<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc);
-  else
+                                         f32x16 (&acc)[C::MB][C::NB], Pre&& pre = Pre{}) {
+  if constexpr (C::PIPE) {
+    gemm_pipe<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc, pre);
+  } else {
     gemm_tile<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc);
+    pre();
+  }
 }
 
 }  // namespace lr
