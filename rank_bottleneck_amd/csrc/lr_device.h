@@ -106,6 +106,7 @@ template <typename E_, int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
   using E = E_;
   static constexpr bool PIPE = false;
+  static constexpr bool REGS = false;
   static constexpr int WPE = 1;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk

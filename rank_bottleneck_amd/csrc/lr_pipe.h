@@ -33,10 +33,13 @@ namespace lr {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int WPE_ = 1>
+// REGS_: operand tiles travel global -> registers -> LDS (two LDS buffers,
+// one stage in registers) instead of by direct-to-LDS loads.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int WPE_ = 1, bool REGS_ = false>
 struct PipeCfg {
   using E = bf16;
   static constexpr bool PIPE = true;
+  static constexpr bool REGS = REGS_;
   static constexpr int WPE = WPE_;  // waves per SIMD the kernels are built for
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr int VEC = 8;
@@ -47,10 +50,13 @@ struct PipeCfg {
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LPS_A = A_BYTES / (1024 * NWAVES), LPS_B = B_BYTES / (1024 * NWAVES);
   static constexpr int LPS = LPS_A + LPS_B;                // DMA instructions per stage per wave
-  // ring of STAGES stages, then a stage-sized sink that takes the (zero) loads of
-  // stages past the end of K, so that they never land on LDS the epilogue uses
+  // ring of STAGES stages, then a sink that takes the (zero) loads of stages past
+  // the end of K, A and B parts on top of each other, so that they never land on
+  // LDS the epilogue uses
   static constexpr int SINK_BYTE = STAGES * STAGE_BYTES;
-  static constexpr int LDS_UINT4 = (STAGES + 1) * STAGE_BYTES / 16;
+  static constexpr int SINK_BYTES = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
+  static constexpr int LDS_UINT4 = (STAGES * STAGE_BYTES + (REGS ? 0 : SINK_BYTES)) / 16;
+  static_assert(!REGS || STAGES == 2, "register staging uses two LDS buffers");
   static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "tile / wave mismatch");
   static_assert(BK % 16 == 0 && (BK * 2 == 64 || BK * 2 == 128), "BK must be 32 or 64");
   static_assert((STAGES - 1) * LPS <= 63, "vmcnt range");
@@ -143,6 +149,13 @@ struct DmaTile {
     return Rsrc4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), live ? (int)b : 0, 0x00020000};
   }
 
+  // the same range as a compiler buffer resource (register staging)
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(int st, bool live) const {
+    int64_t b = bytes0 - (int64_t)st * step;
+    b = b < 0 ? 0 : (b > kMaxRecords ? kMaxRecords : b);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base0) + (int64_t)st * step, (short)0,
+                                             live ? (int)b : 0, 0x00020000);
+  }
   __device__ __forceinline__ void issue(const Rsrc4& r, uint32_t lds_tile, int wave) const {
 #pragma unroll
     for (int q = 0; q < Q; ++q) dma16(r, off[q], lds_tile + (q * C::NWAVES + wave) * 1024);
@@ -178,8 +191,19 @@ __device__ __forceinline__ uint4 frag(const char LR_LDS* t, int rbase, int s, in
   }
 }
 
-// sum of squares of the 8 bf16 values of a fragment register
-__device__ __forceinline__ float frag_sumsq(const uint4& q) { return sumsq_vec(q, (bf16*)nullptr); }
+// running sum of squares of the 8 bf16 values of a fragment register (packed
+// bf16 dot products, fp32 accumulation)
+__device__ __forceinline__ float frag_sumsq(const uint4& q, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w[i]);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+  }
+  return acc;
+}
+
 
 // pre() hook of kernels that load nothing ahead of their epilogue
 struct NoPre {
@@ -221,9 +245,9 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
   auto issue_stage = [&](int st) {
     // stages past the end read nothing (empty resource) and fill a buffer no one reads with zeros
     const bool live = st < nk;
-    const uint32_t buf = lds0 + (live ? (st % C::STAGES) * C::STAGE_BYTES : C::SINK_BYTE);
-    da.issue(da.rsrc(st, live), buf, wave);
-    db.issue(db.rsrc(st, live), buf + C::A_BYTES, wave);
+    const uint32_t ba = lds0 + (live ? (st % C::STAGES) * C::STAGE_BYTES : C::SINK_BYTE);
+    da.issue(da.rsrc(st, live), ba, wave);
+    db.issue(db.rsrc(st, live), live ? ba + C::A_BYTES : ba, wave);
   };
   auto read_frags = [&](int st, int s, uint4 (&fa)[C::MB], uint4 (&fb)[C::NB]) {
     const char LR_LDS* ta = ldsp + (st % C::STAGES) * C::STAGE_BYTES;
@@ -261,19 +285,21 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
     constexpr int NF = C::MB + C::NB;
     static_assert((QA + QB) % 2 == 0 && HALF <= NMF, "load spreading");
     static_assert(C::KS >= 2, "the refill is split over the first and the last sub-step");
-    auto issue_q = [&](int q, const Rsrc4& ra, const Rsrc4& rb, uint32_t buf) {
+    // ba / bb: LDS bases of the A and B parts (both the sink for stages past the end)
+    auto issue_q = [&](int q, const Rsrc4& ra, const Rsrc4& rb, uint32_t ba, uint32_t bb) {
       if (q < QA)
-        da.issue_one(q, ra, buf, wave);
+        da.issue_one(q, ra, ba, wave);
       else
-        db.issue_one(q - QA, rb, buf + C::A_BYTES, wave);
+        db.issue_one(q - QA, rb, bb, wave);
     };
 #pragma unroll
     for (int st = 0; st < C::STAGES - 1; ++st) issue_stage(st);
     constexpr int ST0 = C::STAGES - 1;
     Rsrc4 pra = da.rsrc(ST0, ST0 < nk), prb = db.rsrc(ST0, ST0 < nk);
-    uint32_t pbuf = lds0 + (ST0 < nk ? ST0 * C::STAGE_BYTES : C::SINK_BYTE);
+    uint32_t pba = lds0 + (ST0 < nk ? ST0 * C::STAGE_BYTES : C::SINK_BYTE);
+    uint32_t pbb = ST0 < nk ? pba + C::A_BYTES : pba;
 #pragma unroll
-    for (int q = 0; q < HALF; ++q) issue_q(q, pra, prb, pbuf);
+    for (int q = 0; q < HALF; ++q) issue_q(q, pra, prb, pba, pbb);
     wait_vmcnt<(C::STAGES - 2) * C::LPS + HALF>();
     block_barrier();
     uint4 a[2][C::MB], b[2][C::NB];
@@ -286,7 +312,7 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
         const int cur = s & 1, nxt = cur ^ 1;
         const bool last = s + 1 == C::KS;
         Rsrc4 ra = pra, rb = prb;
-        uint32_t buf = pbuf;
+        uint32_t ba = pba, bb = pbb;
         int qbase = HALF;               // first sub-step: second half of the pending refill
         int fst = kt, fs = s + 1;       // source of the next fragments
         if (last) {
@@ -299,10 +325,12 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
           const bool live = st < nk;
           ra = da.rsrc(st, live);
           rb = db.rsrc(st, live);
-          buf = lds0 + (live ? (st % C::STAGES) * C::STAGE_BYTES : C::SINK_BYTE);
+          ba = lds0 + (live ? (st % C::STAGES) * C::STAGE_BYTES : C::SINK_BYTE);
+          bb = live ? ba + C::A_BYTES : ba;
           pra = ra;
           prb = rb;
-          pbuf = buf;
+          pba = ba;
+          pbb = bb;
           qbase = 0;
           fst = kt + 1;                 // past the end: reads nobody uses
           fs = 0;
@@ -310,11 +338,9 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
         const bool loads_here = last || s == 0;
         const char LR_LDS* fa = ldsp + (fst % C::STAGES) * C::STAGE_BYTES;
         const char LR_LDS* fb = fa + C::A_BYTES;
-        if constexpr (ROWSTAT) {
-          if (wn == 0) {
+        if constexpr (ROWSTAT) {   // every wave (no branch); the wn == 0 waves publish
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) ss[mb] += frag_sumsq(a[cur][mb]);
-          }
+          for (int mb = 0; mb < C::MB; ++mb) ss[mb] = frag_sumsq(a[cur][mb], ss[mb]);
         }
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
@@ -326,7 +352,7 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
               b[nxt][i - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (i - C::MB) * 32, fs, lane);
           }
           constexpr int EVERY = NMF / HALF;
-          if (loads_here && (i % EVERY) == EVERY - 1) issue_q(qbase + i / EVERY, ra, rb, buf);
+          if (loads_here && (i % EVERY) == EVERY - 1) issue_q(qbase + i / EVERY, ra, rb, ba, bb);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -352,11 +378,146 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
 }
 
 
+// Register-staged mainloop (C::REGS): the same LDS image and fragment reads as
+// gemm_pipe, filled by ordinary buffer loads into registers and LDS stores.
+// Stage kt is read from LDS buffer kt%2 while its successor's registers are
+// stored into the other buffer (sub-steps 0 and 1) and the loads of stage kt+2
+// are issued (sub-step 2); one barrier per stage, at the start of the last
+// sub-step.  The compiler tracks every load, so pre() needs no accounting.
+template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB, class Pre>
+__device__ __forceinline__ void gemm_regs(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
+                                          int n0, int kbeg, int K, uint4* lds, float* rowss,
+                                          f32x16 (&acc)[C::MB][C::NB], Pre&& pre) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  float ss[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) ss[mb] = 0.f;
+
+  DmaTile<C, C::BM, A_MNC> da;
+  DmaTile<C, C::BN, B_MNC> db;
+  da.init(oa, ma, m0, wave, lane);
+  db.init(ob, mbm, n0, wave, lane);
+  da.init_range(oa, m0, kbeg);
+  db.init_range(ob, n0, kbeg);
+  const char LR_LDS* ldsp = (const char LR_LDS*)(lds);
+  char LR_LDS* ldsw = (char LR_LDS*)(lds);
+  const int nk = (K + C::BK - 1) / C::BK;
+  constexpr int QA = DmaTile<C, C::BM, A_MNC>::Q, QB = DmaTile<C, C::BN, B_MNC>::Q, QT = QA + QB;
+  constexpr int NMF = C::MB * C::NB;
+  constexpr int NF = C::MB + C::NB;
+  static_assert(C::KS == 4 && QT % 2 == 0 && QT / 2 <= NMF && QT <= NMF, "register staging schedule");
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+  uint4 stg[QT];
+  auto gload_one = [&](int q, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb) {
+    if (q < QA)
+      stg[q] = buf_load16(rsa, da.off[q]);
+    else
+      stg[q] = buf_load16(rsb, db.off[q - QA]);
+  };
+  // LDS byte of staged vector q of this lane in buffer `buf` (the direct-load image)
+  auto lds_byte = [&](int q, int buf) {
+    const int part = q < QA ? 0 : C::A_BYTES, qq = q < QA ? q : q - QA;
+    return buf * C::STAGE_BYTES + part + (qq * C::NWAVES + wave) * 1024 + 16 * lane;
+  };
+  auto lwrite_one = [&](int q, int buf) {
+    *reinterpret_cast<u32x4 LR_LDS*>(ldsw + lds_byte(q, buf)) = __builtin_bit_cast(u32x4, stg[q]);
+  };
+  auto read_frags = [&](int st, int s, uint4 (&fa)[C::MB], uint4 (&fb)[C::NB]) {
+    const char LR_LDS* ta = ldsp + (st & 1) * C::STAGE_BYTES;
+    const char LR_LDS* tb = ta + C::A_BYTES;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, s, lane);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, s, lane);
+  };
+
+  if (nk > 0) {
+    {
+      const __amdgpu_buffer_rsrc_t rsa = da.brsrc(0, true), rsb = db.brsrc(0, true);
+#pragma unroll
+      for (int q = 0; q < QT; ++q) gload_one(q, rsa, rsb);
+#pragma unroll
+      for (int q = 0; q < QT; ++q) lwrite_one(q, 0);
+      const __amdgpu_buffer_rsrc_t rsa1 = da.brsrc(1, 1 < nk), rsb1 = db.brsrc(1, 1 < nk);
+#pragma unroll
+      for (int q = 0; q < QT; ++q) gload_one(q, rsa1, rsb1);
+    }
+    __syncthreads();
+    uint4 a[2][C::MB], b[2][C::NB];
+    read_frags(0, 0, a[0], b[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool final_k = kt + 1 == nk;
+      if (final_k) pre();
+      const int nbuf = (kt + 1) & 1;
+      const __amdgpu_buffer_rsrc_t rsa = da.brsrc(kt + 2, kt + 2 < nk), rsb = db.brsrc(kt + 2, kt + 2 < nk);
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int cur = s & 1, nxt = cur ^ 1;
+        const bool last = s + 1 == C::KS;
+        int fst = kt, fs = s + 1;
+        if (last) {
+          if (!final_k) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            block_barrier();
+          }
+          fst = kt + 1;   // past the end: reads nobody uses
+          fs = 0;
+        }
+        const char LR_LDS* fa = ldsp + (fst & 1) * C::STAGE_BYTES;
+        const char LR_LDS* fb = fa + C::A_BYTES;
+        if constexpr (ROWSTAT) {   // every wave (no branch); the wn == 0 waves publish
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) ss[mb] = frag_sumsq(a[cur][mb], ss[mb]);
+        }
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          mfma_chunk(acc[i / C::NB][i % C::NB], b[cur][i % C::NB], a[cur][i / C::NB], (bf16*)nullptr);
+          if (i < NF) {
+            if (i < C::MB)
+              a[nxt][i] = frag<C, C::BM, A_MNC>(fa, wm * C::WTM + i * 32, fs, lane);
+            else
+              b[nxt][i - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (i - C::MB) * 32, fs, lane);
+          }
+          constexpr int WEVERY = NMF / (QT / 2), LEVERY = NMF / QT;
+          if (s < 2 && (i % WEVERY) == WEVERY - 1) lwrite_one(s * (QT / 2) + i / WEVERY, nbuf);
+          if (s == 2 && (i % LEVERY) == LEVERY - 1) gload_one(i / LEVERY, rsa, rsb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else {
+    pre();
+  }
+  if constexpr (ROWSTAT) {
+    static_assert(!A_MNC, "row statistics need a K-contiguous A");
+    __syncthreads();  // rowss may alias the buffers: every wave is past its last fragment read
+    if (wn == 0) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const float v = ss[mb] + __shfl_xor(ss[mb], 32);
+        if (lane < 32) rowss[wm * C::WTM + mb * 32 + lane] = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB, class Pre = NoPre>
 __device__ __forceinline__ void mainloop(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
                                          int n0, int kbeg, int K, uint4* lds, float* rowss,
                                          f32x16 (&acc)[C::MB][C::NB], Pre&& pre = Pre{}) {
-  if constexpr (C::PIPE) {
+  if constexpr (C::PIPE && C::REGS) {
+    gemm_regs<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc, pre);
+  } else if constexpr (C::PIPE) {
     gemm_pipe<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc, pre);
   } else {
     gemm_tile<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc);
