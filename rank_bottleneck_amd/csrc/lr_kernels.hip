@@ -607,7 +607,7 @@ template <typename E>
 struct Cfgs;
 template <>
 struct Cfgs<bf16> {
-  using Main = PipeCfg<256, 256, 32, 2, 2, 4>;
+  using Main = PipeCfg<256, 256, 64, 2, 2, 2>;
 };
 template <>
 struct Cfgs<float> {

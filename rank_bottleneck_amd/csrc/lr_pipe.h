@@ -142,19 +142,23 @@ struct DmaTile {
       step = (int64_t)C::BK * o.ld * 2;
     }
   }
+  // bytes left from stage st, clamped to [0, kMaxRecords] with 32-bit compares of
+  // the two halves (scalar instructions only)
+  __device__ __forceinline__ uint32_t records(int st) const {
+    const int64_t b = bytes0 - (int64_t)st * step;
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)b >> 32));
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    return (hi >> 31) ? 0u : (hi != 0 || lo > (uint32_t)kMaxRecords ? (uint32_t)kMaxRecords : lo);
+  }
   __device__ __forceinline__ Rsrc4 rsrc(int st, bool live) const {
-    int64_t b = bytes0 - (int64_t)st * step;
-    b = b < 0 ? 0 : (b > kMaxRecords ? kMaxRecords : b);
     const uint64_t a = reinterpret_cast<uint64_t>(base0) + (uint64_t)((int64_t)st * step);
-    return Rsrc4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), live ? (int)b : 0, 0x00020000};
+    return Rsrc4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), live ? (int)records(st) : 0, 0x00020000};
   }
 
   // the same range as a compiler buffer resource (register staging)
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(int st, bool live) const {
-    int64_t b = bytes0 - (int64_t)st * step;
-    b = b < 0 ? 0 : (b > kMaxRecords ? kMaxRecords : b);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base0) + (int64_t)st * step, (short)0,
-                                             live ? (int)b : 0, 0x00020000);
+                                             live ? (int)records(st) : 0, 0x00020000);
   }
   __device__ __forceinline__ void issue(const Rsrc4& r, uint32_t lds_tile, int wave) const {
 #pragma unroll
