@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "low-rank block fwd+bwd TFLOP/s (bf16) and % MFMA peak; tokens/s per block"
+METRIC_FWD = "low-rank block forward HBM GB/s (small-rank, memory-bound sweep)"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (published)
 PEAK_GBS = 8000.0                                # MI355X HBM3E (published)
 KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
@@ -90,6 +91,8 @@ def cpu_baseline(wl, budget_s: float = 15.0):
         if wl.seam:
             p, ss = oracle.down_partial(*args[:3])
             oracle.up_finish(p, ss, args[3], wl.r, wl.g, wl.act, wl.eps, wl.D)
+        elif wl.fwd_only:
+            oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D)
         else:
             oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D)
             oracle.block_bwd(*args, [t.v for t in inp.dy], wl.r, wl.g, wl.act, wl.eps, wl.D)
@@ -102,6 +105,10 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     log(f"cpu oracle: probe {probe} rows {tp:.2f}s -> sample {rows} rows")
     t = run(rows)
     sub = wl.replace(T=rows)
+    if wl.fwd_only:
+        return {"value": sub.fwd_bytes() / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy forward, {t:.1f} s",
+                "tokens_per_s": rows / t}
     flops = sub.fwd_flops() + (0 if wl.seam else sub.bwd_flops())
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy fwd+bwd, {t:.1f} s",
@@ -132,7 +139,7 @@ def main():
     wl = WORKLOADS[args.workload]
     log("workload", wl)
     torch.cuda.set_device(0)
-    inp = make_inputs(wl, seed=0, with_dy=not wl.seam)
+    inp = make_inputs(wl, seed=0, with_dy=not (wl.seam or wl.fwd_only))
 
     def dev(t):
         if t.dtype == "bf16":
@@ -141,7 +148,7 @@ def main():
 
     x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
     B = [dev(b) for b in inp.B]
-    dy = None if wl.seam else [dev(t) for t in inp.dy]
+    dy = None if (wl.seam or wl.fwd_only) else [dev(t) for t in inp.dy]
     del inp
     dims = rb.make_dims(wl.T, wl.d, wl.r, wl.g, wl.act, wl.dtype, wl.eps, wl.d_norm)
     dt = rb.TORCH_DTYPE[dims.dtype]
@@ -156,6 +163,10 @@ def main():
         def step():
             rb.lr_down_partial(dims, x, gamma, A, partial, sumsq, wsf)
             rb.lr_up_finish(dims, partial, sumsq, B, y, h, wsf)
+        flops = wl.fwd_flops()
+    elif wl.fwd_only:
+        def step():
+            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, wsf)
         flops = wl.fwd_flops()
     else:
         wsb = rb.workspace(dims, True)
@@ -229,11 +240,16 @@ def main():
         if rec and rec.get("source_hash") == source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
 
-    out = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+    metric, value, unit = METRIC, tflops, "TFLOP/s"
+    if wl.fwd_only:
+        metric, value, unit = METRIC_FWD, wl.fwd_bytes() / (ms_step * 1e-3) / 1e9, "GB/s"
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
            "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "r": wl.r, "g": wl.g, "act": wl.act,
-                      "d_norm": wl.D, "step": "seam fwd" if wl.seam else "fwd+bwd", "parallelism": "none (1 GPU)"},
+                      "d_norm": wl.D, "step": "seam fwd" if wl.seam else ("fwd" if wl.fwd_only else "fwd+bwd"),
+                      "parallelism": "none (1 GPU)"},
+           "tflops": tflops,
            "tokens_per_s": wl.T / (ms_step * 1e-3),
            "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wl.dtype],
            "kernel_ms_warmup_step": per_kernel,

@@ -81,6 +81,8 @@ template <typename E> hipError_t launch_fold_gamma(const void* A, const void* ga
                                                    hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 template <typename E> hipError_t launch_down(const DownArgs& a, hipStream_t s);
+// whether launch_down picks its 64-row tiles for this shape (fewer 256 x 256 tiles than CUs)
+template <typename E> bool down_uses_skinny(int T, int r, int g, bool gateup);
 template <typename E> hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, int T,
                                                int r, int g, int act, float invD, float eps, hipStream_t s);

@@ -603,16 +603,36 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
 }
 
 // ------------------------------------------------------------------ launchers
+
 template <typename E>
 struct Cfgs;
 template <>
 struct Cfgs<bf16> {
   using Main = PipeCfg<256, 256, 64, 2, 2, 2>;
+  // 64-row tiles for a down-projection whose 256 x 256 grid would leave CUs idle
+  // (small g*r): four waves side by side over 256 columns
+  using Skinny = PipeCfg<64, 256, 64, 1, 4, 2>;
+  static constexpr bool HAS_SKINNY = true;
 };
 template <>
 struct Cfgs<float> {
   using Main = TileCfg<float, 128, 128, 2, 2>;
+  using Skinny = Main;
+  static constexpr bool HAS_SKINNY = false;
 };
+
+constexpr int kNumCu = 256;
+
+// The skinny down tiles are used when the 256 x 256 grid has fewer tiles than CUs.
+template <typename E>
+bool down_uses_skinny(int T, int r, int g, bool gateup) {
+  if (!Cfgs<E>::HAS_SKINNY) return false;
+  using C = typename Cfgs<E>::Main;
+  const int tiles = ((T + C::BM - 1) / C::BM) * (gateup ? (2 * r + C::BN - 1) / C::BN : (g * r + C::BN - 1) / C::BN);
+  return tiles < kNumCu;
+}
+template bool down_uses_skinny<bf16>(int, int, int, bool);
+template bool down_uses_skinny<float>(int, int, int, bool);
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -640,20 +660,28 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E>
-hipError_t launch_down(const DownArgs& a, hipStream_t s) {
-  using C = typename Cfgs<E>::Main;
-  if (a.T == 0) return hipSuccess;
-  const int gr = a.g * a.r;
+template <class C>
+hipError_t launch_down_cfg(const DownArgs& a, hipStream_t s) {
   const bool gateup = a.act == ACT_SWIGLU && a.mode == DOWN_BLOCK;
   if (gateup) {
     const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN / 2);
     hipLaunchKernelGGL((k_down<C, true>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   } else {
-    const int tiles = cdiv(a.T, C::BM) * cdiv(gr, C::BN);
+    const int tiles = cdiv(a.T, C::BM) * cdiv(a.g * a.r, C::BN);
     hipLaunchKernelGGL((k_down<C, false>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_down(const DownArgs& a, hipStream_t s) {
+  using C = typename Cfgs<E>::Main;
+  if (a.T == 0) return hipSuccess;
+  if constexpr (Cfgs<E>::HAS_SKINNY) {
+    if (down_uses_skinny<E>(a.T, a.r, a.g, a.act == ACT_SWIGLU && a.mode == DOWN_BLOCK))
+      return launch_down_cfg<typename Cfgs<E>::Skinny>(a, s);
+  }
+  return launch_down_cfg<C>(a, s);
 }
 
 template <typename E>

@@ -135,7 +135,7 @@ struct DmaTile {
       base0 = static_cast<const char*>(o.p) + ((int64_t)mn0 * o.ld + kbeg) * 2;
       bytes0 = ((int64_t)(o.MN - mn0 - 1) * o.ld + (o.K - kbeg)) * 2;
       step = (int64_t)C::BK * 2;
-      if (o.MN - mn0 <= 0) bytes0 = -(int64_t)1 << 62;
+      if (o.MN - mn0 <= 0) bytes0 = -((int64_t)1 << 62);
     } else {
       base0 = static_cast<const char*>(o.p) + ((int64_t)kbeg * o.ld + mn0) * 2;
       bytes0 = ((int64_t)(o.K - kbeg - 1) * o.ld + (o.MN - mn0)) * 2;
@@ -284,10 +284,10 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
     // count of every k step the same.  pre() runs at the start of the last k step,
     // which has no wait and no barrier, so its loads overlap the last MFMAs.
     constexpr int QA = DmaTile<C, C::BM, A_MNC>::Q, QB = DmaTile<C, C::BN, B_MNC>::Q;
-    constexpr int HALF = (QA + QB) / 2;
+    constexpr int HALF = (QA + QB) / 2;          // loads in the last sub-step; the rest in the first
+    constexpr int REST = QA + QB - HALF;
     constexpr int NMF = C::MB * C::NB;
     constexpr int NF = C::MB + C::NB;
-    static_assert((QA + QB) % 2 == 0 && HALF <= NMF, "load spreading");
     static_assert(C::KS >= 2, "the refill is split over the first and the last sub-step");
     // ba / bb: LDS bases of the A and B parts (both the sink for stages past the end)
     auto issue_q = [&](int q, const Rsrc4& ra, const Rsrc4& rb, uint32_t ba, uint32_t bb) {
@@ -355,8 +355,14 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
             else
               b[nxt][i - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (i - C::MB) * 32, fs, lane);
           }
-          constexpr int EVERY = NMF / HALF;
-          if (loads_here && (i % EVERY) == EVERY - 1) issue_q(qbase + i / EVERY, ra, rb, ba, bb);
+          // the sub-step's n loads go out after MFMAs floor(j*NMF/n) + NMF/n - 1, spread evenly
+          if (loads_here) {
+            const int n = last ? HALF : REST;
+#pragma unroll
+            for (int j = 0; j < (HALF > REST ? HALF : REST); ++j)
+              if (j < n && (j * NMF) / n + (NMF / n > 0 ? NMF / n : 1) - 1 == (i < NMF ? i : NMF - 1))
+                issue_q(qbase + j, ra, rb, ba, bb);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }

@@ -72,6 +72,20 @@ def test_block_forward_backward_small(wl):
         assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
 
 
+def test_forward_main_down_tiles_ragged():
+    """The small cases above have fewer 256 x 256 down tiles than CUs, so their
+    down-projection runs on 64-row tiles; this shape (264 tiles, ragged T) runs the
+    256 x 256 tiles, compared in full."""
+    wl = Workload("bf16_main_tiles", 8269, 128, 1024, 2, "silu", "bf16")
+    _say("main tiles", wl)
+    inp = make_inputs(wl, seed=2, with_dy=False)
+    _, _, y, h = _run_fwd(wl, inp)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    for i, yi in enumerate(y):
+        assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+
+
 @pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5]], ids=lambda w: w.name)
 def test_inference_forward_without_checkpoint(wl):
     inp = make_inputs(wl, seed=2, with_dy=False)

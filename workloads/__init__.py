@@ -43,6 +43,7 @@ class Workload:
     d_norm: int = 0       # 0 -> d ; the unsharded width for a tensor-parallel shard
     d_weight: int = 0     # width used for A's init variance; 0 -> d
     seam: bool = False    # run through the shard seam (partial + finish) instead of the fused block
+    fwd_only: bool = False  # benchmarked as a forward pass (HBM-bound small-rank sweep)
     note: str = ""
 
     @property
@@ -58,6 +59,14 @@ class Workload:
 
     def bwd_flops(self) -> float:
         return 4.0 * self.T * self.r * self.d * self.n_up + 4.0 * self.T * self.d * self.g * self.r
+
+    def fwd_bytes(self) -> float:
+        """Bytes a forward pass must move at least: x, gamma, A, the B_i, the y_i
+        and the saved rank-r pre-activation."""
+        e = 2 if self.dtype == "bf16" else 4
+        gr = self.g * self.r
+        return float(e * (self.T * self.d + self.d + self.d * gr + self.n_up * self.r * self.d
+                          + self.n_up * self.T * self.d + self.T * gr))
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -81,7 +90,7 @@ WORKLOADS: Dict[str, Workload] = {
 # memory-bound small-rank sweep (forward)
 for _r in (64, 128, 256):
     WORKLOADS[f"small_r{_r}"] = Workload(f"small_r{_r}", T=16384, d=4096, r=_r, g=1, act="silu",
-                                         dtype="bf16")
+                                         dtype="bf16", fwd_only=True)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
