@@ -72,18 +72,39 @@ def test_block_forward_backward_small(wl):
         assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
 
 
-def test_forward_main_down_tiles_ragged():
-    """The small cases above have fewer 256 x 256 down tiles than CUs, so their
-    down-projection runs on 64-row tiles; this shape (264 tiles, ragged T) runs the
-    256 x 256 tiles, compared in full."""
-    wl = Workload("bf16_main_tiles", 8269, 128, 1024, 2, "silu", "bf16")
-    _say("main tiles", wl)
+# The small cases above have fewer 256 x 256 down tiles than CUs, so their
+# down-projection runs on 64-row tiles.  These shapes (ragged T, 396 and 264
+# tiles) run the 256 x 256 tiles, with a full and a nearly empty last round.
+@pytest.mark.parametrize("wl", [Workload("bf16_main_tiles", 8269, 128, 1536, 2, "silu", "bf16"),
+                                Workload("bf16_main_tiles_tail", 8269, 128, 1024, 2, "silu", "bf16")],
+                         ids=lambda w: w.name)
+def test_forward_down_tile_configs_ragged(wl):
+    _say("tile config", wl)
     inp = make_inputs(wl, seed=2, with_dy=False)
     _, _, y, h = _run_fwd(wl, inp)
     ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
     assert_close(host(h), ref["h"], wl.dtype, "h")
     for i, yi in enumerate(y):
         assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+
+
+def test_backward_256_tiles_ragged():
+    """More than one round of 256 x 256 tiles in down and dz (260, ragged T) at a
+    size the oracle takes whole; every gradient compared in full."""
+    wl = Workload("bf16_bwd_tiles", 16461, 128, 1024, 1, "silu", "bf16")
+    _say("256 tiles bwd", wl)
+    inp = make_inputs(wl, seed=3)
+    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    assert_close(host(y[0]), ref["y"][0], wl.dtype, "y0")
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy])
+    torch.cuda.synchronize()
+    rb_ = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), rb_[k], wl.dtype, k)
+    assert_close(host(g["dB"][0]), rb_["dB"][0], wl.dtype, "dB0")
 
 
 @pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5]], ids=lambda w: w.name)
