@@ -48,9 +48,18 @@ struct Carve {
   }
 };
 
+// split count of the small-rank forward for these dims (0: not used)
+int small_splits(const lr_dims* d) {
+  return d->dtype == LR_BF16 ? lr::small_rank_splits<bf16>((int)d->T, (int)d->d, (int)d->r, (int)d->g, d->act)
+                             : lr::small_rank_splits<float>((int)d->T, (int)d->d, (int)d->r, (int)d->g, d->act);
+}
+
+// A' (or A'^T), z, then for the small-rank forward the split partials and sums of squares
 size_t fwd_ws(const lr_dims* d) {
-  const size_t es = esize(d->dtype), gr = (size_t)(d->g * d->r);
-  return align_up((size_t)d->d * gr * es) + align_up((size_t)d->T * gr * es);
+  const size_t es = esize(d->dtype), gr = (size_t)(d->g * d->r), T = (size_t)d->T;
+  const size_t ns = (size_t)small_splits(d);
+  return align_up((size_t)d->d * gr * es) + align_up(T * gr * es) + align_up(ns * T * gr * 4) +
+         align_up(ns * T * 4);
 }
 
 template <typename E>
@@ -107,11 +116,28 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
-  lr::DownArgs da{};
-  da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_BLOCK;
-  da.invD = inv_width(d); da.eps = d->eps; da.h = h_save; da.z = z;
-  LR_LAUNCH("down", s, lr::launch_down<E>(da, s));
+  const int ns = small_splits(d);
+  if (ns > 0) {
+    // small g*r: split-K down-projection into fp32 partials, then the finish
+    // kernel (sum, deferred rstd, sigma), then the up-projection
+    float* part = cv.take<float>((size_t)ns * T * gr * 4);
+    float* ssp = cv.take<float>((size_t)ns * T * 4);
+    LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma_t<E>(A, gamma, Ap, D, gr, s));
+    lr::SplitDownArgs sa{};
+    sa.x = x; sa.Apt = Ap; sa.T = T; sa.d = D; sa.gr = gr; sa.nsplit = ns; sa.partial = part; sa.sumsq = ssp;
+    {
+      const int BK = lr::gemm_bk<E>();
+      sa.ksplit = (((D + BK - 1) / BK + ns - 1) / ns) * BK;
+    }
+    LR_LAUNCH("down", s, lr::launch_down_split<E>(sa, s));
+    LR_LAUNCH("finish", s, lr::launch_finish<E>(part, ssp, h_save, z, T, r, g, d->act, inv_width(d), d->eps, ns, s));
+  } else {
+    LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
+      lr::DownArgs da{};
+    da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_BLOCK;
+    da.invD = inv_width(d); da.eps = d->eps; da.h = h_save; da.z = z;
+    LR_LAUNCH("down", s, lr::launch_down<E>(da, s));
+  }
   lr::UpArgs ua{};
   const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
   ua.z = z_is_h ? h_save : z;
@@ -191,7 +217,7 @@ lr_status finish_impl(const lr_dims* d, const float* partial, const float* sumsq
   Carve cv{static_cast<char*>(ws)};
   cv.take<void>((size_t)D * gr * sizeof(E));  // same layout as the forward
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  LR_LAUNCH("finish", s, lr::launch_finish<E>(partial, sumsq, h_save, z, T, r, g, d->act, inv_width(d), d->eps, s));
+  LR_LAUNCH("finish", s, lr::launch_finish<E>(partial, sumsq, h_save, z, T, r, g, d->act, inv_width(d), d->eps, 1, s));
   lr::UpArgs ua{};
   const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
   ua.z = z_is_h ? h_save : z;

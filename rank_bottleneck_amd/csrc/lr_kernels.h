@@ -23,6 +23,16 @@ struct DownArgs {
   float* sumsq;       // DOWN_PARTIAL: [T]
 };
 
+// Small-rank forward: split-K down-projection into fp32 partials.
+struct SplitDownArgs {
+  const void* x;      // [T, d]
+  const void* Apt;    // [g*r, d]: (diag(gamma) A)^T, K-contiguous
+  int T, d, gr;
+  int nsplit, ksplit; // token-independent split of K = d (ksplit a multiple of the k step)
+  float* partial;     // [nsplit][T][g*r]
+  float* sumsq;       // [nsplit][T]
+};
+
 struct UpArgs {
   const void* z;      // A operand source; branch i starts at column i*r
   int64_t ldz;
@@ -84,8 +94,17 @@ template <typename E> hipError_t launch_down(const DownArgs& a, hipStream_t s);
 // whether launch_down picks its 64-row tiles for this shape (fewer 256 x 256 tiles than CUs)
 template <typename E> bool down_uses_skinny(int T, int r, int g, bool gateup);
 template <typename E> hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s);
+// h = rstd * sum of the nsplit partials, z = sigma(h); partial [nsplit][T][g*r], sumsq [nsplit][T]
 template <typename E> hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, int T,
-                                               int r, int g, int act, float invD, float eps, hipStream_t s);
+                                               int r, int g, int act, float invD, float eps, int nsplit,
+                                               hipStream_t s);
+// A'^T [n, d] = (diag(gamma) A)^T for A [d, n]
+template <typename E> hipError_t launch_fold_gamma_t(const void* A, const void* gamma, void* Apt, int d, int n,
+                                                     hipStream_t s);
+// Number of K splits of the small-rank forward path for this shape, 0 when the
+// regular down-projection is used.
+template <typename E> int small_rank_splits(int T, int d, int r, int g, int act);
+template <typename E> hipError_t launch_down_split(const SplitDownArgs& a, hipStream_t s);
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 // sums the split partials of launch_wgrad (nothing to do when nsplit == 1)

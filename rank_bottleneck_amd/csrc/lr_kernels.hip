@@ -83,32 +83,52 @@ __global__ __launch_bounds__(256) void k_fold_gamma(const E* __restrict__ A, con
   *reinterpret_cast<uint4*>(Ap + i) = q;
 }
 
+// A'^T [n, d]: one thread per output element, consecutive threads along d (the
+// reads of A are strided; the matrix is small next to x)
+template <typename E>
+__global__ __launch_bounds__(256) void k_fold_gamma_t(const E* __restrict__ A, const E* __restrict__ gamma,
+                                                      E* __restrict__ Apt, int d, int n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)d * n) return;
+  const int c = (int)(i / d), j = (int)(i % d);
+  Apt[i] = from_f32<E>(to_f32(A[(int64_t)j * n + c]) * to_f32(gamma[j]));
+}
+
 __global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
 }
 
 // seam: h = partial * rstd, z = sigma(h)
+// (the partials and sums of squares of nsplit K splits are added in split order)
 template <typename E>
 __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partial, const float* __restrict__ sumsq,
                                                 E* __restrict__ h, E* __restrict__ z, int T, int r, int g,
-                                                int act, float invD, float eps) {
+                                                int act, float invD, float eps, int nsplit) {
   const int gr = g * r;
   const int ncols = (act == ACT_SWIGLU) ? r : gr;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)T * ncols) return;
   const int t = (int)(i / ncols), c = (int)(i % ncols);
-  const float rs = 1.0f / sqrtf(sumsq[t] * invD + eps);
+  const int64_t pstride = (int64_t)T * gr;
+  float ss = 0.f;
+  for (int k = 0; k < nsplit; ++k) ss += sumsq[(int64_t)k * T + t];
+  const float rs = 1.0f / sqrtf(ss * invD + eps);
   const float* pr = partial + (int64_t)t * gr;
+  auto col = [&](int cc) {
+    float v = 0.f;
+    for (int k = 0; k < nsplit; ++k) v += pr[k * pstride + cc];
+    return v;
+  };
   if (act == ACT_SWIGLU) {
-    const float hg = pr[c] * rs, hu = pr[r + c] * rs;
+    const float hg = col(c) * rs, hu = col(r + c) * rs;
     if (h) {
       h[(int64_t)t * gr + c] = from_f32<E>(hg);
       h[(int64_t)t * gr + r + c] = from_f32<E>(hu);
     }
     z[(int64_t)t * r + c] = from_f32<E>(hg * sigmoidf_(hg) * hu);
   } else {
-    const float hv = pr[c] * rs;
+    const float hv = col(c) * rs;
     if (h) h[(int64_t)t * gr + c] = from_f32<E>(hv);
     if (act == ACT_SILU) z[(int64_t)t * gr + c] = from_f32<E>(hv * sigmoidf_(hv));
     else if (!h) z[(int64_t)t * gr + c] = from_f32<E>(hv);
@@ -219,6 +239,48 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
         }
       });
     }
+  }
+}
+
+// ------------------------------------------------------------------ small-rank down projection
+// acc = x . A' over the split's K range; fp32 partial rows of split `split` and
+// the split's partial sums of squares (column tile 0 writes them).
+template <class C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_down_split(
+    SplitDownArgs a) {
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  float* rowss = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);
+  const int tiles_m = (a.T + C::BM - 1) / C::BM, tiles_n = (a.gr + C::BN - 1) / C::BN;
+  const int per_split = tiles_m * tiles_n;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = logical / per_split;
+  int tm, tn;
+  grouped_tile<kGroupM>(logical % per_split, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int kbeg = split * a.ksplit;
+  const int klen = min(a.ksplit, a.d - kbeg);
+  Opnd oa{a.x, a.d, a.T, a.d};     // x [T, d]
+  Opnd ob{a.Apt, a.d, a.gr, a.d};  // A'^T: (n = c, k = j) at Apt[c*d + j]
+  f32x16 acc[C::MB][C::NB];
+  mainloop<C, false, false, true>(oa, ob, MapId{}, MapId{}, m0, n0, kbeg, klen > 0 ? klen : 0, lds, rowss, acc);
+
+  float* part = a.partial + (int64_t)split * a.T * a.gr;
+  if (tn == 0) {
+    for (int i = threadIdx.x; i < C::BM; i += C::THREADS)
+      if (m0 + i < a.T) a.sumsq[(int64_t)split * a.T + m0 + i] = rowss[i];
+  }
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  char LR_LDS* reg = stage_region<C>(lds);
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    stage_block<C>(acc, mb, reg);
+    const int rbase = m0 + wm * C::WTM + mb * 32;
+    sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+      const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+      if (row >= a.T || col >= a.gr) return;
+      const float4 v = lds_f4(rp + cl * 4);
+      store4(part + (int64_t)row * a.gr + col, v.x, v.y, v.z, v.w);
+    });
   }
 }
 
@@ -612,16 +674,26 @@ struct Cfgs<bf16> {
   // 64-row tiles for a down-projection whose 256 x 256 grid would leave CUs idle
   // (small g*r): four waves side by side over 256 columns
   using Skinny = PipeCfg<64, 256, 64, 1, 4, 2>;
+  // small-rank split-K down-projection: 256 rows by 64 or 128 columns, waves stacked in M
+  using N64 = PipeCfg<256, 64, 64, 4, 1, 2>;
+  using N128 = PipeCfg<256, 128, 64, 4, 1, 2>;
+  // short-K up-projection: 128 x 256 tiles, two work-groups per CU, so that one
+  // group's stores overlap the other's loads and MFMAs
+  using UpShort = PipeCfg<128, 256, 32, 2, 2, 2, 2>;
   static constexpr bool HAS_SKINNY = true;
 };
 template <>
 struct Cfgs<float> {
   using Main = TileCfg<float, 128, 128, 2, 2>;
   using Skinny = Main;
+  using N64 = Main;
+  using N128 = Main;
+  using UpShort = Main;
   static constexpr bool HAS_SKINNY = false;
 };
 
 constexpr int kNumCu = 256;
+constexpr int kUpShortK = 256;   // up-projections with K = r up to this use UpShort tiles
 
 // The skinny down tiles are used when the 256 x 256 grid has fewer tiles than CUs.
 template <typename E>
@@ -684,22 +756,69 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   return launch_down_cfg<C>(a, s);
 }
 
-template <typename E>
-hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s) {
-  using C = typename Cfgs<E>::Main;
-  if (a.T == 0) return hipSuccess;
+template <class C>
+hipError_t launch_up_cfg(const UpArgs& a, int n_up, hipStream_t s) {
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
   hipLaunchKernelGGL((k_up<C>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename E>
+hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if constexpr (Cfgs<E>::HAS_SKINNY) {
+    if (a.r <= kUpShortK) return launch_up_cfg<typename Cfgs<E>::UpShort>(a, n_up, s);
+  }
+  return launch_up_cfg<typename Cfgs<E>::Main>(a, n_up, s);
+}
+
+template <typename E>
+hipError_t launch_fold_gamma_t(const void* A, const void* gamma, void* Apt, int d, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_fold_gamma_t<E>, dim3(cdiv((int64_t)d * n, 256)), dim3(256), 0, s, static_cast<const E*>(A),
+                     static_cast<const E*>(gamma), static_cast<E*>(Apt), d, n);
+  return hipGetLastError();
+}
+
+// The split-K path serves g*r <= 256 when the regular down-projection would have
+// fewer 256 x 256 tiles than CUs; the splits bring the work-groups to about one
+// per CU, each split covering whole k steps.
+template <typename E>
+int small_rank_splits(int T, int d, int r, int g, int act) {
+  if (!Cfgs<E>::HAS_SKINNY || g * r > 256 || T <= 0) return 0;
+  if (!down_uses_skinny<E>(T, r, g, act == ACT_SWIGLU)) return 0;
+  using C = typename Cfgs<E>::Main;
+  const int tiles = cdiv(T, C::BM);
+  const int ksteps = cdiv(d, C::BK);
+  int ns = cdiv(kNumCu, tiles);
+  return ns < 1 ? 1 : (ns > ksteps ? ksteps : ns);
+}
+
+template <class C>
+hipError_t launch_down_split_cfg(const SplitDownArgs& a, hipStream_t s) {
+  const int tiles = cdiv(a.T, C::BM) * cdiv(a.gr, C::BN) * a.nsplit;
+  hipLaunchKernelGGL((k_down_split<C>), dim3(tiles), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_down_split(const SplitDownArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if constexpr (Cfgs<E>::HAS_SKINNY) {
+    if (a.gr <= 64) return launch_down_split_cfg<typename Cfgs<E>::N64>(a, s);
+    if (a.gr <= 128) return launch_down_split_cfg<typename Cfgs<E>::N128>(a, s);
+    return launch_down_split_cfg<typename Cfgs<E>::Main>(a, s);
+  } else {
+    return hipErrorInvalidValue;  // the fp32 path has no split-K down-projection
+  }
+}
+
+template <typename E>
 hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, int T, int r, int g, int act,
-                         float invD, float eps, hipStream_t s) {
+                         float invD, float eps, int nsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int ncols = act == ACT_SWIGLU ? r : g * r;
   hipLaunchKernelGGL(k_finish<E>, dim3(cdiv((int64_t)T * ncols, 256)), dim3(256), 0, s, partial, sumsq,
-                     static_cast<E*>(h), static_cast<E*>(z), T, r, g, act, invD, eps);
+                     static_cast<E*>(h), static_cast<E*>(z), T, r, g, act, invD, eps, nsplit);
   return hipGetLastError();
 }
 
@@ -799,8 +918,14 @@ template hipError_t launch_down<bf16>(const DownArgs&, hipStream_t);
 template hipError_t launch_down<float>(const DownArgs&, hipStream_t);
 template hipError_t launch_up<bf16>(const UpArgs&, int, hipStream_t);
 template hipError_t launch_up<float>(const UpArgs&, int, hipStream_t);
-template hipError_t launch_finish<bf16>(const float*, const float*, void*, void*, int, int, int, int, float, float, hipStream_t);
-template hipError_t launch_finish<float>(const float*, const float*, void*, void*, int, int, int, int, float, float, hipStream_t);
+template hipError_t launch_finish<bf16>(const float*, const float*, void*, void*, int, int, int, int, float, float, int, hipStream_t);
+template hipError_t launch_finish<float>(const float*, const float*, void*, void*, int, int, int, int, float, float, int, hipStream_t);
+template hipError_t launch_fold_gamma_t<bf16>(const void*, const void*, void*, int, int, hipStream_t);
+template hipError_t launch_fold_gamma_t<float>(const void*, const void*, void*, int, int, hipStream_t);
+template int small_rank_splits<bf16>(int, int, int, int, int);
+template int small_rank_splits<float>(int, int, int, int, int);
+template hipError_t launch_down_split<bf16>(const SplitDownArgs&, hipStream_t);
+template hipError_t launch_down_split<float>(const SplitDownArgs&, hipStream_t);
 template hipError_t launch_dz<bf16>(const DzArgs&, int, hipStream_t);
 template hipError_t launch_dz<float>(const DzArgs&, int, hipStream_t);
 template hipError_t launch_wgrad<bf16>(const WgradArgs&, hipStream_t);

@@ -48,6 +48,9 @@ SMALL = [
     Workload("bf16_swiglu", 777, 1024, 256, 2, "swiglu", "bf16"),
     Workload("bf16_g1_r64", 1000, 512, 64, 1, "silu", "bf16"),
     Workload("bf16_dnorm", 333, 384, 128, 2, "silu", "bf16", d_norm=1536),
+    # g*r <= 256 with few row tiles: the split-K small-rank forward
+    Workload("bf16_swiglu_r64", 640, 256, 64, 2, "swiglu", "bf16"),
+    Workload("bf16_identity_r128", 513, 320, 128, 1, "identity", "bf16"),
 ]
 
 
@@ -107,7 +110,7 @@ def test_backward_256_tiles_ragged():
     assert_close(host(g["dB"][0]), rb_["dB"][0], wl.dtype, "dB0")
 
 
-@pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5]], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5], SMALL[8], SMALL[9]], ids=lambda w: w.name)
 def test_inference_forward_without_checkpoint(wl):
     inp = make_inputs(wl, seed=2, with_dy=False)
     _, _, y, h = _run_fwd(wl, inp, save_h=False)
