@@ -83,15 +83,25 @@ __global__ __launch_bounds__(256) void k_fold_gamma(const E* __restrict__ A, con
   *reinterpret_cast<uint4*>(Ap + i) = q;
 }
 
-// A'^T [n, d]: one thread per output element, consecutive threads along d (the
-// reads of A are strided; the matrix is small next to x)
+// A'^T [n, d] through 64 x 16 blocks (64 rows of A, 16 of its columns) in LDS:
+// the rows of A'^T are written with consecutive threads on consecutive elements
+// (d is a multiple of 64, n of 16)
 template <typename E>
 __global__ __launch_bounds__(256) void k_fold_gamma_t(const E* __restrict__ A, const E* __restrict__ gamma,
                                                       E* __restrict__ Apt, int d, int n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)d * n) return;
-  const int c = (int)(i / d), j = (int)(i % d);
-  Apt[i] = from_f32<E>(to_f32(A[(int64_t)j * n + c]) * to_f32(gamma[j]));
+  __shared__ float tile[64][17];
+  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 16;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = threadIdx.x + k * 256, jj = e / 16, cc = e % 16;
+    tile[jj][cc] = to_f32(A[(int64_t)(j0 + jj) * n + c0 + cc]) * to_f32(gamma[j0 + jj]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = threadIdx.x + k * 256, cc = e / 64, jj = e % 64;
+    Apt[(int64_t)(c0 + cc) * d + j0 + jj] = from_f32<E>(tile[jj][cc]);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t n) {
@@ -100,38 +110,47 @@ __global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t
 }
 
 // seam: h = partial * rstd, z = sigma(h)
-// (the partials and sums of squares of nsplit K splits are added in split order)
+// (the partials and sums of squares of nsplit K splits are added in split order);
+// one thread per 4 consecutive output columns of a row
 template <typename E>
 __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partial, const float* __restrict__ sumsq,
                                                 E* __restrict__ h, E* __restrict__ z, int T, int r, int g,
                                                 int act, float invD, float eps, int nsplit) {
   const int gr = g * r;
   const int ncols = (act == ACT_SWIGLU) ? r : gr;
+  const int q4 = ncols / 4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)T * ncols) return;
-  const int t = (int)(i / ncols), c = (int)(i % ncols);
+  if (i >= (int64_t)T * q4) return;
+  const int t = (int)(i / q4), c = (int)(i % q4) * 4;
   const int64_t pstride = (int64_t)T * gr;
   float ss = 0.f;
   for (int k = 0; k < nsplit; ++k) ss += sumsq[(int64_t)k * T + t];
   const float rs = 1.0f / sqrtf(ss * invD + eps);
   const float* pr = partial + (int64_t)t * gr;
-  auto col = [&](int cc) {
-    float v = 0.f;
-    for (int k = 0; k < nsplit; ++k) v += pr[k * pstride + cc];
-    return v;
-  };
-  if (act == ACT_SWIGLU) {
-    const float hg = col(c) * rs, hu = col(r + c) * rs;
-    if (h) {
-      h[(int64_t)t * gr + c] = from_f32<E>(hg);
-      h[(int64_t)t * gr + r + c] = from_f32<E>(hu);
+  auto col4 = [&](int cc) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < nsplit; ++k) {
+      const float4 p = *reinterpret_cast<const float4*>(pr + k * pstride + cc);
+      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
     }
-    z[(int64_t)t * r + c] = from_f32<E>(hg * sigmoidf_(hg) * hu);
+    return make_float4(v.x * rs, v.y * rs, v.z * rs, v.w * rs);
+  };
+  const int64_t hrow = (int64_t)t * gr;
+  if (act == ACT_SWIGLU) {
+    const float4 g4 = col4(c), u4 = col4(r + c);
+    if (h) {
+      store4(h + hrow + c, g4.x, g4.y, g4.z, g4.w);
+      store4(h + hrow + r + c, u4.x, u4.y, u4.z, u4.w);
+    }
+    store4(z + (int64_t)t * r + c, g4.x * sigmoidf_(g4.x) * u4.x, g4.y * sigmoidf_(g4.y) * u4.y,
+           g4.z * sigmoidf_(g4.z) * u4.z, g4.w * sigmoidf_(g4.w) * u4.w);
   } else {
-    const float hv = col(c) * rs;
-    if (h) h[(int64_t)t * gr + c] = from_f32<E>(hv);
-    if (act == ACT_SILU) z[(int64_t)t * gr + c] = from_f32<E>(hv * sigmoidf_(hv));
-    else if (!h) z[(int64_t)t * gr + c] = from_f32<E>(hv);
+    const float4 v = col4(c);
+    if (h) store4(h + hrow + c, v.x, v.y, v.z, v.w);
+    if (act == ACT_SILU)
+      store4(z + hrow + c, v.x * sigmoidf_(v.x), v.y * sigmoidf_(v.y), v.z * sigmoidf_(v.z), v.w * sigmoidf_(v.w));
+    else if (!h)
+      store4(z + hrow + c, v.x, v.y, v.z, v.w);
   }
 }
 
@@ -675,8 +694,9 @@ struct Cfgs<bf16> {
   // (small g*r): four waves side by side over 256 columns
   using Skinny = PipeCfg<64, 256, 64, 1, 4, 2>;
   // small-rank split-K down-projection: 256 rows by 64 or 128 columns, waves stacked in M
-  using N64 = PipeCfg<256, 64, 64, 4, 1, 2>;
-  using N128 = PipeCfg<256, 128, 64, 4, 1, 2>;
+  using N64 = PipeCfg<256, 64, 64, 4, 1, 3>;
+  using N128 = PipeCfg<256, 128, 32, 4, 1, 4>;
+  using N256 = PipeCfg<256, 256, 32, 2, 2, 4>;
   // short-K up-projection: 128 x 256 tiles, two work-groups per CU, so that one
   // group's stores overlap the other's loads and MFMAs
   using UpShort = PipeCfg<128, 256, 32, 2, 2, 2, 2>;
@@ -688,6 +708,7 @@ struct Cfgs<float> {
   using Skinny = Main;
   using N64 = Main;
   using N128 = Main;
+  using N256 = Main;
   using UpShort = Main;
   static constexpr bool HAS_SKINNY = false;
 };
@@ -774,7 +795,7 @@ hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s) {
 
 template <typename E>
 hipError_t launch_fold_gamma_t(const void* A, const void* gamma, void* Apt, int d, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_fold_gamma_t<E>, dim3(cdiv((int64_t)d * n, 256)), dim3(256), 0, s, static_cast<const E*>(A),
+  hipLaunchKernelGGL(k_fold_gamma_t<E>, dim3(d / 64, n / 16), dim3(256), 0, s, static_cast<const E*>(A),
                      static_cast<const E*>(gamma), static_cast<E*>(Apt), d, n);
   return hipGetLastError();
 }
@@ -806,7 +827,7 @@ hipError_t launch_down_split(const SplitDownArgs& a, hipStream_t s) {
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (a.gr <= 64) return launch_down_split_cfg<typename Cfgs<E>::N64>(a, s);
     if (a.gr <= 128) return launch_down_split_cfg<typename Cfgs<E>::N128>(a, s);
-    return launch_down_split_cfg<typename Cfgs<E>::Main>(a, s);
+    return launch_down_split_cfg<typename Cfgs<E>::N256>(a, s);
   } else {
     return hipErrorInvalidValue;  // the fp32 path has no split-K down-projection
   }
@@ -817,7 +838,7 @@ hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void
                          float invD, float eps, int nsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int ncols = act == ACT_SWIGLU ? r : g * r;
-  hipLaunchKernelGGL(k_finish<E>, dim3(cdiv((int64_t)T * ncols, 256)), dim3(256), 0, s, partial, sumsq,
+  hipLaunchKernelGGL(k_finish<E>, dim3(cdiv((int64_t)T * (ncols / 4), 256)), dim3(256), 0, s, partial, sumsq,
                      static_cast<E*>(h), static_cast<E*>(z), T, r, g, act, invD, eps, nsplit);
   return hipGetLastError();
 }
