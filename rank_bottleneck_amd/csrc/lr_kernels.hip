@@ -43,8 +43,19 @@ __global__ __launch_bounds__(256) void k_rms_stats(const E* __restrict__ x, cons
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
   const E* xr = x + (int64_t)row * d;
+  // U independent 16-byte loads in flight per lane before any arithmetic
+  constexpr int U = 8;
   float s = 0.f;
-  for (int j = lane * VEC; j < d; j += 64 * VEC) s += sumsq_vec(*reinterpret_cast<const uint4*>(xr + j), (E*)nullptr);
+  for (int j0 = lane * VEC; j0 < d; j0 += 64 * VEC * U) {
+    uint4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 64 * VEC;
+      q[u] = j < d ? *reinterpret_cast<const uint4*>(xr + j) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += sumsq_vec(q[u], (E*)nullptr);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   const float rs = 1.0f / sqrtf(s * invD + eps);
@@ -574,9 +585,19 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
   const bool active = i < nB + nA;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (active) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float4 p = *reinterpret_cast<const float4*>(a.wpart + (int64_t)s * a.part_stride + i);
-      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    // up to U partial loads in flight, then added in split order
+    constexpr int U = 8;
+    for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+      float4 p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        p[u] = s0 + u < a.nsplit ? *reinterpret_cast<const float4*>(a.wpart + (int64_t)(s0 + u) * a.part_stride + i)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u >= a.nsplit) break;
+        acc.x += p[u].x; acc.y += p[u].y; acc.z += p[u].z; acc.w += p[u].w;
+      }
     }
   }
   if (active && i < nB) {
