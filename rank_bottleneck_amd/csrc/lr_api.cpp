@@ -67,8 +67,8 @@ size_t bwd_ws_t(const lr_dims* d) {
   const size_t es = sizeof(E), gr = (size_t)(d->g * d->r), T = (size_t)d->T;
   const int nsp = n_up_of(d) * lr::dz_nparts<E>((int)d->r);
   const int ngp = lr::wgrad_nparts<E>((int)gr);
-  const int ns = lr::wgrad_splits<E>((int)d->T, (int)d->d, (int)d->r, (int)d->g, n_up_of(d));
-  const size_t part = ns > 1 ? (size_t)ns * ((size_t)n_up_of(d) * d->r * d->d + (size_t)d->d * gr) * 4 : 0;
+  const lr::WgradPlan wp = lr::wgrad_plan<E>((int)d->T, (int)d->d, (int)d->r, (int)d->g, n_up_of(d));
+  const size_t part = (size_t)wp.part_floats * 4;
   return align_up(T * 4) + align_up(T * gr * es) * 2 + align_up(T * nsp * 4) + align_up((size_t)d->d * ngp * 4) +
          align_up(part);
 }
@@ -161,9 +161,11 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
   float* spart = cv.take<float>((size_t)T * nsp * 4);
   float* gpart = cv.take<float>((size_t)D * ngp * 4);
-  const int ns = lr::wgrad_splits<E>(T, D, r, g, n_up);
+  const lr::WgradPlan wp = lr::wgrad_plan<E>(T, D, r, g, n_up);
+  const int ns = wp.nsplit;
+  const bool reduced = wp.streamk || ns > 1;
   const int64_t pstride = (int64_t)n_up * r * D + (int64_t)D * gr;
-  float* wpart = cv.take<float>(ns > 1 ? (size_t)ns * pstride * 4 : 0);
+  float* wpart = cv.take<float>((size_t)wp.part_floats * 4);
 
   LR_LAUNCH("rms_stats", s, lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd, T, D, inv_width(d), d->eps, s));
 
@@ -180,14 +182,16 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   wa.x = x; wa.dh = dh; wa.A = A; wa.gamma = gamma; wa.dA = dA; wa.gpart = gpart; wa.ngpart = ngp;
   wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
   wa.nsplit = ns; wa.wpart = wpart; wa.part_stride = pstride; wa.part_offA = (int64_t)n_up * r * D;
+  wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
+  wa.sk_maxseg = wp.maxseg;
   {
     const int BK = lr::gemm_bk<E>();   // split lengths are whole k steps
     const int ksteps = (T + BK - 1) / BK;
     wa.ksplit = ((ksteps + ns - 1) / ns) * BK;
   }
   LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
-  if (ns > 1) LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
-  LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, ns), ngp, s));
+  if (reduced) LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
+  LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, reduced), ngp, s));
 
   lr::DxArgs xa{};
   xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp;

@@ -67,9 +67,21 @@ struct WgradArgs {
   int ngpart;
   int T, d, r, g, n_up;
   int nsplit, ksplit;       // token splits and tokens per split (a multiple of the k step)
-  float* wpart;             // nsplit x part_stride fp32 partial tiles (nsplit > 1)
+  float* wpart;             // nsplit x part_stride fp32 partial tiles (nsplit > 1), or the stream-K slots
   int64_t part_stride;      // n_up*r*d + d*g*r
   int64_t part_offA;        // n_up*r*d
+  // stream-K (streamk != 0): G work-groups split tiles*KS k steps evenly, the first R
+  // taking Q+1 and the rest Q; each (tile, covering work-group) writes a BM x BN
+  // fp32 slot at wpart[(tile*maxseg + ordinal) * BM*BN]
+  int streamk, sk_G, sk_Q, sk_R, sk_KS, sk_maxseg;
+};
+
+// How the token-reduced weight gradients are split.
+struct WgradPlan {
+  int streamk;        // 1: stream-K over (tile, k step); 0: nsplit equal token splits
+  int nsplit;         // token splits when !streamk (1 = one pass, no reduction)
+  int G, Q, R, KS, maxseg, tiles;
+  int64_t part_floats;  // fp32 partial floats the plan needs in the workspace
 };
 
 struct DxArgs {
@@ -114,7 +126,7 @@ hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, i
 template <typename E> int dz_nparts(int r);
 template <typename E> int wgrad_nparts(int gr);
 template <typename E> int gemm_bk();
-template <typename E> int wgrad_nparts_used(int gr, int nsplit);
-template <typename E> int wgrad_splits(int T, int d, int r, int g, int n_up);
+template <typename E> int wgrad_nparts_used(int gr, bool reduced);
+template <typename E> WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up);
 
 }  // namespace lr

@@ -624,6 +624,144 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
   if (active && (threadIdx.x & 15) == 0) a.gpart[(int64_t)row * a.ngpart + col / 64] = s;
 }
 
+// Stream-K weight gradients.  Tiles are numbered job-major (dB_0 .. dB_{n_up-1},
+// dA), row-major within a job; work-group w covers the k steps [s_w, s_w + len_w)
+// of the concatenated (tile, k step) sequence and writes one fp32 slot per tile
+// it touches.  k_wgrad_sk_reduce sums each tile's slots in work-group order.
+__device__ __forceinline__ int sk_owner(int64_t q, int Q, int R) {
+  const int64_t big = (int64_t)R * (Q + 1);
+  return q < big ? (int)(q / (Q + 1)) : (int)(R + (q - big) / Q);
+}
+
+struct SkTile {
+  int job, tm, tn, M, N;
+};
+template <class C>
+__device__ __forceinline__ SkTile sk_tile(const WgradArgs& a, int t) {
+  const int gr = a.g * a.r;
+  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+  const int tnA = (gr + C::BN - 1) / C::BN;
+  SkTile s;
+  const int nB = a.n_up * tmB * tnB;
+  if (t < nB) {
+    s.job = t / (tmB * tnB);
+    const int w = t % (tmB * tnB);
+    s.tm = w / tnB; s.tn = w % tnB; s.M = a.r; s.N = a.d;
+  } else {
+    const int w = t - nB;
+    s.job = a.n_up; s.tm = w / tnA; s.tn = w % tnA; s.M = a.d; s.N = gr;
+  }
+  return s;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_wgrad_sk(
+    WgradArgs a) {
+  using E = typename C::E;
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  const int gr = a.g * a.r;
+  // No XCD renumbering: the hardware deals ids to the 8 XCDs in turn, and work-groups
+  // w, w+8, ... start at the same k offset within their tiles, so an XCD's L2 holds
+  // the same token rows for all of its tiles.
+  const int w = blockIdx.x;
+  const int64_t s0 = (int64_t)w * a.sk_Q + min(w, a.sk_R);
+  const int64_t s1 = s0 + a.sk_Q + (w < a.sk_R ? 1 : 0);
+  const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  for (int64_t cur = s0; cur < s1;) {
+    const int t = (int)(cur / a.sk_KS);
+    const int64_t tend = min(s1, (int64_t)(t + 1) * a.sk_KS);
+    const int kk0 = (int)(cur - (int64_t)t * a.sk_KS), kk1 = (int)(tend - (int64_t)t * a.sk_KS);
+    const int ord = w - sk_owner((int64_t)t * a.sk_KS, a.sk_Q, a.sk_R);
+    const SkTile st = sk_tile<C>(a, t);
+    const int m0 = st.tm * C::BM, n0 = st.tn * C::BN;
+    const int kbeg = kk0 * C::BK;
+    const int klen = min(kk1 * C::BK, a.T) - kbeg;
+    Opnd oa, ob;
+    if (st.job == a.n_up) {
+      oa = Opnd{a.x, a.d, a.d, a.T};   // x^T: (m = j, k = t) at x[t*d + j]
+      ob = Opnd{a.dh, gr, gr, a.T};    // dh': (n = c, k = t) at dh[t*gr + c]
+    } else {
+      oa = Opnd{static_cast<const E*>(a.z) + (int64_t)st.job * a.r, a.ldz, a.r, a.T};
+      ob = Opnd{a.dy[st.job], a.d, a.d, a.T};
+    }
+    __syncthreads();   // the previous segment's epilogue is done with LDS
+    f32x16 acc[C::MB][C::NB];
+    mainloop<C, true, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, kbeg, klen > 0 ? klen : 0, lds, nullptr, acc);
+    float* slot = a.wpart + ((int64_t)t * a.sk_maxseg + ord) * (C::BM * C::BN);
+    char LR_LDS* reg = stage_region<C>(lds);
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      stage_block<C>(acc, mb, reg);
+      const int rl0 = wm * C::WTM + mb * 32;
+      sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+        const int lr_ = rl0 + rl, lc = wn * C::WTN + cl;
+        if (m0 + lr_ >= st.M || n0 + lc >= st.N) return;
+        const float4 v = lds_f4(rp + cl * 4);
+        store4(slot + (int64_t)lr_ * C::BN + lc, v.x, v.y, v.z, v.w);
+      });
+    }
+    cur = tend;
+  }
+}
+
+// Sum of each tile's stream-K slots in work-group order; one thread per 4
+// consecutive outputs, the dB tensors (job-major) first, then dA, which also gets
+// gamma_j and the row partial sum_c A_jc M_jc (one partial per 64-column group).
+template <class C>
+__global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
+  using E = typename C::E;
+  const int gr = a.g * a.r;
+  const int64_t nB = (int64_t)a.n_up * a.r * a.d, nA = (int64_t)a.d * gr;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const bool active = i < nB + nA;
+  int job = 0, row = 0, col = 0;
+  if (active) {
+    if (i < nB) {
+      job = (int)(i / ((int64_t)a.r * a.d));
+      const int64_t k = i % ((int64_t)a.r * a.d);
+      row = (int)(k / a.d); col = (int)(k % a.d);
+    } else {
+      job = a.n_up;
+      const int64_t k = i - nB;
+      row = (int)(k / gr); col = (int)(k % gr);
+    }
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (active) {
+    const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+    const int tnA = (gr + C::BN - 1) / C::BN;
+    const int tm = row / C::BM, tn = col / C::BN;
+    const int t = job < a.n_up ? job * tmB * tnB + tm * tnB + tn : a.n_up * tmB * tnB + tm * tnA + tn;
+    const int first = sk_owner((int64_t)t * a.sk_KS, a.sk_Q, a.sk_R);
+    const int last = sk_owner((int64_t)(t + 1) * a.sk_KS - 1, a.sk_Q, a.sk_R);
+    const float* slot = a.wpart + (int64_t)t * a.sk_maxseg * (C::BM * C::BN) +
+                        (int64_t)(row - tm * C::BM) * C::BN + (col - tn * C::BN);
+    for (int j = 0; j <= last - first; ++j) {
+      const float4 p = *reinterpret_cast<const float4*>(slot + (int64_t)j * (C::BM * C::BN));
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+  }
+  if (active && job < a.n_up) {
+    *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.d + col) = acc;
+    return;
+  }
+  float s = 0.f;
+  if (active) {
+    const E* Aw = static_cast<const E*>(a.A);
+    const float gj = to_f32(static_cast<const E*>(a.gamma)[row]);
+    const float4 a4 = load4(Aw + (int64_t)row * gr + col);
+    s = a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
+    *reinterpret_cast<float4*>(a.dA + (int64_t)row * gr + col) =
+        make_float4(gj * acc.x, gj * acc.y, gj * acc.z, gj * acc.w);
+  }
+  // 16 threads share one 64-column group of a row (gr is a multiple of 64)
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 8);
+  if (active && (threadIdx.x & 15) == 0) a.gpart[(int64_t)row * a.ngpart + col / 64] = s;
+}
+
 // ------------------------------------------------------------------ backward: dx
 // acc = dh' . A^T over K = g*r.  Row-sweep epilogue: dx = gamma*acc - x*rstd*S'/D,
 // with S' summed from the dz partials.  x rows of block mb+1 are loaded while
@@ -877,12 +1015,12 @@ template int gemm_bk<bf16>();
 template int gemm_bk<float>();
 
 template <typename E>
-int wgrad_nparts_used(int gr, int nsplit) {
+int wgrad_nparts_used(int gr, bool reduced) {
   using C = typename Cfgs<E>::Main;
-  return nsplit > 1 ? gr / 64 : cdiv(gr, C::BN) * C::WN;
+  return reduced ? gr / 64 : cdiv(gr, C::BN) * C::WN;
 }
-template int wgrad_nparts_used<bf16>(int, int);
-template int wgrad_nparts_used<float>(int, int);
+template int wgrad_nparts_used<bf16>(int, bool);
+template int wgrad_nparts_used<float>(int, bool);
 
 template <typename E>
 int wgrad_nparts(int gr) {
@@ -907,15 +1045,40 @@ hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
 }
 
 template <typename E>
-int wgrad_splits(int T, int d, int r, int g, int n_up) {
+WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
   using C = typename Cfgs<E>::Main;
   const int gr = g * r;
-  const int tiles = n_up * cdiv(r, C::BM) * cdiv(d, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
-  // aim for at least two waves of work-groups on 256 CUs, with >= 16 k steps per split
-  const int ksteps = cdiv(T, C::BK);
-  int s = 1;
-  while (tiles * s < 512 && ksteps / (2 * s) >= 16 && s < 16) s *= 2;
-  return s;
+  WgradPlan p{};
+  p.tiles = n_up * cdiv(r, C::BM) * cdiv(d, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
+  p.KS = cdiv(T, C::BK);
+  const int64_t total = (int64_t)p.tiles * p.KS;
+  p.nsplit = 1;
+  if (Cfgs<E>::HAS_SKINNY && p.tiles < kNumCu && total >= 2 * kNumCu) {
+    // stream-K: about one work-group per CU, at least 8 k steps each
+    p.streamk = 1;
+    p.G = (int)(total / 8 < kNumCu ? total / 8 : kNumCu);
+    p.Q = (int)(total / p.G);
+    p.R = (int)(total % p.G);
+    p.maxseg = 0;
+    for (int t = 0; t < p.tiles; ++t) {
+      const int64_t q0 = (int64_t)t * p.KS, q1 = q0 + p.KS - 1;
+      auto owner = [&](int64_t q) {
+        const int64_t big = (int64_t)p.R * (p.Q + 1);
+        return q < big ? (int)(q / (p.Q + 1)) : (int)(p.R + (q - big) / p.Q);
+      };
+      const int n = owner(q1) - owner(q0) + 1;
+      p.maxseg = n > p.maxseg ? n : p.maxseg;
+    }
+    p.part_floats = (int64_t)p.tiles * p.maxseg * C::BM * C::BN;
+    return p;
+  }
+  // token splits: aim for at least two waves of work-groups on 256 CUs, with
+  // >= 16 k steps per split
+  int sp = 1;
+  while (p.tiles * sp < 2 * kNumCu && p.KS / (2 * sp) >= 16 && sp < 16) sp *= 2;
+  p.nsplit = sp;
+  p.part_floats = sp > 1 ? (int64_t)sp * ((int64_t)n_up * r * d + (int64_t)d * gr) : 0;
+  return p;
 }
 
 template <typename E>
@@ -925,14 +1088,26 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   const int tilesB = cdiv(a.r, C::BM) * cdiv(a.d, C::BN);
   const int tilesA = cdiv(a.d, C::BM) * cdiv(gr, C::BN);
   const int total = (a.n_up * tilesB + tilesA) * a.nsplit;
+  if constexpr (Cfgs<E>::HAS_SKINNY) {
+    if (a.streamk) {
+      hipLaunchKernelGGL((k_wgrad_sk<C>), dim3(a.sk_G), dim3(C::THREADS), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((k_wgrad<C>), dim3(total), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename E>
 hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
-  if (a.nsplit == 1) return hipSuccess;
   const int64_t n4 = ((int64_t)a.n_up * a.r * a.d + (int64_t)a.d * a.g * a.r) / 4;
+  if constexpr (Cfgs<E>::HAS_SKINNY) {
+    if (a.streamk) {
+      hipLaunchKernelGGL((k_wgrad_sk_reduce<typename Cfgs<E>::Main>), dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.nsplit == 1) return hipSuccess;
   hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -980,7 +1155,7 @@ template int dz_nparts<bf16>(int);
 template int dz_nparts<float>(int);
 template int wgrad_nparts<bf16>(int);
 template int wgrad_nparts<float>(int);
-template int wgrad_splits<bf16>(int, int, int, int, int);
-template int wgrad_splits<float>(int, int, int, int, int);
+template WgradPlan wgrad_plan<bf16>(int, int, int, int, int);
+template WgradPlan wgrad_plan<float>(int, int, int, int, int);
 
 }  // namespace lr
