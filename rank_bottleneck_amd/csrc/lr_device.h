@@ -512,14 +512,18 @@ __device__ __forceinline__ bool row_sum_lane() {
   return (threadIdx.x & (LPR - 1)) == LPR - 1;
 }
 
-// 4 consecutive values -> memory (8 bytes of bf16 / 16 bytes of fp32)
+// 4 consecutive values -> memory (8 bytes of bf16 / 16 bytes of fp32), as
+// nontemporal stores: every CU writes its output tiles at about the same time,
+// and streaming them out measured 1-5% faster per kernel than write-back stores
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  *reinterpret_cast<bf16x4*>(p) = v;
+  const bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, v), reinterpret_cast<unsigned long long*>(p));
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
 }
 __device__ __forceinline__ float4 load4(const bf16* p) {
   const uint2 u = *reinterpret_cast<const uint2*>(p);
