@@ -105,13 +105,14 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     log(f"cpu oracle: probe {probe} rows {tp:.2f}s -> sample {rows} rows")
     t = run(rows)
     sub = wl.replace(T=rows)
-    if wl.fwd_only:
+    if wl.fwd_only and wl.hbm_metric:
         return {"value": sub.fwd_bytes() / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy forward, {t:.1f} s",
                 "tokens_per_s": rows / t}
-    flops = sub.fwd_flops() + (0 if wl.seam else sub.bwd_flops())
+    flops = sub.fwd_flops() + (0 if (wl.seam or wl.fwd_only) else sub.bwd_flops())
+    step = "forward" if (wl.seam or wl.fwd_only) else "fwd+bwd"
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy fwd+bwd, {t:.1f} s",
+            "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy {step}, {t:.1f} s",
             "tokens_per_s": rows / t}
 
 
@@ -241,8 +242,10 @@ def main():
             roof["traffic"] = rec["bytes_per_launch"]
 
     metric, value, unit = METRIC, tflops, "TFLOP/s"
-    if wl.fwd_only:
+    if wl.fwd_only and wl.hbm_metric:
         metric, value, unit = METRIC_FWD, wl.fwd_bytes() / (ms_step * 1e-3) / 1e9, "GB/s"
+    elif wl.fwd_only:
+        metric = "low-rank block forward TFLOP/s (bf16)"
     out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",

@@ -244,7 +244,7 @@ def test_status_on_bad_call_launches_nothing():
 
 
 # ------------------------------------------------------------------ full-size shapes
-FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r256"]
+FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r256", "vanilla_tp_shard"]
 
 
 def _sample_rows(T, n=192, seed=0):

@@ -43,7 +43,8 @@ class Workload:
     d_norm: int = 0       # 0 -> d ; the unsharded width for a tensor-parallel shard
     d_weight: int = 0     # width used for A's init variance; 0 -> d
     seam: bool = False    # run through the shard seam (partial + finish) instead of the fused block
-    fwd_only: bool = False  # benchmarked as a forward pass (HBM-bound small-rank sweep)
+    fwd_only: bool = False  # benchmarked as a forward pass
+    hbm_metric: bool = False  # reported as forward HBM GB/s (memory-bound sweep) instead of TFLOP/s
     note: str = ""
 
     @property
@@ -90,7 +91,13 @@ WORKLOADS: Dict[str, Workload] = {
 # memory-bound small-rank sweep (forward)
 for _r in (64, 128, 256):
     WORKLOADS[f"small_r{_r}"] = Workload(f"small_r{_r}", T=16384, d=4096, r=_r, g=1, act="silu",
-                                         dtype="bf16", fwd_only=True)
+                                         dtype="bf16", fwd_only=True, hbm_metric=True)
+# contrast to btp_shard: the same d=8192, r=2048 block under vanilla low-rank TP=4
+WORKLOADS["vanilla_tp_shard"] = Workload(
+    "vanilla_tp_shard", T=8192, d=8192, r=512, g=1, act="silu", dtype="bf16", fwd_only=True,
+    note="one of four vanilla tensor-parallel shards of the d=8192, r=2048 block: A column slice [8192, 512], "
+         "B row slice [512, 8192]; y is a [T, d] partial (the all-reduce payload). Same FLOPs as btp_shard, "
+         "but the up-projection's K is r/4 = 512")
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
