@@ -106,7 +106,6 @@ template <typename E_, int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
   using E = E_;
   static constexpr bool PIPE = false;
-  static constexpr bool REGS = false;
   static constexpr int WPE = 1;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
@@ -378,23 +377,6 @@ __device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles
   tm = first_m + w % gsz;
   tn = w / gsz;
 }
-
-// Output position of this lane's accumulators.  The MFMA's first operand is the
-// B tile (so the 32x32 accumulator's "row" runs over N): block (mb, nb) of lane l
-// holds output row  m0 + wm*WTM + mb*32 + l%32  and, in registers 4q..4q+3, the
-// four consecutive output columns  n0 + wn*WTN + nb*32 + 8q + 4*(l/32) + 0..3.
-template <class C>
-struct FragPos {
-  int row0, col0, lane;
-  __device__ __forceinline__ FragPos(int m0, int n0) {
-    const int tid = threadIdx.x, wave = tid >> 6;
-    lane = tid & 63;
-    row0 = m0 + (wave / C::WN) * C::WTM + (lane & 31);
-    col0 = n0 + (wave % C::WN) * C::WTN + 4 * (lane >> 5);
-  }
-  __device__ __forceinline__ int row(int mb) const { return row0 + mb * 32; }
-  __device__ __forceinline__ int col(int nb, int q) const { return col0 + nb * 32 + 8 * q; }
-};
 
 #define LR_LDS __attribute__((address_space(3)))
 

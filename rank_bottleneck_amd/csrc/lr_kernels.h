@@ -101,7 +101,6 @@ template <typename E> hipError_t launch_rms_stats(const void* x, const void* gam
                                                   float* rstd, int T, int d, float invD, float eps, hipStream_t s);
 template <typename E> hipError_t launch_fold_gamma(const void* A, const void* gamma, void* Ap, int d, int n,
                                                    hipStream_t s);
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 template <typename E> hipError_t launch_down(const DownArgs& a, hipStream_t s);
 // whether launch_down picks its 64-row tiles for this shape (fewer 256 x 256 tiles than CUs)
 template <typename E> bool down_uses_skinny(int T, int r, int g, bool gateup);

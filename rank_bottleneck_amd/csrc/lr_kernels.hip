@@ -115,11 +115,6 @@ __global__ __launch_bounds__(256) void k_fold_gamma_t(const E* __restrict__ A, c
   }
 }
 
-__global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0.f;
-}
-
 // seam: h = partial * rstd, z = sigma(h)
 // (the partials and sums of squares of nsplit K splits are added in split order);
 // one thread per 4 consecutive output columns of a row
@@ -903,12 +898,6 @@ hipError_t launch_fold_gamma(const void* A, const void* gamma, void* Ap, int d, 
   const int64_t total = (int64_t)d * n / VEC;
   hipLaunchKernelGGL(k_fold_gamma<E>, dim3(cdiv(total, 256)), dim3(256), 0, s, static_cast<const E*>(A),
                      static_cast<const E*>(gamma), static_cast<E*>(Ap), d, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_f32, dim3(cdiv(n, 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

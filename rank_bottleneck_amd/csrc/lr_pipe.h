@@ -33,13 +33,10 @@ namespace lr {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// REGS_: operand tiles travel global -> registers -> LDS (two LDS buffers,
-// one stage in registers) instead of by direct-to-LDS loads.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int WPE_ = 1, bool REGS_ = false>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int WPE_ = 1>
 struct PipeCfg {
   using E = bf16;
   static constexpr bool PIPE = true;
-  static constexpr bool REGS = REGS_;
   static constexpr int WPE = WPE_;  // waves per SIMD the kernels are built for
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr int VEC = 8;
@@ -55,8 +52,7 @@ struct PipeCfg {
   // LDS the epilogue uses
   static constexpr int SINK_BYTE = STAGES * STAGE_BYTES;
   static constexpr int SINK_BYTES = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
-  static constexpr int LDS_UINT4 = (STAGES * STAGE_BYTES + (REGS ? 0 : SINK_BYTES)) / 16;
-  static_assert(!REGS || STAGES == 2, "register staging uses two LDS buffers");
+  static constexpr int LDS_UINT4 = (STAGES * STAGE_BYTES + SINK_BYTES) / 16;
   static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "tile / wave mismatch");
   static_assert(BK % 16 == 0 && (BK * 2 == 64 || BK * 2 == 128), "BK must be 32 or 64");
   static_assert((STAGES - 1) * LPS <= 63, "vmcnt range");
@@ -387,147 +383,11 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
   __syncthreads();
 }
 
-
-// Register-staged mainloop (C::REGS): the same LDS image and fragment reads as
-// gemm_pipe, filled by ordinary buffer loads into registers and LDS stores.
-// Stage kt is read from LDS buffer kt%2 while its successor's registers are
-// stored into the other buffer (sub-steps 0 and 1) and the loads of stage kt+2
-// are issued (sub-step 2); one barrier per stage, at the start of the last
-// sub-step.  The compiler tracks every load, so pre() needs no accounting.
-template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB, class Pre>
-__device__ __forceinline__ void gemm_regs(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
-                                          int n0, int kbeg, int K, uint4* lds, float* rowss,
-                                          f32x16 (&acc)[C::MB][C::NB], Pre&& pre) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-  float ss[C::MB];
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) ss[mb] = 0.f;
-
-  DmaTile<C, C::BM, A_MNC> da;
-  DmaTile<C, C::BN, B_MNC> db;
-  da.init(oa, ma, m0, wave, lane);
-  db.init(ob, mbm, n0, wave, lane);
-  da.init_range(oa, m0, kbeg);
-  db.init_range(ob, n0, kbeg);
-  const char LR_LDS* ldsp = (const char LR_LDS*)(lds);
-  char LR_LDS* ldsw = (char LR_LDS*)(lds);
-  const int nk = (K + C::BK - 1) / C::BK;
-  constexpr int QA = DmaTile<C, C::BM, A_MNC>::Q, QB = DmaTile<C, C::BN, B_MNC>::Q, QT = QA + QB;
-  constexpr int NMF = C::MB * C::NB;
-  constexpr int NF = C::MB + C::NB;
-  static_assert(C::KS == 4 && QT % 2 == 0 && QT / 2 <= NMF && QT <= NMF, "register staging schedule");
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-  uint4 stg[QT];
-  auto gload_one = [&](int q, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb) {
-    if (q < QA)
-      stg[q] = buf_load16(rsa, da.off[q]);
-    else
-      stg[q] = buf_load16(rsb, db.off[q - QA]);
-  };
-  // LDS byte of staged vector q of this lane in buffer `buf` (the direct-load image)
-  auto lds_byte = [&](int q, int buf) {
-    const int part = q < QA ? 0 : C::A_BYTES, qq = q < QA ? q : q - QA;
-    return buf * C::STAGE_BYTES + part + (qq * C::NWAVES + wave) * 1024 + 16 * lane;
-  };
-  auto lwrite_one = [&](int q, int buf) {
-    *reinterpret_cast<u32x4 LR_LDS*>(ldsw + lds_byte(q, buf)) = __builtin_bit_cast(u32x4, stg[q]);
-  };
-  auto read_frags = [&](int st, int s, uint4 (&fa)[C::MB], uint4 (&fb)[C::NB]) {
-    const char LR_LDS* ta = ldsp + (st & 1) * C::STAGE_BYTES;
-    const char LR_LDS* tb = ta + C::A_BYTES;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) fa[mb] = frag<C, C::BM, A_MNC>(ta, wm * C::WTM + mb * 32, s, lane);
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, s, lane);
-  };
-
-  if (nk > 0) {
-    {
-      const __amdgpu_buffer_rsrc_t rsa = da.brsrc(0, true), rsb = db.brsrc(0, true);
-#pragma unroll
-      for (int q = 0; q < QT; ++q) gload_one(q, rsa, rsb);
-#pragma unroll
-      for (int q = 0; q < QT; ++q) lwrite_one(q, 0);
-      const __amdgpu_buffer_rsrc_t rsa1 = da.brsrc(1, 1 < nk), rsb1 = db.brsrc(1, 1 < nk);
-#pragma unroll
-      for (int q = 0; q < QT; ++q) gload_one(q, rsa1, rsb1);
-    }
-    __syncthreads();
-    uint4 a[2][C::MB], b[2][C::NB];
-    read_frags(0, 0, a[0], b[0]);
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool final_k = kt + 1 == nk;
-      if (final_k) pre();
-      const int nbuf = (kt + 1) & 1;
-      const __amdgpu_buffer_rsrc_t rsa = da.brsrc(kt + 2, kt + 2 < nk), rsb = db.brsrc(kt + 2, kt + 2 < nk);
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const int cur = s & 1, nxt = cur ^ 1;
-        const bool last = s + 1 == C::KS;
-        int fst = kt, fs = s + 1;
-        if (last) {
-          if (!final_k) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            block_barrier();
-          }
-          fst = kt + 1;   // past the end: reads nobody uses
-          fs = 0;
-        }
-        const char LR_LDS* fa = ldsp + (fst & 1) * C::STAGE_BYTES;
-        const char LR_LDS* fb = fa + C::A_BYTES;
-        if constexpr (ROWSTAT) {   // every wave (no branch); the wn == 0 waves publish
-#pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb) ss[mb] = frag_sumsq(a[cur][mb], ss[mb]);
-        }
-#pragma unroll
-        for (int i = 0; i < NMF; ++i) {
-          mfma_chunk(acc[i / C::NB][i % C::NB], b[cur][i % C::NB], a[cur][i / C::NB], (bf16*)nullptr);
-          if (i < NF) {
-            if (i < C::MB)
-              a[nxt][i] = frag<C, C::BM, A_MNC>(fa, wm * C::WTM + i * 32, fs, lane);
-            else
-              b[nxt][i - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (i - C::MB) * 32, fs, lane);
-          }
-          constexpr int WEVERY = NMF / (QT / 2), LEVERY = NMF / QT;
-          if (s < 2 && (i % WEVERY) == WEVERY - 1) lwrite_one(s * (QT / 2) + i / WEVERY, nbuf);
-          if (s == 2 && (i % LEVERY) == LEVERY - 1) gload_one(i / LEVERY, rsa, rsb);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-  } else {
-    pre();
-  }
-  if constexpr (ROWSTAT) {
-    static_assert(!A_MNC, "row statistics need a K-contiguous A");
-    __syncthreads();  // rowss may alias the buffers: every wave is past its last fragment read
-    if (wn == 0) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        const float v = ss[mb] + __shfl_xor(ss[mb], 32);
-        if (lane < 32) rowss[wm * C::WTM + mb * 32 + lane] = v;
-      }
-    }
-  }
-  __syncthreads();
-}
-
 template <class C, bool A_MNC, bool B_MNC, bool ROWSTAT, class MapA, class MapB, class Pre = NoPre>
 __device__ __forceinline__ void mainloop(const Opnd& oa, const Opnd& ob, const MapA& ma, const MapB& mbm, int m0,
                                          int n0, int kbeg, int K, uint4* lds, float* rowss,
                                          f32x16 (&acc)[C::MB][C::NB], Pre&& pre = Pre{}) {
-  if constexpr (C::PIPE && C::REGS) {
-    gemm_regs<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc, pre);
-  } else if constexpr (C::PIPE) {
+  if constexpr (C::PIPE) {
     gemm_pipe<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc, pre);
   } else {
     gemm_tile<C, A_MNC, B_MNC, ROWSTAT>(oa, ob, ma, mbm, m0, n0, kbeg, K, lds, rowss, acc);
