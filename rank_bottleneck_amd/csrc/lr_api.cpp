@@ -69,7 +69,8 @@ size_t bwd_ws_t(const lr_dims* d) {
   const int ngp = lr::wgrad_nparts<E>((int)gr);
   const lr::WgradPlan wp = lr::wgrad_plan<E>((int)d->T, (int)d->d, (int)d->r, (int)d->g, n_up_of(d));
   const size_t part = (size_t)wp.part_floats * 4;
-  return align_up(T * 4) + align_up(T * gr * es) * 2 + align_up(T * nsp * 4) + align_up((size_t)d->d * ngp * 4) +
+  return align_up(T * 4) + align_up(T * gr * es) * 2 + align_up(T * lr::spart_stride(nsp) * 4) +
+         align_up((size_t)d->d * ngp * 4) +
          align_up(part);
 }
 
@@ -159,7 +160,8 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   float* rstd = cv.take<float>((size_t)T * 4);
   void* dh = cv.take<void>((size_t)T * gr * sizeof(E));
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  float* spart = cv.take<float>((size_t)T * nsp * 4);
+  const int sps = lr::spart_stride(nsp);
+  float* spart = cv.take<float>((size_t)T * sps * 4);
   float* gpart = cv.take<float>((size_t)D * ngp * 4);
   const lr::WgradPlan wp = lr::wgrad_plan<E>(T, D, r, g, n_up);
   const int ns = wp.nsplit;
@@ -171,7 +173,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
 
   lr::DzArgs za{};
   for (int i = 0; i < n_up; ++i) { za.dy[i] = dy[i]; za.B[i] = B[i]; }
-  za.h = h; za.rstd = rstd; za.dh = dh; za.z = z; za.spart = spart; za.nspart = nsp;
+  za.h = h; za.rstd = rstd; za.dh = dh; za.z = z; za.spart = spart; za.spstride = sps;
   za.T = T; za.d = D; za.r = r; za.g = g; za.act = d->act;
   LR_LAUNCH("dz", s, lr::launch_dz<E>(za, n_up, s));
 
@@ -194,7 +196,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, reduced), ngp, s));
 
   lr::DxArgs xa{};
-  xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp;
+  xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp; xa.spstride = sps;
   xa.dx = dx; xa.T = T; xa.d = D; xa.r = r; xa.g = g; xa.invD = inv_width(d);
   LR_LAUNCH("dx", s, lr::launch_dx<E>(xa, s));
   return LR_OK;

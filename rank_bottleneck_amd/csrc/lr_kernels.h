@@ -48,8 +48,8 @@ struct DzArgs {
   const float* rstd;  // [T]
   void* dh;           // [T, g*r]   rstd * dh
   void* z;            // sigma(h): [T, g*r] (SiLU) or [T, r] (SwiGLU); unused for identity
-  float* spart;       // [T, nspart]
-  int nspart;
+  float* spart;       // [T, spstride]: partials of S' (columns past the partial count unused)
+  int spstride;
   int T, d, r, g, act;
 };
 
@@ -90,8 +90,8 @@ struct DxArgs {
   const void* x;
   const void* gamma;
   const float* rstd;
-  const float* spart;
-  int nspart;
+  const float* spart;  // [T, spstride], the first nspart columns of each row used
+  int nspart, spstride;
   void* dx;
   int T, d, r, g;
   float invD;
@@ -123,6 +123,8 @@ template <typename E> hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStre
 template <typename E> hipError_t launch_dx(const DxArgs& a, hipStream_t s);
 hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, int stride, hipStream_t s);
 template <typename E> int dz_nparts(int r);
+// row stride of the S' partials: the count rounded up to whole float4s
+inline int spart_stride(int nparts) { return (nparts + 3) & ~3; }
 template <typename E> int wgrad_nparts(int gr);
 template <typename E> int gemm_bk();
 template <typename E> int wgrad_nparts_used(int gr, bool reduced);

@@ -479,7 +479,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
         }
       }
       srow = row_sum<SW::LPR>(srow);
-      if (row < a.T && row_sum_lane<SW::LPR>()) a.spart[(int64_t)row * a.nspart + part] = srow;
+      if (row < a.T && row_sum_lane<SW::LPR>()) a.spart[(int64_t)row * a.spstride + part] = srow;
     }
   };
 #pragma unroll
@@ -757,6 +757,48 @@ __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
   if (active && (threadIdx.x & 15) == 0) a.gpart[(int64_t)row * a.ngpart + col / 64] = s;
 }
 
+// rstd * S' / D of a tile's rows, one row per thread.  The S' partials of the
+// row are issued as float4 loads at the start of the last k step and summed (in
+// column order) after the mainloop, so that no load is waited for inside it;
+// partials past the first 4*Q are read after the mainloop.
+template <class C>
+struct SprimeRows {
+  static constexpr int N = (C::BM + C::THREADS - 1) / C::THREADS;
+  static constexpr int Q = 8;
+  float4 q[N][Q];
+  float rs[N];
+  __device__ __forceinline__ void load(const DxArgs& a, int m0) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = threadIdx.x + j * C::THREADS, t = m0 + i;
+      const bool ok = i < C::BM && t < a.T;
+      rs[j] = ok ? a.rstd[t] * a.invD : 0.f;
+      const float4* p = reinterpret_cast<const float4*>(a.spart + (int64_t)(ok ? t : 0) * a.spstride);
+#pragma unroll
+      for (int k = 0; k < Q; ++k) q[j][k] = ok && 4 * k < a.nspart ? p[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void publish(const DxArgs& a, int m0, float* dst) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = threadIdx.x + j * C::THREADS, t = m0 + i;
+      if (i >= C::BM) continue;
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < Q; ++k) {
+        const int b = 4 * k;
+        sum += b < a.nspart ? q[j][k].x : 0.f;
+        sum += b + 1 < a.nspart ? q[j][k].y : 0.f;
+        sum += b + 2 < a.nspart ? q[j][k].z : 0.f;
+        sum += b + 3 < a.nspart ? q[j][k].w : 0.f;
+      }
+      if (t < a.T)
+        for (int k = 4 * Q; k < a.nspart; ++k) sum += a.spart[(int64_t)t * a.spstride + k];
+      dst[i] = t < a.T ? sum * rs[j] : 0.f;
+    }
+  }
+};
+
 // ------------------------------------------------------------------ backward: dx
 // acc = dh' . A^T over K = g*r.  Row-sweep epilogue: dx = gamma*acc - x*rstd*S'/D,
 // with S' summed from the dz partials.  x rows of block mb+1 are loaded while
@@ -791,16 +833,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
     }
   };
   typename R::T graw = R::zero();
-  RowVals<C> srv;
+  SprimeRows<C> srv;
   auto pre = [&]() {   // the row values first: they are needed first
-    srv.load([&](int i) {
-      const int t = m0 + i;
-      if (t >= a.T) return 0.f;
-      const float* p = a.spart + (int64_t)t * a.nspart;
-      float sum = 0.f;
-      for (int k = 0; k < a.nspart; ++k) sum += p[k];
-      return sum * a.rstd[t] * a.invD;
-    });
+    srv.load(a, m0);
     graw = cok ? R::load(static_cast<const E*>(a.gamma) + col) : R::zero();
     load_block(0, xin0);
   };
@@ -809,7 +844,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   Opnd ob{a.A, gr, a.d, gr};    // A^T: (n = j, k = c) at A[j*gr + c]
   f32x16 acc[C::MB][C::NB];
   mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc, pre);
-  srv.publish(srow);
+  srv.publish(a, m0, srow);
   __syncthreads();
 
   const float4 g4 = R::f4(graw);

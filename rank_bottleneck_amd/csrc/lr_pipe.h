@@ -29,7 +29,13 @@
 
 #include "lr_device.h"
 
+
 namespace lr {
+
+// sub-steps over which the refill of one stage is spread: loads issued later than
+// the first sub-step of the next stage are not back in time for the wait before
+// its last sub-step, and packing them denser stalls the MFMA issue
+constexpr int kRefillSubsteps = 2;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -280,11 +286,13 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
     // count of every k step the same.  pre() runs at the start of the last k step,
     // which has no wait and no barrier, so its loads overlap the last MFMAs.
     constexpr int QA = DmaTile<C, C::BM, A_MNC>::Q, QB = DmaTile<C, C::BN, B_MNC>::Q;
-    constexpr int HALF = (QA + QB) / 2;          // loads in the last sub-step; the rest in the first
-    constexpr int REST = QA + QB - HALF;
+    // the refill of a stage is cut into NS chunks: chunk 0 goes out in the last
+    // sub-step of stage kt, chunk u in sub-step u-1 of stage kt+1
+    constexpr int NS = kRefillSubsteps < C::KS ? kRefillSubsteps : C::KS;
+    constexpr int HALF = (QA + QB) / NS;         // loads of chunk 0 (issued in the prologue too)
     constexpr int NMF = C::MB * C::NB;
     constexpr int NF = C::MB + C::NB;
-    static_assert(C::KS >= 2, "the refill is split over the first and the last sub-step");
+    static_assert(C::KS >= 2 && NS >= 2, "the refill is split over at least two sub-steps");
     // ba / bb: LDS bases of the A and B parts (both the sink for stages past the end)
     auto issue_q = [&](int q, const Rsrc4& ra, const Rsrc4& rb, uint32_t ba, uint32_t bb) {
       if (q < QA)
@@ -313,7 +321,6 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
         const bool last = s + 1 == C::KS;
         Rsrc4 ra = pra, rb = prb;
         uint32_t ba = pba, bb = pbb;
-        int qbase = HALF;               // first sub-step: second half of the pending refill
         int fst = kt, fs = s + 1;       // source of the next fragments
         if (last) {
           if (!final_k) {
@@ -331,11 +338,12 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
           prb = rb;
           pba = ba;
           pbb = bb;
-          qbase = 0;
           fst = kt + 1;                 // past the end: reads nobody uses
           fs = 0;
         }
-        const bool loads_here = last || s == 0;
+        const bool loads_here = last || s < NS - 1;
+        const int u = last ? 0 : s + 1;  // refill chunk of this sub-step
+        const int qlo = u * (QA + QB) / NS, qn = (u + 1) * (QA + QB) / NS - qlo;
         const char LR_LDS* fa = ldsp + (fst % C::STAGES) * C::STAGE_BYTES;
         const char LR_LDS* fb = fa + C::A_BYTES;
         if constexpr (ROWSTAT) {   // every wave (no branch); the wn == 0 waves publish
@@ -345,19 +353,23 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
           mfma_chunk(acc[i / C::NB][i % C::NB], b[cur][i % C::NB], a[cur][i / C::NB], (bf16*)nullptr);
-          if (i < NF) {
-            if (i < C::MB)
-              a[nxt][i] = frag<C, C::BM, A_MNC>(fa, wm * C::WTM + i * 32, fs, lane);
+          // fragment reads after the even MFMAs and refill loads after the odd ones,
+          // where there are MFMAs enough for that (a slot with both stalls the MFMA pipe)
+          constexpr bool DISJ = NMF >= 2 * NF;
+          if (DISJ ? (i % 2 == 0 && i / 2 < NF) : (i < NF)) {
+            const int fi = DISJ ? i / 2 : i;
+            if (fi < C::MB)
+              a[nxt][fi] = frag<C, C::BM, A_MNC>(fa, wm * C::WTM + fi * 32, fs, lane);
             else
-              b[nxt][i - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (i - C::MB) * 32, fs, lane);
+              b[nxt][fi - C::MB] = frag<C, C::BN, B_MNC>(fb, wn * C::WTN + (fi - C::MB) * 32, fs, lane);
           }
           // the sub-step's n loads go out after MFMAs floor(j*NMF/n) + NMF/n - 1, spread evenly
           if (loads_here) {
-            const int n = last ? HALF : REST;
+            constexpr int QMAX = (QA + QB + NS - 1) / NS;
 #pragma unroll
-            for (int j = 0; j < (HALF > REST ? HALF : REST); ++j)
-              if (j < n && (j * NMF) / n + (NMF / n > 0 ? NMF / n : 1) - 1 == (i < NMF ? i : NMF - 1))
-                issue_q(qbase + j, ra, rb, ba, bb);
+            for (int j = 0; j < QMAX; ++j)
+              if (j < qn && (j * NMF) / qn + (NMF / qn > 0 ? NMF / qn : 1) - 1 == (i < NMF ? i : NMF - 1))
+                issue_q(qlo + j, ra, rb, ba, bb);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
