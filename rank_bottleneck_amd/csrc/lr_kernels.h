@@ -21,6 +21,7 @@ struct DownArgs {
   void* z;            // [T, g*r] (SwiGLU: [T, r]); identity: used only when h is null
   float* partial;     // DOWN_PARTIAL: [T, g*r]
   float* sumsq;       // DOWN_PARTIAL: [T]
+  int tile0;          // first tile of this launch (launch_down sets it)
 };
 
 // Small-rank forward: split-K down-projection into fp32 partials.
@@ -51,6 +52,7 @@ struct DzArgs {
   float* spart;       // [T, spstride]: partials of S' (columns past the partial count unused)
   int spstride;
   int T, d, r, g, act;
+  int tile0;          // first tile of this launch (launch_dz sets it)
 };
 
 struct WgradArgs {

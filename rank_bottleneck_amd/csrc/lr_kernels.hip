@@ -170,6 +170,34 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   out[i] = s;
 }
 
+// Work-group -> tile.  A grid of T/256 x N/256 tiles whose last round would
+// leave at least half of the CUs idle runs its full rounds as 256-row tiles and
+// each remaining tile as two 128-row halves (HALF), which fill the CUs once;
+// both in one launch, the halves' work-groups after the whole tiles'.  Work-group
+// bid of nblk (of its part) takes tile tile0 + i in the grid's order (per-XCD
+// ranges, groups of row panels), i its renumbered index; in the HALF part the
+// renumbered pairs (2i, 2i+1) take the two halves of tile tile0 + i.
+template <bool HALF>
+__device__ __forceinline__ void tail_index(int tile0, int bid, int nblk, int& t, int& piece) {
+  const int idx = xcd_remap(bid, nblk);
+  t = tile0 + (HALF ? idx / 2 : idx);
+  piece = HALF ? idx % 2 : 0;
+}
+// rows of tiles of the full grid: of 2*BM rows for HALF launches
+template <class C, bool HALF>
+__device__ __forceinline__ int tile_rows(int T) {
+  constexpr int ROWS = HALF ? 2 * C::BM : C::BM;
+  return (T + ROWS - 1) / ROWS;
+}
+template <class C, bool HALF>
+__device__ __forceinline__ void tail_tile(int tile0, int bid, int nblk, int T, int tiles_n, int& tm, int& tn,
+                                          int& m0) {
+  int t, piece;
+  tail_index<HALF>(tile0, bid, nblk, t, piece);
+  grouped_tile<kGroupM>(t, tile_rows<C, HALF>(T), tiles_n, tm, tn);
+  m0 = (tm * (HALF ? 2 : 1) + piece) * C::BM;
+}
+
 // LDS words a GEMM kernel needs: the mainloop ring or the epilogue staging,
 // whichever is larger, plus BM floats of per-row values.
 // LDS of a GEMM kernel: the mainloop's tiles, then (after the mainloop) the
@@ -187,18 +215,16 @@ struct KernLds {
 // ------------------------------------------------------------------ down projection
 // acc = x . A' over K = d; mode DOWN_BLOCK: h = rstd*acc, z = sigma(h);
 // mode DOWN_PARTIAL: fp32 partial = acc and sumsq (tile column 0 writes it).
-template <class C, bool GATEUP>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_down(DownArgs a) {
+template <class C, bool GATEUP, bool HALF>
+__device__ __forceinline__ void down_tile(const DownArgs& a, uint4* lds, int bid, int nblk, int tile0) {
   using E = typename C::E;
-  __shared__ uint4 lds[KernLds<C>::TOTAL];
   float* rowss = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);
   const int gr = a.g * a.r;
   constexpr int TN = GATEUP ? C::BN / 2 : C::BN;  // logical columns per tile
   const int tiles_n = ((GATEUP ? a.r : gr) + TN - 1) / TN;
-  const int tiles_m = (a.T + C::BM - 1) / C::BM;
-  int tm, tn;
-  grouped_tile<kGroupM>(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM, n0 = tn * TN;
+  int tm, tn, m0;
+  tail_tile<C, HALF>(tile0, bid, nblk, a.T, tiles_n, tm, tn, m0);
+  const int n0 = tn * TN;
 
   Opnd oa{a.x, a.d, a.T, a.d};
   Opnd ob{a.Ap, gr, gr, a.d};
@@ -265,6 +291,25 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
       });
     }
   }
+}
+
+template <class C, bool GATEUP>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_down(DownArgs a) {
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  down_tile<C, GATEUP, false>(a, lds, blockIdx.x, gridDim.x, 0);
+}
+// whole tiles 0 .. a.tile0-1 on the first a.tile0 work-groups, the halves of the
+// rest on the others
+template <class C, class H, bool GATEUP>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_down_tail(
+    DownArgs a) {
+  static_assert(C::THREADS == H::THREADS && C::WPE == H::WPE, "one launch shape");
+  constexpr int N = KernLds<C>::TOTAL > KernLds<H>::TOTAL ? KernLds<C>::TOTAL : KernLds<H>::TOTAL;
+  __shared__ uint4 lds[N];
+  if ((int)blockIdx.x < a.tile0)
+    down_tile<C, GATEUP, false>(a, lds, blockIdx.x, a.tile0, 0);
+  else
+    down_tile<H, GATEUP, true>(a, lds, blockIdx.x - a.tile0, gridDim.x - a.tile0, a.tile0);
 }
 
 // ------------------------------------------------------------------ small-rank down projection
@@ -370,21 +415,25 @@ struct RowVals {
 // z = sigma(h) (SiLU/SwiGLU) and one partial of S' = sum_c dh'*h per (row, wave).
 // The h rows of 32-row block mb+1 are loaded while block mb is computed; those of
 // block 0 and the rows' rstd are loaded at the start of the last k step.
-template <class C, int ACT>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dz(DzArgs a) {
+template <class C, int ACT, bool HALF>
+__device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, int nblk, int tile0) {
   using E = typename C::E;
   using R = Raw4<E>;
   using SW = Sweep<C, C::WTN>;
   constexpr int NL = ACT == ACT_SWIGLU ? 2 : 1;
-  __shared__ uint4 lds[KernLds<C>::TOTAL];
   float* rs_tile = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] rstd of the tile's rows
   const int tiles_n = (a.r + C::BN - 1) / C::BN;
-  const int tiles_m = (a.T + C::BM - 1) / C::BM;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int br = logical / (tiles_m * tiles_n);
-  int tm, tn;
-  grouped_tile<kGroupM>(logical % (tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  // tiles of all branches in turn: branch br, then (tm, tn) within it
+  int br, tm, tn, m0;
+  {
+    const int per = tile_rows<C, HALF>(a.T) * tiles_n;
+    int t, piece;
+    tail_index<HALF>(tile0, bid, nblk, t, piece);
+    br = t / per;
+    grouped_tile<kGroupM>(t % per, tile_rows<C, HALF>(a.T), tiles_n, tm, tn);
+    m0 = (tm * (HALF ? 2 : 1) + piece) * C::BM;
+  }
+  const int n0 = tn * C::BN;
   const int gr = a.g * a.r;
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const SW sw;
@@ -487,6 +536,24 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
     block(mb, g0, u0, g1, u1);
     if (mb + 1 < C::MB) block(mb + 1, g1, u1, g0, u0);
   }
+}
+
+template <class C, int ACT>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dz(DzArgs a) {
+  __shared__ uint4 lds[KernLds<C>::TOTAL];
+  dz_tile<C, ACT, false>(a, lds, blockIdx.x, gridDim.x, 0);
+}
+// whole tiles 0 .. a.tile0-1 on the first a.tile0 work-groups, the halves of the
+// rest on the others
+template <class C, class H, int ACT>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dz_tail(DzArgs a) {
+  static_assert(C::THREADS == H::THREADS && C::WPE == H::WPE, "one launch shape");
+  constexpr int N = KernLds<C>::TOTAL > KernLds<H>::TOTAL ? KernLds<C>::TOTAL : KernLds<H>::TOTAL;
+  __shared__ uint4 lds[N];
+  if ((int)blockIdx.x < a.tile0)
+    dz_tile<C, ACT, false>(a, lds, blockIdx.x, a.tile0, 0);
+  else
+    dz_tile<H, ACT, true>(a, lds, blockIdx.x - a.tile0, gridDim.x - a.tile0, a.tile0);
 }
 
 // ------------------------------------------------------------------ backward: weight gradients
@@ -889,6 +956,8 @@ struct Cfgs<bf16> {
   // short-K up-projection: 128 x 256 tiles, two work-groups per CU, so that one
   // group's stores overlap the other's loads and MFMAs
   using UpShort = PipeCfg<128, 256, 32, 2, 2, 2, 2>;
+  // 128-row halves of the main tiles, for the last round of a grid (see tail_tile)
+  using Half = PipeCfg<128, 256, 64, 2, 2, 2>;
   static constexpr bool HAS_SKINNY = true;
 };
 template <>
@@ -899,8 +968,10 @@ struct Cfgs<float> {
   using N128 = Main;
   using N256 = Main;
   using UpShort = Main;
+  using Half = Main;
   static constexpr bool HAS_SKINNY = false;
 };
+
 
 constexpr int kNumCu = 256;
 constexpr int kUpShortK = 256;   // up-projections with K = r up to this use UpShort tiles
@@ -917,6 +988,21 @@ template bool down_uses_skinny<bf16>(int, int, int, bool);
 template bool down_uses_skinny<float>(int, int, int, bool);
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Tiles of a grid of `tiles` main tiles that run whole: all of them, unless the
+// last round would occupy at most half of the CUs; then only the full rounds (the
+// rest runs as 128-row halves, one round).
+template <class C>
+constexpr bool kHasHalf = Cfgs<typename C::E>::HAS_SKINNY && std::is_same<C, typename Cfgs<typename C::E>::Main>::value;
+template <typename E, class C>
+int tail_full_tiles(int tiles) {
+  if constexpr (!kHasHalf<C>) {
+    return tiles;
+  } else {
+    const int rem = tiles % kNumCu;
+    return rem > 0 && 2 * rem <= kNumCu ? tiles - rem : tiles;
+  }
+}
 
 template <typename E>
 hipError_t launch_rms_stats(const void* x, const void* gamma, void* y, float* sumsq, float* rstd, int T, int d,
@@ -937,13 +1023,25 @@ hipError_t launch_fold_gamma(const void* A, const void* gamma, void* Ap, int d, 
 }
 
 template <class C>
-hipError_t launch_down_cfg(const DownArgs& a, hipStream_t s) {
-  const bool gateup = a.act == ACT_SWIGLU && a.mode == DOWN_BLOCK;
+hipError_t launch_down_cfg(const DownArgs& a0, hipStream_t s) {
+  const bool gateup = a0.act == ACT_SWIGLU && a0.mode == DOWN_BLOCK;
+  const int tiles = cdiv(a0.T, C::BM) * (gateup ? cdiv(a0.r, C::BN / 2) : cdiv(a0.g * a0.r, C::BN));
+  DownArgs a = a0;
+  a.tile0 = tail_full_tiles<typename C::E, C>(tiles);
+  if constexpr (kHasHalf<C>) {
+    if (a.tile0 < tiles) {  // full rounds of whole tiles, then the rest in halves
+      using H = typename Cfgs<typename C::E>::Half;
+      const int grid = a.tile0 + 2 * (tiles - a.tile0);
+      if (gateup)
+        hipLaunchKernelGGL((k_down_tail<C, H, true>), dim3(grid), dim3(C::THREADS), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_down_tail<C, H, false>), dim3(grid), dim3(C::THREADS), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (gateup) {
-    const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN / 2);
     hipLaunchKernelGGL((k_down<C, true>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   } else {
-    const int tiles = cdiv(a.T, C::BM) * cdiv(a.g * a.r, C::BN);
     hipLaunchKernelGGL((k_down<C, false>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   }
   return hipGetLastError();
@@ -1058,13 +1156,29 @@ template <typename E>
 hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
   using C = typename Cfgs<E>::Main;
   if (a.T == 0) return hipSuccess;
-  const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN);
-  if (a.act == ACT_SWIGLU)
-    hipLaunchKernelGGL((k_dz<C, ACT_SWIGLU>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
-  else if (a.act == ACT_SILU)
-    hipLaunchKernelGGL((k_dz<C, ACT_SILU>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_dz<C, ACT_IDENTITY>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN) * n_up;
+  DzArgs b = a;
+  b.tile0 = tail_full_tiles<E, C>(tiles);
+  if constexpr (kHasHalf<C>) {
+    if (b.tile0 < tiles) {  // full rounds of whole tiles, then the rest in halves
+      using H = typename Cfgs<E>::Half;
+      const int grid = b.tile0 + 2 * (tiles - b.tile0);
+      if (a.act == ACT_SWIGLU)
+        hipLaunchKernelGGL((k_dz_tail<C, H, ACT_SWIGLU>), dim3(grid), dim3(C::THREADS), 0, s, b);
+      else if (a.act == ACT_SILU)
+        hipLaunchKernelGGL((k_dz_tail<C, H, ACT_SILU>), dim3(grid), dim3(C::THREADS), 0, s, b);
+      else
+        hipLaunchKernelGGL((k_dz_tail<C, H, ACT_IDENTITY>), dim3(grid), dim3(C::THREADS), 0, s, b);
+      return hipGetLastError();
+    }
+  }
+  if (a.act == ACT_SWIGLU) {
+    hipLaunchKernelGGL((k_dz<C, ACT_SWIGLU>), dim3(tiles), dim3(C::THREADS), 0, s, b);
+  } else if (a.act == ACT_SILU) {
+    hipLaunchKernelGGL((k_dz<C, ACT_SILU>), dim3(tiles), dim3(C::THREADS), 0, s, b);
+  } else {
+    hipLaunchKernelGGL((k_dz<C, ACT_IDENTITY>), dim3(tiles), dim3(C::THREADS), 0, s, b);
+  }
   return hipGetLastError();
 }
 
