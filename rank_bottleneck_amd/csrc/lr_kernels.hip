@@ -956,6 +956,9 @@ struct Cfgs<bf16> {
   // short-K up-projection: 128 x 256 tiles, two work-groups per CU, so that one
   // group's stores overlap the other's loads and MFMAs
   using UpShort = PipeCfg<128, 256, 32, 2, 2, 2, 2>;
+  // up-projection: eight waves (two per SIMD, 128 x 64 each, accumulators in
+  // VGPRs), so that one wave's load issue overlaps the other's MFMAs
+  using Up = PipeCfg<256, 256, 64, 2, 4, 2, 2>;
   // 128-row halves of the main tiles, for the last round of a grid (see tail_tile)
   using Half = PipeCfg<128, 256, 64, 2, 2, 2>;
   static constexpr bool HAS_SKINNY = true;
@@ -968,6 +971,7 @@ struct Cfgs<float> {
   using N128 = Main;
   using N256 = Main;
   using UpShort = Main;
+  using Up = Main;
   using Half = Main;
   static constexpr bool HAS_SKINNY = false;
 };
@@ -1071,7 +1075,7 @@ hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s) {
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (a.r <= kUpShortK) return launch_up_cfg<typename Cfgs<E>::UpShort>(a, n_up, s);
   }
-  return launch_up_cfg<typename Cfgs<E>::Main>(a, n_up, s);
+  return launch_up_cfg<typename Cfgs<E>::Up>(a, n_up, s);
 }
 
 template <typename E>
