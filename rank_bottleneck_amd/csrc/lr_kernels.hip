@@ -961,6 +961,11 @@ struct Cfgs<bf16> {
   using Up = PipeCfg<256, 256, 64, 2, 4, 2, 2>;
   // 128-row halves of the main tiles, for the last round of a grid (see tail_tile)
   using Half = PipeCfg<128, 256, 64, 2, 2, 2>;
+  // down-projection: eight waves (two per SIMD, 64 x 128 each), so that one
+  // wave's load issue overlaps the other's MFMAs
+  using Down = PipeCfg<256, 256, 64, 4, 2, 2, 2>;
+  using DownHalf = PipeCfg<128, 256, 64, 4, 2, 2, 2>;
+  using Wgrad = Main;
   static constexpr bool HAS_SKINNY = true;
 };
 template <>
@@ -973,6 +978,9 @@ struct Cfgs<float> {
   using UpShort = Main;
   using Up = Main;
   using Half = Main;
+  using Down = Main;
+  using DownHalf = Main;
+  using Wgrad = Main;
   static constexpr bool HAS_SKINNY = false;
 };
 
@@ -996,8 +1004,21 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // Tiles of a grid of `tiles` main tiles that run whole: all of them, unless the
 // last round would occupy at most half of the CUs; then only the full rounds (the
 // rest runs as 128-row halves, one round).
+// the 128-row half configuration of a 256-row tile configuration (void: none)
 template <class C>
-constexpr bool kHasHalf = Cfgs<typename C::E>::HAS_SKINNY && std::is_same<C, typename Cfgs<typename C::E>::Main>::value;
+struct HalfOf {
+  using type = void;
+};
+template <>
+struct HalfOf<Cfgs<bf16>::Main> {
+  using type = Cfgs<bf16>::Half;
+};
+template <>
+struct HalfOf<Cfgs<bf16>::Down> {
+  using type = Cfgs<bf16>::DownHalf;
+};
+template <class C>
+constexpr bool kHasHalf = !std::is_void<typename HalfOf<C>::type>::value;
 template <typename E, class C>
 int tail_full_tiles(int tiles) {
   if constexpr (!kHasHalf<C>) {
@@ -1034,7 +1055,7 @@ hipError_t launch_down_cfg(const DownArgs& a0, hipStream_t s) {
   a.tile0 = tail_full_tiles<typename C::E, C>(tiles);
   if constexpr (kHasHalf<C>) {
     if (a.tile0 < tiles) {  // full rounds of whole tiles, then the rest in halves
-      using H = typename Cfgs<typename C::E>::Half;
+      using H = typename HalfOf<C>::type;
       const int grid = a.tile0 + 2 * (tiles - a.tile0);
       if (gateup)
         hipLaunchKernelGGL((k_down_tail<C, H, true>), dim3(grid), dim3(C::THREADS), 0, s, a);
@@ -1053,7 +1074,7 @@ hipError_t launch_down_cfg(const DownArgs& a0, hipStream_t s) {
 
 template <typename E>
 hipError_t launch_down(const DownArgs& a, hipStream_t s) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Down;
   if (a.T == 0) return hipSuccess;
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (down_uses_skinny<E>(a.T, a.r, a.g, a.act == ACT_SWIGLU && a.mode == DOWN_BLOCK))
@@ -1142,7 +1163,7 @@ template int gemm_bk<float>();
 
 template <typename E>
 int wgrad_nparts_used(int gr, bool reduced) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Wgrad;
   return reduced ? gr / 64 : cdiv(gr, C::BN) * C::WN;
 }
 template int wgrad_nparts_used<bf16>(int, bool);
@@ -1151,7 +1172,7 @@ template int wgrad_nparts_used<float>(int, bool);
 template <typename E>
 int wgrad_nparts(int gr) {
   // one partial per (column tile, wave column) without splits, one per 64 columns with
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Wgrad;
   const int a = cdiv(gr, C::BN) * C::WN, b = gr / 64;
   return a > b ? a : b;
 }
@@ -1165,7 +1186,7 @@ hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
   b.tile0 = tail_full_tiles<E, C>(tiles);
   if constexpr (kHasHalf<C>) {
     if (b.tile0 < tiles) {  // full rounds of whole tiles, then the rest in halves
-      using H = typename Cfgs<E>::Half;
+      using H = typename HalfOf<C>::type;
       const int grid = b.tile0 + 2 * (tiles - b.tile0);
       if (a.act == ACT_SWIGLU)
         hipLaunchKernelGGL((k_dz_tail<C, H, ACT_SWIGLU>), dim3(grid), dim3(C::THREADS), 0, s, b);
@@ -1188,7 +1209,7 @@ hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
 
 template <typename E>
 WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Wgrad;
   const int gr = g * r;
   WgradPlan p{};
   p.tiles = n_up * cdiv(r, C::BM) * cdiv(d, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
@@ -1225,7 +1246,7 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
 
 template <typename E>
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Wgrad;
   const int gr = a.g * a.r;
   const int tilesB = cdiv(a.r, C::BM) * cdiv(a.d, C::BN);
   const int tilesA = cdiv(a.d, C::BM) * cdiv(gr, C::BN);
@@ -1245,7 +1266,7 @@ hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
   const int64_t n4 = ((int64_t)a.n_up * a.r * a.d + (int64_t)a.d * a.g * a.r) / 4;
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (a.streamk) {
-      hipLaunchKernelGGL((k_wgrad_sk_reduce<typename Cfgs<E>::Main>), dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((k_wgrad_sk_reduce<typename Cfgs<E>::Wgrad>), dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }

@@ -263,17 +263,7 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) fb[nb] = frag<C, C::BN, B_MNC>(tb, wn * C::WTN + nb * 32, s, lane);
   };
-  // LDS reads of the next fragments interleaved one-for-one with this sub-step's MFMAs
-  auto interleave = [&]() {
-    constexpr int NREAD = C::MB * (A_MNC ? 2 : 1) + C::NB * (B_MNC ? 2 : 1);
-    constexpr int NMFMA = C::MB * C::NB;
-#pragma unroll
-    for (int i = 0; i < (NREAD < NMFMA ? NREAD : NMFMA); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    }
-    if constexpr (NMFMA > NREAD) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
-  };
+
 
   if (nk > 0) {
     // Prefetch distance: STAGES stages.  Once every wave holds its last fragments of
@@ -353,11 +343,14 @@ __device__ __forceinline__ void gemm_pipe(const Opnd& oa, const Opnd& ob, const 
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
           mfma_chunk(acc[i / C::NB][i % C::NB], b[cur][i % C::NB], a[cur][i / C::NB], (bf16*)nullptr);
-          // fragment reads after the even MFMAs and refill loads after the odd ones,
-          // where there are MFMAs enough for that (a slot with both stalls the MFMA pipe)
+          // fragment fi is read after MFMA slot(fi): after the even MFMAs, with the
+          // refill loads after the odd ones, where there are MFMAs enough for that
+          // (a slot with both stalls the MFMA pipe); spread over all MFMAs otherwise
           constexpr bool DISJ = NMF >= 2 * NF;
-          if (DISJ ? (i % 2 == 0 && i / 2 < NF) : (i < NF)) {
-            const int fi = DISJ ? i / 2 : i;
+#pragma unroll
+          for (int fi = 0; fi < NF; ++fi) {
+            const int slot = DISJ ? 2 * fi : (NF <= NMF ? fi : fi * NMF / NF);
+            if (slot != i) continue;
             if (fi < C::MB)
               a[nxt][fi] = frag<C, C::BM, A_MNC>(fa, wm * C::WTM + fi * 32, fs, lane);
             else
