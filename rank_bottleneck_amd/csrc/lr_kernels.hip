@@ -421,6 +421,10 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, in
   using R = Raw4<E>;
   using SW = Sweep<C, C::WTN>;
   constexpr int NL = ACT == ACT_SWIGLU ? 2 : 1;
+  // four waves: the epilogue's first loads go out in the last k step and those
+  // of row block mb+1 while block mb is computed; eight (two per SIMD) have no
+  // registers for that, the other wave of the SIMD covers the wait instead
+  constexpr bool PF = C::NWAVES <= 4;
   float* rs_tile = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] rstd of the tile's rows
   const int tiles_n = (a.r + C::BN - 1) / C::BN;
   // tiles of all branches in turn: branch br, then (tm, tn) within it
@@ -468,7 +472,12 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, in
   Opnd oa{a.dy[br], a.d, a.T, a.d};
   Opnd ob{a.B[br], a.d, a.r, a.d};  // B_i^T: (n = c, k = j) at B_i[c*d + j]
   f32x16 acc[C::MB][C::NB];
-  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc, pre);
+  if constexpr (PF) {
+    mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc, pre);
+  } else {
+    mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.d, lds, nullptr, acc);
+    pre();
+  }
   rsv.publish(rs_tile);
   __syncthreads();
 
@@ -476,7 +485,7 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, in
   char LR_LDS* reg = stage_region<C>(lds);
   // block mb computes from `cur` while block mb+1 loads into `nxt`
   auto block = [&](int mb, const Buf& cg, const Buf& cu, Buf& ng, Buf& nu) {
-    if (mb + 1 < C::MB) load_block(mb + 1, ng, nu);
+    if (PF && mb + 1 < C::MB) load_block(mb + 1, ng, nu);
     stage_block<C>(acc, mb, reg);
     const int rb = m0 + wm * C::WTM + mb * 32;
 #pragma unroll
@@ -531,10 +540,18 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, in
       if (row < a.T && row_sum_lane<SW::LPR>()) a.spart[(int64_t)row * a.spstride + part] = srow;
     }
   };
+  if constexpr (PF) {
 #pragma unroll
-  for (int mb = 0; mb < C::MB; mb += 2) {
-    block(mb, g0, u0, g1, u1);
-    if (mb + 1 < C::MB) block(mb + 1, g1, u1, g0, u0);
+    for (int mb = 0; mb < C::MB; mb += 2) {
+      block(mb, g0, u0, g1, u1);
+      if (mb + 1 < C::MB) block(mb + 1, g1, u1, g0, u0);
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      if (mb > 0) load_block(mb, g0, u0);
+      block(mb, g0, u0, g0, u0);
+    }
   }
 }
 
@@ -875,6 +892,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   using E = typename C::E;
   using R = Raw4<E>;
   using SW = Sweep<C, C::WTN>;
+  constexpr bool PF = C::NWAVES <= 4;  // prefetch of the next row block's x (see dz)
   __shared__ uint4 lds[KernLds<C>::TOTAL];
   float* srow = reinterpret_cast<float*>(lds + KernLds<C>::MAIN);  // [BM] : rstd*S'/D
   const int gr = a.g * a.r;
@@ -910,7 +928,12 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   Opnd oa{a.dh, gr, a.T, gr};   // dh' [T, gr]
   Opnd ob{a.A, gr, a.d, gr};    // A^T: (n = j, k = c) at A[j*gr + c]
   f32x16 acc[C::MB][C::NB];
-  mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc, pre);
+  if constexpr (PF) {
+    mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc, pre);
+  } else {
+    mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc);
+    pre();
+  }
   srv.publish(a, m0, srow);
   __syncthreads();
 
@@ -918,7 +941,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   char LR_LDS* reg = stage_region<C>(lds);
   // block mb computes from `cur` while block mb+1 loads into `nxt`
   auto block = [&](int mb, const typename R::T (&cur)[SW::IT], typename R::T (&nxt)[SW::IT]) {
-    if (mb + 1 < C::MB) load_block(mb + 1, nxt);
+    if (PF && mb + 1 < C::MB) load_block(mb + 1, nxt);
     stage_block<C>(acc, mb, reg);
     const int rb = m0 + wm * C::WTM + mb * 32;
 #pragma unroll
@@ -932,10 +955,18 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
              g4.z * v.z - x4.z * sr, g4.w * v.w - x4.w * sr);
     }
   };
+  if constexpr (PF) {
 #pragma unroll
-  for (int mb = 0; mb < C::MB; mb += 2) {
-    block(mb, xin0, xin1);
-    if (mb + 1 < C::MB) block(mb + 1, xin1, xin0);
+    for (int mb = 0; mb < C::MB; mb += 2) {
+      block(mb, xin0, xin1);
+      if (mb + 1 < C::MB) block(mb + 1, xin1, xin0);
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      if (mb > 0) load_block(mb, xin0);
+      block(mb, xin0, xin0);
+    }
   }
 }
 
@@ -961,11 +992,14 @@ struct Cfgs<bf16> {
   using Up = PipeCfg<256, 256, 64, 2, 4, 2, 2>;
   // 128-row halves of the main tiles, for the last round of a grid (see tail_tile)
   using Half = PipeCfg<128, 256, 64, 2, 2, 2>;
-  // down-projection: eight waves (two per SIMD, 64 x 128 each), so that one
-  // wave's load issue overlaps the other's MFMAs
+  // down-projection: eight waves (two per SIMD, 64 x 128 each, accumulators in
+  // VGPRs), so that one wave's load issue overlaps the other's MFMAs
   using Down = PipeCfg<256, 256, 64, 4, 2, 2, 2>;
   using DownHalf = PipeCfg<128, 256, 64, 4, 2, 2, 2>;
   using Wgrad = Main;
+  // dz and dx: eight waves as the down-projection
+  using Dz = Down;
+  using Dx = Down;
   static constexpr bool HAS_SKINNY = true;
 };
 template <>
@@ -981,6 +1015,8 @@ struct Cfgs<float> {
   using Down = Main;
   using DownHalf = Main;
   using Wgrad = Main;
+  using Dz = Main;
+  using Dx = Main;
   static constexpr bool HAS_SKINNY = false;
 };
 
@@ -1151,7 +1187,7 @@ hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void
 
 template <typename E>
 int dz_nparts(int r) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Dz;
   return cdiv(r, C::BN) * C::WN;
 }
 template <typename E>
@@ -1179,7 +1215,7 @@ int wgrad_nparts(int gr) {
 
 template <typename E>
 hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Dz;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.r, C::BN) * n_up;
   DzArgs b = a;
@@ -1277,7 +1313,7 @@ hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
 
 template <typename E>
 hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
-  using C = typename Cfgs<E>::Main;
+  using C = typename Cfgs<E>::Dx;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
   hipLaunchKernelGGL((k_dx<C>), dim3(tiles), dim3(C::THREADS), 0, s, a);
