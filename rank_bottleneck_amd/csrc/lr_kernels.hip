@@ -815,18 +815,9 @@ __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
     const int last = sk_owner((int64_t)(t + 1) * a.sk_KS - 1, a.sk_Q, a.sk_R);
     const float* slot = a.wpart + (int64_t)t * a.sk_maxseg * (C::BM * C::BN) +
                         (int64_t)(row - tm * C::BM) * C::BN + (col - tn * C::BN);
-    // the first four slots' loads all in flight before the sums (in slot order)
-    const int nseg = last - first + 1;
-    float4 p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < nseg) p[j] = *reinterpret_cast<const float4*>(slot + (int64_t)j * (C::BM * C::BN));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < nseg) { acc.x += p[j].x; acc.y += p[j].y; acc.z += p[j].z; acc.w += p[j].w; }
-    for (int j = 4; j < nseg; ++j) {
-      const float4 q = *reinterpret_cast<const float4*>(slot + (int64_t)j * (C::BM * C::BN));
-      acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+    for (int j = 0; j <= last - first; ++j) {
+      const float4 p = *reinterpret_cast<const float4*>(slot + (int64_t)j * (C::BM * C::BN));
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
     }
   }
   if (active && job < a.n_up) {
