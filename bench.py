@@ -28,7 +28,8 @@ METRIC_FWD = "low-rank block forward HBM GB/s (small-rank, memory-bound sweep)"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (published)
 PEAK_GBS = 8000.0                                # MI355X HBM3E (published)
 KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
-                  "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h"]
+                  "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h",
+                  "rank_bottleneck_amd/csrc/lr_fused.hip"]
 
 
 def log(*a):
@@ -53,6 +54,9 @@ def kernel_work(wl, name: str):
         if wl.seam:   # fp32 partial + sumsq
             return 2.0 * T * d * gr, e * (T * d + d * gr) + 4 * (T * gr + T)
         return 2.0 * T * d * gr, e * (T * d + d * gr + T * gr + T * zcols)
+    if name == "fused":   # one-kernel small-rank forward: x, A'^T, B, y and h, each once
+        return (2.0 * T * d * gr + 2.0 * T * r * d * nu,
+                e * (T * d + d * gr + nu * r * d + nu * T * d + T * gr))
     if name == "up":
         return 2.0 * T * r * d * nu, e * (T * r * nu + nu * r * d + nu * T * d)
     if name == "dz":
@@ -64,8 +68,9 @@ def kernel_work(wl, name: str):
         return 0.0, 4 * (d * gr + nu * r * d)
     if name == "dx":
         return 2.0 * T * gr * d, e * (T * gr + d * gr + 2 * T * d) + 4 * T
-    if name == "fold_gamma":
-        return 0.0, e * (2 * d * gr + d)
+    if name == "fold_gamma":   # the one-kernel small-rank path also transposes B
+        fused = wl.dtype == "bf16" and g == 1 and r in (64, 128, 256) and wl.act != "swiglu" and not wl.seam
+        return 0.0, e * ((4 if fused else 2) * d * gr + d)
     if name == "rms_stats":
         return 0.0, e * T * d + 4 * T
     if name == "finish":

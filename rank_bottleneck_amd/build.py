@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblrblock.so")
-SOURCES = ["lr_kernels.hip", "lr_api.cpp"]
+SOURCES = ["lr_kernels.hip", "lr_fused.hip", "lr_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -54,9 +54,17 @@ int small_splits(const lr_dims* d) {
                              : lr::small_rank_splits<float>((int)d->T, (int)d->d, (int)d->r, (int)d->g, d->act);
 }
 
-// A' (or A'^T), z, then for the small-rank forward the split partials and sums of squares
+// whether the forward runs as the one-kernel small-rank path
+bool fused_fwd(const lr_dims* d) {
+  return d->dtype == LR_BF16 && lr::fused_fwd_supported((int)d->r, (int)d->g, d->act);
+}
+
+// A' (or A'^T), z, then for the small-rank forward the split partials and sums of
+// squares.  The one-kernel path uses A'^T and B in fragment order; z stays reserved for the shard
+// seam (lr_up_finish), which shares this size.
 size_t fwd_ws(const lr_dims* d) {
   const size_t es = esize(d->dtype), gr = (size_t)(d->g * d->r), T = (size_t)d->T;
+  if (fused_fwd(d)) return 2 * align_up((size_t)d->d * gr * es) + align_up(T * gr * es);
   const size_t ns = (size_t)small_splits(d);
   return align_up((size_t)d->d * gr * es) + align_up(T * gr * es) + align_up(ns * T * gr * 4) +
          align_up(ns * T * 4);
@@ -116,6 +124,17 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
+  if (fused_fwd(d)) {
+    // g = 1, small r: x . A', deferred rstd, sigma and the up-projection in one
+    // kernel; z stays in LDS
+    void* Bf = cv.take<void>((size_t)D * gr * sizeof(E));
+    LR_LAUNCH("fold_gamma", s, lr::launch_fold_fused(A, gamma, B[0], Ap, Bf, D, gr, s));
+    lr::FusedArgs fa{};
+    fa.x = x; fa.Apt = Ap; fa.Bf = Bf; fa.y = y[0]; fa.h = h_save;
+    fa.T = T; fa.d = D; fa.r = r; fa.invD = inv_width(d); fa.eps = d->eps;
+    LR_LAUNCH("fused", s, lr::launch_fused_fwd(fa, d->act, s));
+    return LR_OK;
+  }
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
   const int ns = small_splits(d);
   if (ns > 0) {

@@ -1,0 +1,383 @@
+// Small-rank forward of the block in one kernel (g = 1, g*r in {64, 128, 256}):
+//   h = diag(rstd) . ((x (.) gamma) . A),  z = sigma(h),  y = z . B
+// BOOST's low-rank layer pairs a d x r and an r x d projection with the
+// operations between them (summary, section 2.1) and normalizes with statistics
+// accumulated alongside the projection (section 2.2, Online RMSNorm).  At small r
+// both GEMMs are thin and the block is bound by HBM: it must read x once and
+// write y (and the checkpoint h) once.  Here the rank-r activation z never
+// leaves the chip: each work-group owns BM token rows, forms z for them in LDS
+// and streams the up-projection out of it.
+//
+// Work-group of 8 waves in two roles, because on this chip the vector memory
+// counter counts stores as well as loads: a wave that waits for a DMA stage
+// after issuing output stores also waits for those stores.
+//   MMA waves (0-3): all global loads (x and A' tiles by DMA into LDS in phase 1;
+//     B fragments straight into registers in phase 3) and the MFMAs.
+//   store waves (4-7): the row sum of squares (phase 1, from the x tiles in LDS),
+//     h and z (phase 2), and the y stores (phase 3, from bf16 tiles the MMA waves
+//     stage in LDS, double-buffered).  They issue no global loads.
+// Both roles run the same sequence of barriers (one per k step of phase 1, one
+// per column tile of phase 3, and the phase boundaries), with every branch on
+// the role inside a barrier interval.
+//
+// Phase 3 reads B in MFMA fragment order (written with A'^T by the fold kernel):
+// the operand fragment of 32 columns x 16 k values is 1 KB of consecutive memory,
+// lane l's 16 bytes holding column l%32 and k values 8(l/32) .. +7, so every
+// fragment is one fully coalesced load into registers.  The MMA waves hold the
+// next column tile's fragments while they multiply the current one, so the
+// up-projection needs no LDS ring and no wait on other waves' loads.
+//
+// LDS (bytes from 0):
+//   phase 1: ring of S1 stages [x tile | A'^T tile] and the sink of dead stages;
+//   phases 2-3 (after the ring is drained): z as KT tiles of [BM][64] (K
+//     contiguous, swizzled as an MFMA A tile), BM floats of rstd, then the fp32
+//     staging of h (phase 2) or two bf16 y tiles (phase 3).
+#include "lr_kernels.h"
+#include "lr_pipe.h"
+
+namespace lr {
+
+template <int GR>
+struct FusedGeo {
+  static constexpr int BM = 64;
+  static constexpr int BK1 = GR == 256 ? 32 : 64;
+  static constexpr int S1 = GR == 64 ? 8 : (GR == 128 ? 6 : 7);
+  // phase 1 tile [BM, GR]: MMA waves 2 x 2, wave tile 32 x GR/2
+  using C1 = PipeCfg<BM, GR, BK1, 2, 2, S1>;
+  // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of 32
+  // columns; the B fragments of PF column tiles ahead in flight (register
+  // buffers NBUF = PF + 1), 48-64 KB per CU
+  static constexpr int BN3 = 128;
+  static constexpr int PF = GR == 64 ? 3 : (GR == 128 ? 2 : 1);
+  static constexpr int NBUF = PF + 1;
+  using C3 = PipeCfg<BM, 128, 64, 2, 2, 2>;  // z fragment geometry (BK = 64)
+  static constexpr int KT = GR / 64;  // 64-deep k blocks of z
+  static constexpr int THREADS = 512;
+
+  static constexpr int P1 = S1 * C1::STAGE_BYTES + C1::SINK_BYTES;
+  static constexpr int ZT = BM * 128;                  // one [BM][64] bf16 z tile
+  static constexpr int ZB = KT * ZT;
+  static constexpr int ROWSS = ZB;
+  static constexpr int STG = ZB + 256;
+  static constexpr int STG2_PITCH = GR * 4 + 16;       // fp32 h row + pad
+  static constexpr int STG2_BYTES = BM * STG2_PITCH;
+  static constexpr int STG3_PITCH = BN3 * 2 + 16;      // bf16 y row + pad
+  static constexpr int STG3_BUF = BM * STG3_PITCH;
+  static constexpr int P3 = STG + 2 * STG3_BUF;
+  static constexpr int P2 = STG + STG2_BYTES;
+  static constexpr int LDS = P1 > P3 ? (P1 > P2 ? P1 : P2) : (P3 > P2 ? P3 : P2);
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(GR % 64 == 0 && GR <= 256, "rank");
+  static constexpr int Q1X = DmaTile<C1, BM, false>::Q, Q1A = DmaTile<C1, GR, false>::Q;
+  static_assert((S1 - 2) * (Q1X + Q1A) <= 63, "vmcnt range");
+};
+
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int GR, int ACT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fused_fwd(FusedArgs a) {
+  using G = FusedGeo<GR>;
+  using C1 = typename G::C1;
+  using C3 = typename G::C3;
+  __shared__ uint4 lds[G::LDS / 16];
+  char LR_LDS* ldsp = (char LR_LDS*)(lds);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)ldsp;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool mma = wave < 4;
+  const int w = wave & 3;                 // index within the role
+  const int wm = w >> 1, wn = w & 1;      // MMA wave position (2 x 2)
+  const int u = w * 64 + lane;            // store-role thread index 0..255
+  const int m0 = blockIdx.x * G::BM;
+  const int d = a.d;
+
+  // ---------------------------------------------------------------- phase 1: acc1 = x . A'
+  const int nk1 = d / C1::BK;
+  f32x16 acc1[C1::NB];
+#pragma unroll
+  for (int nb = 0; nb < C1::NB; ++nb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc1[nb][v] = 0.f;
+  float ss = 0.f;
+
+  DmaTile<C1, G::BM, false> dxt;
+  DmaTile<C1, GR, false> dat;
+  const Opnd ox{a.x, d, a.T, d};
+  const Opnd oa{a.Apt, d, GR, d};
+  if (mma) {
+    dxt.init(ox, MapId{}, m0, w, lane);
+    dat.init(oa, MapId{}, 0, w, lane);
+    dxt.init_range(ox, m0, 0);
+    dat.init_range(oa, 0, 0);
+  }
+  auto issue1 = [&](int st) {
+    const bool live = st < nk1;
+    const uint32_t base = lds0 + (live ? (st % G::S1) * C1::STAGE_BYTES : G::S1 * C1::STAGE_BYTES);
+    dxt.issue(dxt.rsrc(st, live), base, w);
+    dat.issue(dat.rsrc(st, live), live ? base + C1::A_BYTES : base, w);
+  };
+  if (mma) {
+#pragma unroll
+    for (int st = 0; st < G::S1 - 1; ++st) issue1(st);
+  }
+  for (int kt = 0; kt < nk1; ++kt) {
+    if (mma) wait_vmcnt<(G::S1 - 2) * (G::Q1X + G::Q1A)>();
+    lgkm_wait0();
+    block_barrier();  // stage kt landed for every wave; stage kt-1's buffer is free
+    const char LR_LDS* ta = ldsp + (kt % G::S1) * C1::STAGE_BYTES;
+    if (mma) {
+      issue1(kt + G::S1 - 1);
+      const char LR_LDS* tb = ta + C1::A_BYTES;
+#pragma unroll
+      for (int s = 0; s < C1::KS; ++s) {
+        const uint4 fa = frag<C1, G::BM, false>(ta, wm * 32, s, lane);
+#pragma unroll
+        for (int nb = 0; nb < C1::NB; ++nb) {
+          const uint4 fb = frag<C1, GR, false>(tb, wn * C1::WTN + nb * 32, s, lane);
+          mfma_chunk(acc1[nb], fb, fa, (bf16*)nullptr);
+        }
+      }
+    } else {
+      // sum of squares of row u/4 over this stage: 4 lanes per row, each a
+      // quarter of the row's 16-byte chunks (their order within the row does
+      // not matter for the sum)
+      constexpr int RB = C1::BK * 2, CPL = RB / 16 / 4;
+      const char LR_LDS* rp = ta + (u >> 2) * RB + (u & 3) * CPL * 16;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const uint4 q = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4 LR_LDS*>(rp + c * 16));
+        ss = frag_sumsq(q, ss);
+      }
+    }
+  }
+  if (mma) wait_vmcnt<0>();  // the sink loads of dead stages
+  lgkm_wait0();
+  block_barrier();  // the ring is dead from here on
+
+  // ---------------------------------------------------------------- phase 2: h, z
+  float LR_LDS* rowss = reinterpret_cast<float LR_LDS*>(ldsp + G::ROWSS);
+  char LR_LDS* stg = ldsp + G::STG;
+  if (mma) {
+    // lane l holds row l%32 of its 32-row block, columns 8q + 4(l/32) + 0..3 of
+    // each 32-column block nb (the swapped operand order of mfma_chunk)
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    char LR_LDS* rowp = stg + (wm * 32 + (lane & 31)) * G::STG2_PITCH + 16 * (lane >> 5);
+#pragma unroll
+    for (int nb = 0; nb < C1::NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 v = {acc1[nb][4 * q], acc1[nb][4 * q + 1], acc1[nb][4 * q + 2], acc1[nb][4 * q + 3]};
+        *reinterpret_cast<f4 LR_LDS*>(rowp + (wn * C1::WTN + nb * 32 + 8 * q) * 4) = v;
+      }
+  } else {
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    if ((u & 3) == 0) rowss[u >> 2] = __builtin_amdgcn_rsqf(ss * a.invD + a.eps);
+  }
+  lgkm_wait0();
+  block_barrier();
+  if (!mma) {
+    constexpr int LPR = GR / 4, RPI = 256 / LPR;
+    bf16* h = static_cast<bf16*>(a.h);
+    const int c = (u % LPR) * 4;
+    // z tile of column c: [BM][64] K-contiguous, 16-byte chunks swizzled as the
+    // MFMA A-operand reads expect
+    const int zt = c / 64, kk = c % 64;
+#pragma unroll 4
+    for (int p = 0; p < G::BM / RPI; ++p) {
+      const int rl = p * RPI + u / LPR;
+      const float4 v = lds_f4(stg + rl * G::STG2_PITCH + c * 4);
+      const float rs = rowss[rl];
+      float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
+      if (h && m0 + rl < a.T) store4(h + (int64_t)(m0 + rl) * GR + c, hv[0], hv[1], hv[2], hv[3]);
+      if constexpr (ACT == ACT_SILU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = hv[e] * sigmoidf_(hv[e]);
+      }
+      const bf16x4 zv = {(bf16)hv[0], (bf16)hv[1], (bf16)hv[2], (bf16)hv[3]};
+      const int slot = (kk / 8) ^ kc_swz<128>(rl);
+      *reinterpret_cast<bf16x4 LR_LDS*>(ldsp + zt * G::ZT + rl * 128 + slot * 16 + (kk % 8) * 2) = zv;
+    }
+  }
+  lgkm_wait0();
+  block_barrier();  // z complete; the h staging and rstd are dead
+
+  // ---------------------------------------------------------------- phase 3: y = z . B
+  const int nt_count = (d + G::BN3 - 1) / G::BN3;
+  bf16* y = static_cast<bf16*>(a.y);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  // z fragments (both 32-row blocks) in registers up to r = 128; at r = 256 they
+  // are read from LDS (z stays there through phase 3) to leave registers for B
+  constexpr bool ZREG = GR <= 128;
+  uint4 zf[ZREG ? 2 : 1][ZREG ? G::KT : 1][4];
+  f32x16 acc3[2];
+  uint4 bb[G::NBUF][G::KT][4];
+  const bf16* Bf = static_cast<const bf16*>(a.Bf);
+  // B fragments of this wave's 32 columns of column tile nt: fragment (column
+  // block cb, k16 block kb) starts at element ((cb * GR/16 + kb) * 64) * 8; a
+  // column block past d (the last tile's upper half when d is an odd multiple of
+  // 64) reads the last one and feeds y columns that are never stored
+  auto load_b = [&](int nt, uint4 (&bf)[G::KT][4]) {
+    const int cb = min(nt * (G::BN3 / 32) + w, d / 32 - 1);
+    const bf16* fp = Bf + ((int64_t)cb * (GR / 16) * 64 + lane) * 8;
+#pragma unroll
+    for (int kt = 0; kt < G::KT; ++kt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        bf[kt][s] = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4*>(fp + (kt * 4 + s) * 64 * 8));
+  };
+  if (mma) {
+    if constexpr (ZREG) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kt = 0; kt < G::KT; ++kt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) zf[mb][kt][s] = frag<C3, G::BM, false>(ldsp + kt * G::ZT, mb * 32, s, lane);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc3[mb][v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::PF; ++j) load_b(j, bb[j]);
+  }
+  // store role: one staged [BM][BN3] bf16 tile -> y (16 lanes per row, 16 bytes
+  // each); write-back stores, which stream faster than nontemporal ones here
+  auto store_tile = [&](int nt) {
+    constexpr int LPR = G::BN3 / 8, RPI = 256 / LPR;
+    const char LR_LDS* buf = stg + (nt & 1) * G::STG3_BUF;
+    const int ch = u % LPR, col = nt * G::BN3 + ch * 8;
+#pragma unroll
+    for (int p = 0; p < G::BM / RPI; ++p) {
+      const int rl = p * RPI + u / LPR;
+      const u32x4 v = *reinterpret_cast<const u32x4 LR_LDS*>(buf + rl * G::STG3_PITCH + ch * 16);
+      if (m0 + rl < a.T && col < d) *reinterpret_cast<u32x4*>(y + (int64_t)(m0 + rl) * d + col) = v;
+    }
+  };
+  // MMA role: column tile nt from buffer bc while tile nt+PF loads into bn (the
+  // buffer tile nt-1 used); the tile is staged as bf16 in LDS buffer nt & 1.
+  // Loads and tiles past the end are not skipped but clamped or masked (see
+  // below): a skipped load would make the compiler merge register values with
+  // copies, and each copy of a load target waits for every load in flight.
+  auto mma_tile = [&](int nt, const uint4 (&bc)[G::KT][4], uint4 (&bn)[G::KT][4]) {
+    load_b(nt + G::PF, bn);
+#pragma unroll
+    for (int kt = 0; kt < G::KT; ++kt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          uint4 za;
+          if constexpr (ZREG)
+            za = zf[mb][kt][s];
+          else
+            za = frag<C3, G::BM, false>(ldsp + kt * G::ZT, mb * 32, s, lane);
+          mfma_chunk(acc3[mb], bc[kt][s], za, (bf16*)nullptr);
+        }
+    // lane l holds row l%32 of row block mb, columns 8q + 4(l/32) + 0..3 of the
+    // wave's 32 columns
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      char LR_LDS* rowp = stg + (nt & 1) * G::STG3_BUF + (mb * 32 + (lane & 31)) * G::STG3_PITCH + 8 * (lane >> 5);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x4 v = {(bf16)acc3[mb][4 * q], (bf16)acc3[mb][4 * q + 1], (bf16)acc3[mb][4 * q + 2],
+                          (bf16)acc3[mb][4 * q + 3]};
+        *reinterpret_cast<bf16x4 LR_LDS*>(rowp + (w * 32 + 8 * q) * 2) = v;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc3[mb][v] = 0.f;
+    }
+  };
+  // NBUF tiles per outer step so that every buffer index is a constant.  The
+  // tile count is rounded up to a multiple of NBUF: the extra tiles multiply the
+  // clamped fragments and stage a tile whose columns all lie past d, which the
+  // store role masks.  Each role runs its own loop with one barrier per tile
+  // (the same count in both): in a shared loop body the compiler's wait analysis
+  // would merge the store role's pending stores with the MMA role's pending
+  // loads and wait for all of them before every fragment load.
+  const int nt_pad = (nt_count + G::NBUF - 1) / G::NBUF * G::NBUF;
+  if (mma) {
+    for (int base = 0; base < nt_pad; base += G::NBUF) {
+#pragma unroll
+      for (int j = 0; j < G::NBUF; ++j) {
+        mma_tile(base + j, bb[j], bb[(j + G::PF) % G::NBUF]);
+        lgkm_wait0();
+        block_barrier();  // tile staged; the previous tile's reads are done, so its buffer is free
+      }
+    }
+  } else {
+    for (int nt = 0; nt < nt_pad; ++nt) {
+      if (nt > 0) store_tile(nt - 1);  // staged in the previous interval
+      lgkm_wait0();
+      block_barrier();
+    }
+    store_tile(nt_pad - 1);
+  }
+}
+
+// A'^T = (diag(gamma) A)^T [n, d] for A [d, n], and B [n, d] in MFMA fragment
+// order, in one launch; one thread per 16-byte output chunk (8 elements), the
+// first n*d/8 threads for A'^T, the rest for B.
+//   A'^T chunk t: column c = t % n of A, rows j0 = 8 (t / n) .. +7 (lanes read
+//     consecutive columns of a row).
+//   B chunk t: fragment f = t / 64 = cb * (n/16) + kb, lane l = t % 64: column
+//     32 cb + l%32, k values 16 kb + 8(l/32) .. +7.
+__global__ __launch_bounds__(256) void k_fold_fused(const bf16* __restrict__ A, const bf16* __restrict__ gamma,
+                                                    const bf16* __restrict__ B, bf16* __restrict__ Apt,
+                                                    bf16* __restrict__ Bf, int d, int n) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t chunks = (int64_t)n * d / 8;
+  bf16x8 v;
+  if (t < chunks) {
+    const int c = (int)(t % n), j0 = (int)(t / n) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)A[(int64_t)(j0 + i) * n + c] * (float)gamma[j0 + i]);
+    *reinterpret_cast<bf16x8*>(Apt + (int64_t)c * d + j0) = v;
+  } else if (t < 2 * chunks) {
+    const int64_t tb = t - chunks;
+    const int l = (int)(tb % 64);
+    const int64_t f = tb / 64;
+    const int kb = (int)(f % (n / 16)), cb = (int)(f / (n / 16));
+    const int col = cb * 32 + (l & 31), k0 = kb * 16 + 8 * (l >> 5);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = B[(int64_t)(k0 + i) * d + col];
+    *reinterpret_cast<bf16x8*>(Bf + tb * 8) = v;
+  }
+}
+
+hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int n,
+                             hipStream_t s) {
+  const int64_t chunks = (int64_t)n * d / 8;
+  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)((2 * chunks + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16*>(A), static_cast<const bf16*>(gamma), static_cast<const bf16*>(B),
+                     static_cast<bf16*>(Apt), static_cast<bf16*>(Bf), d, n);
+  return hipGetLastError();
+}
+
+template <int GR, int ACT>
+static hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_fused_fwd<GR, ACT>), dim3((a.T + 63) / 64), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+bool fused_fwd_supported(int r, int g, int act) {
+  return g == 1 && (r == 64 || r == 128 || r == 256) && (act == ACT_IDENTITY || act == ACT_SILU);
+}
+
+hipError_t launch_fused_fwd(const FusedArgs& a, int act, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (!fused_fwd_supported(a.r, 1, act)) return hipErrorInvalidValue;
+  const bool silu = act == ACT_SILU;
+  switch (a.r) {
+    case 64: return silu ? launch_fused_g<64, ACT_SILU>(a, s) : launch_fused_g<64, ACT_IDENTITY>(a, s);
+    case 128: return silu ? launch_fused_g<128, ACT_SILU>(a, s) : launch_fused_g<128, ACT_IDENTITY>(a, s);
+    default: return silu ? launch_fused_g<256, ACT_SILU>(a, s) : launch_fused_g<256, ACT_IDENTITY>(a, s);
+  }
+}
+
+}  // namespace lr

@@ -34,6 +34,17 @@ struct SplitDownArgs {
   float* sumsq;       // [nsplit][T]
 };
 
+// Small-rank forward in one kernel (g = 1): x, A'^T [r, d] (gamma folded in), B [r, d]
+struct FusedArgs {
+  const void* x;      // [T, d]
+  const void* Apt;    // [r, d]: (diag(gamma) A)^T, K-contiguous
+  const void* Bf;     // B [r, d] in MFMA fragment order (launch_fold_fused)
+  void* y;            // [T, d]
+  void* h;            // [T, r] or null
+  int T, d, r;
+  float invD, eps;
+};
+
 struct UpArgs {
   const void* z;      // A operand source; branch i starts at column i*r
   int64_t ldz;
@@ -118,6 +129,13 @@ template <typename E> hipError_t launch_fold_gamma_t(const void* A, const void* 
 // regular down-projection is used.
 template <typename E> int small_rank_splits(int T, int d, int r, int g, int act);
 template <typename E> hipError_t launch_down_split(const SplitDownArgs& a, hipStream_t s);
+// whether the one-kernel small-rank forward serves these dims (bf16 only)
+bool fused_fwd_supported(int r, int g, int act);
+hipError_t launch_fused_fwd(const FusedArgs& a, int act, hipStream_t s);
+// A'^T = (diag(gamma) A)^T [n, d] for A [d, n], and B [n, d] in MFMA fragment
+// order (fragment of 32 columns x 16 k values = 64 lanes x 8 consecutive k) (bf16)
+hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int n,
+                             hipStream_t s);
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 // sums the split partials of launch_wgrad (nothing to do when nsplit == 1)

@@ -51,6 +51,10 @@ SMALL = [
     # g*r <= 256 with few row tiles: the split-K small-rank forward
     Workload("bf16_swiglu_r64", 640, 256, 64, 2, "swiglu", "bf16"),
     Workload("bf16_identity_r128", 513, 320, 128, 1, "identity", "bf16"),
+    # g = 1, r <= 256: the one-kernel small-rank forward (ragged T, a half-empty
+    # last column tile, a normalization width other than d)
+    Workload("bf16_g1_r256", 257, 448, 256, 1, "silu", "bf16"),
+    Workload("bf16_g1_r128_dnorm", 130, 192, 128, 1, "silu", "bf16", d_norm=768),
 ]
 
 
@@ -110,7 +114,7 @@ def test_backward_256_tiles_ragged():
     assert_close(host(g["dB"][0]), rb_["dB"][0], wl.dtype, "dB0")
 
 
-@pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5], SMALL[8], SMALL[9]], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5], SMALL[8], SMALL[9], SMALL[10]], ids=lambda w: w.name)
 def test_inference_forward_without_checkpoint(wl):
     inp = make_inputs(wl, seed=2, with_dy=False)
     _, _, y, h = _run_fwd(wl, inp, save_h=False)
@@ -175,10 +179,11 @@ def test_shard_seam_small(act, g, dtype):
             assert_close(host(yi), full["y"][i][:, c], dtype, "y (vs unsharded)")
 
 
-def test_exact_selection_case_bitwise():
+@pytest.mark.parametrize("T,d,r,g", [(300, 256, 64, 2), (300, 512, 256, 1)])
+def test_exact_selection_case_bitwise(T, d, r, g):
     """x in {+-1}, eps = 0, gamma = 1, one-hot A, B = A^T: the GPU output is
-    exact (identity) and equals the rounded SiLU(+-1) (SiLU), in fp32 and bf16."""
-    T, d, r, g = 300, 256, 64, 2
+    exact (identity) and equals the rounded SiLU(+-1) (SiLU), in fp32 and bf16
+    (g = 1 in bf16 runs the one-kernel small-rank forward)."""
     rng = np.random.default_rng(0)
     x = np.where(rng.random((T, d)) < 0.5, -1.0, 1.0)
     sel = rng.permutation(d)[: g * r]
@@ -244,7 +249,8 @@ def test_status_on_bad_call_launches_nothing():
 
 
 # ------------------------------------------------------------------ full-size shapes
-FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r256", "vanilla_tp_shard"]
+FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r128", "small_r256",
+            "vanilla_tp_shard"]
 
 
 def _sample_rows(T, n=192, seed=0):
