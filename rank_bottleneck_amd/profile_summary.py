@@ -22,9 +22,10 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
-                  "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h"]
+                  "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h",
+                  "rank_bottleneck_amd/csrc/lr_fused.hip"]
 COPY_BYTES = 256 << 20
-SHORT = [("k_wgrad_sk_reduce", "wgrad_reduce"), ("k_wgrad_reduce", "wgrad_reduce"), ("k_wgrad", "wgrad"), ("k_down", "down"), ("k_up", "up"),
+SHORT = [("k_fused_fwd", "fused"), ("k_fold_fused", "fold_gamma"), ("k_wgrad_sk_reduce", "wgrad_reduce"), ("k_wgrad_reduce", "wgrad_reduce"), ("k_wgrad", "wgrad"), ("k_down", "down"), ("k_up", "up"),
          ("k_dz", "dz"), ("k_dx", "dx"), ("k_rms_stats", "rms_stats"), ("k_fold_gamma", "fold_gamma"),
          ("k_sum_parts", "sum_parts"), ("k_finish", "finish")]
 
