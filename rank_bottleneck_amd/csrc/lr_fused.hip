@@ -13,9 +13,10 @@
 // after issuing output stores also waits for those stores.
 //   MMA waves (0-3): all global loads (x and A' tiles by DMA into LDS in phase 1;
 //     B fragments straight into registers in phase 3) and the MFMAs.
-//   store waves (4-7): the row sum of squares (phase 1, from the x tiles in LDS),
-//     h and z (phase 2), and the y stores (phase 3, from bf16 tiles the MMA waves
-//     stage in LDS, double-buffered).  They issue no global loads.
+//   store waves (4-7): h and z (phase 2) and the y stores (phase 3, from bf16
+//     tiles the MMA waves stage in LDS, double-buffered).  They issue no global
+//     loads; in phase 1 they only keep the barrier count.
+// The row sum of squares comes from the x fragments of the MMA waves.
 // Both roles run the same sequence of barriers (one per k step of phase 1, one
 // per column tile of phase 3, and the phase boundaries), with every branch on
 // the role inside a barrier interval.
@@ -132,23 +133,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int s = 0; s < C1::KS; ++s) {
         const uint4 fa = frag<C1, G::BM, false>(ta, wm * 32, s, lane);
+        // row sum of squares from the x fragments (lane l: row l%32, half l/32
+        // of the k values); the wn = 0 waves publish it
+        ss = frag_sumsq(fa, ss);
 #pragma unroll
         for (int nb = 0; nb < C1::NB; ++nb) {
           const uint4 fb = frag<C1, GR, false>(tb, wn * C1::WTN + nb * 32, s, lane);
           mfma_chunk(acc1[nb], fb, fa, (bf16*)nullptr);
         }
-      }
-    } else {
-      // sum of squares of row u/4 over this stage: 4 lanes per row, each a
-      // quarter of the row's 16-byte chunks (their order within the row does
-      // not matter for the sum)
-      constexpr int RB = C1::BK * 2, CPL = RB / 16 / 4;
-      const char LR_LDS* rp = ta + (u >> 2) * RB + (u & 3) * CPL * 16;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        const uint4 q = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4 LR_LDS*>(rp + c * 16));
-        ss = frag_sumsq(q, ss);
       }
     }
   }
@@ -171,10 +163,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const f4 v = {acc1[nb][4 * q], acc1[nb][4 * q + 1], acc1[nb][4 * q + 2], acc1[nb][4 * q + 3]};
         *reinterpret_cast<f4 LR_LDS*>(rowp + (wn * C1::WTN + nb * 32 + 8 * q) * 4) = v;
       }
-  } else {
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
-    if ((u & 3) == 0) rowss[u >> 2] = __builtin_amdgcn_rsqf(ss * a.invD + a.eps);
+    ss += __shfl_xor(ss, 32);
+    if (wn == 0 && lane < 32) rowss[wm * 32 + lane] = __builtin_amdgcn_rsqf(ss * a.invD + a.eps);
   }
   lgkm_wait0();
   block_barrier();
