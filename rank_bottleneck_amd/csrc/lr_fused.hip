@@ -43,8 +43,16 @@ struct FusedGeo {
   static constexpr int BM = 64;
   static constexpr int BK1 = GR == 256 ? 32 : 64;
   static constexpr int S1 = GR == 64 ? 8 : (GR == 128 ? 6 : 7);
-  // phase 1 tile [BM, GR]: MMA waves 2 x 2, wave tile 32 x GR/2
+  // phase 1 tile [BM, GR].  Up to r = 128 (k split): each MMA wave the whole
+  // tile over one of the four 16-deep k sub-steps of every stage, NSP = 4
+  // partial sums added in phase 2; every LDS fragment is read once and each wave
+  // has 4-8 independent accumulators.  r = 256: MMA waves 2 x 2, wave tile
+  // 32 x GR/2, one partial (four of 64 x 256 would not fit in LDS).
   using C1 = PipeCfg<BM, GR, BK1, 2, 2, S1>;
+  static constexpr bool KSPLIT = GR <= 128;
+  static constexpr int NSP = KSPLIT ? 4 : 1;
+  static constexpr int MB1 = KSPLIT ? 2 : 1, NB1 = KSPLIT ? GR / 32 : C1::NB;
+  static_assert(!KSPLIT || C1::KS == 4, "one k sub-step per MMA wave");
   // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of 32
   // columns; the B fragments of PF column tiles ahead in flight (register
   // buffers NBUF = PF + 1), 48-64 KB per CU
@@ -58,14 +66,14 @@ struct FusedGeo {
   static constexpr int P1 = S1 * C1::STAGE_BYTES + C1::SINK_BYTES;
   static constexpr int ZT = BM * 128;                  // one [BM][64] bf16 z tile
   static constexpr int ZB = KT * ZT;
-  static constexpr int ROWSS = ZB;
-  static constexpr int STG = ZB + 256;
+  static constexpr int ROWSS = ZB;                     // NSP x BM partial sums of squares
+  static constexpr int STG = ZB + 4 * BM * 4;
   static constexpr int STG2_PITCH = GR * 4 + 16;       // fp32 h row + pad
   static constexpr int STG2_BYTES = BM * STG2_PITCH;
   static constexpr int STG3_PITCH = BN3 * 2 + 16;      // bf16 y row + pad
   static constexpr int STG3_BUF = BM * STG3_PITCH;
   static constexpr int P3 = STG + 2 * STG3_BUF;
-  static constexpr int P2 = STG + STG2_BYTES;
+  static constexpr int P2 = STG + NSP * STG2_BYTES;
   static constexpr int LDS = P1 > P3 ? (P1 > P2 ? P1 : P2) : (P3 > P2 ? P3 : P2);
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(GR % 64 == 0 && GR <= 256, "rank");
@@ -95,12 +103,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---------------------------------------------------------------- phase 1: acc1 = x . A'
   const int nk1 = d / C1::BK;
-  f32x16 acc1[C1::NB];
+  constexpr int MB1 = G::MB1, NB1 = G::NB1;
+  f32x16 acc1[MB1][NB1];
 #pragma unroll
-  for (int nb = 0; nb < C1::NB; ++nb)
+  for (int mb = 0; mb < MB1; ++mb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc1[nb][v] = 0.f;
-  float ss = 0.f;
+    for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc1[mb][nb][v] = 0.f;
+  // row sums of squares from the x fragments (lane l: row l%32, half l/32 of
+  // the fragment's k values)
+  float ss[MB1];
+#pragma unroll
+  for (int mb = 0; mb < MB1; ++mb) ss[mb] = 0.f;
 
   DmaTile<C1, G::BM, false> dxt;
   DmaTile<C1, GR, false> dat;
@@ -130,16 +145,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (mma) {
       issue1(kt + G::S1 - 1);
       const char LR_LDS* tb = ta + C1::A_BYTES;
+      if constexpr (G::KSPLIT) {
+        // sub-step w of the stage, all BM rows and GR columns
+        uint4 fa[MB1], fb[NB1];
 #pragma unroll
-      for (int s = 0; s < C1::KS; ++s) {
-        const uint4 fa = frag<C1, G::BM, false>(ta, wm * 32, s, lane);
-        // row sum of squares from the x fragments (lane l: row l%32, half l/32
-        // of the k values); the wn = 0 waves publish it
-        ss = frag_sumsq(fa, ss);
+        for (int mb = 0; mb < MB1; ++mb) fa[mb] = frag<C1, G::BM, false>(ta, mb * 32, w, lane);
 #pragma unroll
-        for (int nb = 0; nb < C1::NB; ++nb) {
-          const uint4 fb = frag<C1, GR, false>(tb, wn * C1::WTN + nb * 32, s, lane);
-          mfma_chunk(acc1[nb], fb, fa, (bf16*)nullptr);
+        for (int nb = 0; nb < NB1; ++nb) fb[nb] = frag<C1, GR, false>(tb, nb * 32, w, lane);
+#pragma unroll
+        for (int mb = 0; mb < MB1; ++mb) {
+          ss[mb] = frag_sumsq(fa[mb], ss[mb]);
+#pragma unroll
+          for (int nb = 0; nb < NB1; ++nb) mfma_chunk(acc1[mb][nb], fb[nb], fa[mb], (bf16*)nullptr);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < C1::KS; ++s) {
+          const uint4 fa = frag<C1, G::BM, false>(ta, wm * 32, s, lane);
+          ss[0] = frag_sumsq(fa, ss[0]);
+#pragma unroll
+          for (int nb = 0; nb < NB1; ++nb) {
+            const uint4 fb = frag<C1, GR, false>(tb, wn * C1::WTN + nb * 32, s, lane);
+            mfma_chunk(acc1[0][nb], fb, fa, (bf16*)nullptr);
+          }
         }
       }
     }
@@ -149,22 +177,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   block_barrier();  // the ring is dead from here on
 
   // ---------------------------------------------------------------- phase 2: h, z
-  float LR_LDS* rowss = reinterpret_cast<float LR_LDS*>(ldsp + G::ROWSS);
+  // NSP fp32 partials of x . A' ([BM][GR] each, padded rows) and NSP x BM
+  // partial sums of squares; the store role adds them in partial order
+  float LR_LDS* ssp = reinterpret_cast<float LR_LDS*>(ldsp + G::ROWSS);
   char LR_LDS* stg = ldsp + G::STG;
   if (mma) {
-    // lane l holds row l%32 of its 32-row block, columns 8q + 4(l/32) + 0..3 of
+    // lane l holds row l%32 of each 32-row block, columns 8q + 4(l/32) + 0..3 of
     // each 32-column block nb (the swapped operand order of mfma_chunk)
     typedef float f4 __attribute__((ext_vector_type(4)));
-    char LR_LDS* rowp = stg + (wm * 32 + (lane & 31)) * G::STG2_PITCH + 16 * (lane >> 5);
+    const int part = G::KSPLIT ? w : 0, r0 = G::KSPLIT ? 0 : wm * 32, c0 = G::KSPLIT ? 0 : wn * C1::WTN;
 #pragma unroll
-    for (int nb = 0; nb < C1::NB; ++nb)
+    for (int mb = 0; mb < MB1; ++mb) {
+      char LR_LDS* rowp =
+          stg + part * G::STG2_BYTES + (r0 + mb * 32 + (lane & 31)) * G::STG2_PITCH + 16 * (lane >> 5);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 v = {acc1[nb][4 * q], acc1[nb][4 * q + 1], acc1[nb][4 * q + 2], acc1[nb][4 * q + 3]};
-        *reinterpret_cast<f4 LR_LDS*>(rowp + (wn * C1::WTN + nb * 32 + 8 * q) * 4) = v;
-      }
-    ss += __shfl_xor(ss, 32);
-    if (wn == 0 && lane < 32) rowss[wm * 32 + lane] = __builtin_amdgcn_rsqf(ss * a.invD + a.eps);
+      for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f4 v = {acc1[mb][nb][4 * q], acc1[mb][nb][4 * q + 1], acc1[mb][nb][4 * q + 2],
+                        acc1[mb][nb][4 * q + 3]};
+          *reinterpret_cast<f4 LR_LDS*>(rowp + (c0 + nb * 32 + 8 * q) * 4) = v;
+        }
+      ss[mb] += __shfl_xor(ss[mb], 32);
+      if ((G::KSPLIT || wn == 0) && lane < 32) ssp[part * G::BM + r0 + mb * 32 + lane] = ss[mb];
+    }
   }
   lgkm_wait0();
   block_barrier();
@@ -178,8 +214,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll 4
     for (int p = 0; p < G::BM / RPI; ++p) {
       const int rl = p * RPI + u / LPR;
-      const float4 v = lds_f4(stg + rl * G::STG2_PITCH + c * 4);
-      const float rs = rowss[rl];
+      float4 v = lds_f4(stg + rl * G::STG2_PITCH + c * 4);
+      float ssr = ssp[rl];
+#pragma unroll
+      for (int pp = 1; pp < G::NSP; ++pp) {
+        const float4 v2 = lds_f4(stg + pp * G::STG2_BYTES + rl * G::STG2_PITCH + c * 4);
+        v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+        ssr += ssp[pp * G::BM + rl];
+      }
+      const float rs = __builtin_amdgcn_rsqf(ssr * a.invD + a.eps);
       float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
       if (h && m0 + rl < a.T) store4(h + (int64_t)(m0 + rl) * GR + c, hv[0], hv[1], hv[2], hv[3]);
       if constexpr (ACT == ACT_SILU) {
@@ -192,7 +235,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   lgkm_wait0();
-  block_barrier();  // z complete; the h staging and rstd are dead
+  block_barrier();  // z complete; the h staging and the sums of squares are dead
 
   // ---------------------------------------------------------------- phase 3: y = z . B
   const int nt_count = (d + G::BN3 - 1) / G::BN3;
