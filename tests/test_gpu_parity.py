@@ -124,6 +124,24 @@ def test_inference_forward_without_checkpoint(wl):
         assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
 
 
+@pytest.mark.parametrize("T,d,r,act", [(1, 64, 64, "silu"), (63, 128, 128, "identity"), (65, 192, 256, "silu"),
+                                        (64, 64, 256, "identity"), (129, 128, 64, "silu")])
+def test_fused_forward_edges(T, d, r, act):
+    """The one-kernel small-rank forward at its edges: a single token, a partly
+    filled last row block, widths where every column tile past the first is
+    padding (d = 64, 128) or half filled (d = 192), with and without the
+    checkpoint."""
+    wl = Workload("fused_edge", T, d, r, 1, act, "bf16")
+    _say("fused edge", wl)
+    inp = make_inputs(wl, seed=6, with_dy=False)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], r, 1, act, wl.eps, wl.D)
+    for save_h in (True, False):
+        _, _, y, h = _run_fwd(wl, inp, save_h=save_h)
+        if save_h:
+            assert_close(host(h), ref["h"], "bf16", "h")
+        assert_close(host(y[0]), ref["y"][0], "bf16", "y0")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_rmsnorm_online(dtype):
     wl = Workload("rms", 1111, 4096, 64, 1, "silu", dtype)
