@@ -3,6 +3,13 @@
     python -m rank_bottleneck_amd.profile_summary stats  <kernel_stats.csv> <out.md> --title T --command C
     python -m rank_bottleneck_amd.profile_summary traffic <fetch_counter_collection.csv> <write_counter_collection.csv>
            --workload W --out profiles/traffic.json --command C
+    python -m rank_bottleneck_amd.profile_summary mfma <counter_collection.csv> <out.md> --title T --command C
+
+`mfma` summarises one `--pmc MfmaUtil MfmaFlopsBF16` pass per kernel: the MFMA
+busy fraction (MFMA busy cycles over active cycles times SIMDs), the bf16 MFMA
+FLOPs the hardware counted (MFMA ops x 512), the rate those FLOPs give over the
+dispatch's duration, and the shader clock that rate and busy fraction imply
+(1024 SIMDs x 1024 dense bf16 FLOP per clock each at full MFMA occupancy).
 
 `traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel into
 HBM bytes per launch.  Each counter is scaled by the factor that makes the same
@@ -88,9 +95,35 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, out: str, command: st
     return summary
 
 
+def mfma(csv_path: str, out: str, title: str, command: str) -> None:
+    util, flops, dur = defaultdict(list), defaultdict(list), defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        k = short_name(r["Kernel_Name"])
+        if k == r["Kernel_Name"]:
+            continue
+        v = float(r["Counter_Value"])
+        if r["Counter_Name"] == "MfmaUtil":
+            util[k].append(v)
+            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        elif r["Counter_Name"] == "MfmaFlopsBF16":
+            flops[k].append(v)
+    with open(out, "w") as f:
+        f.write(f"# {title}\n\nCommand (repository root, one MI355X):\n\n```\n{command}\n```\n\n")
+        f.write("Medians over the profiled launches (kernels run one at a time under counter collection).\n\n")
+        f.write("| kernel | MFMA util % | bf16 MFMA GFLOP / launch | duration us | TFLOP/s | % of 2.5 PF | implied clock GHz |\n")
+        f.write("|---|---|---|---|---|---|---|\n")
+        for k in sorted(util, key=lambda k: -statistics.median(dur[k])):
+            u, t = statistics.median(util[k]), statistics.median(dur[k])
+            fl = statistics.median(flops[k]) if flops.get(k) else 0.0
+            rate = fl / t / 1e12 if t > 0 else 0.0
+            clk = rate * 1e12 / (1024 * 1024 * (u / 100.0)) / 1e9 if u > 0 else 0.0
+            f.write(f"| {k} | {u:.1f} | {fl / 1e9:.2f} | {t * 1e6:.1f} | {rate:.0f} | {100 * rate / 2500:.1f} | "
+                    f"{clk:.2f} |\n")
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["stats", "traffic"])
+    ap.add_argument("mode", choices=["stats", "traffic", "mfma"])
     ap.add_argument("inputs", nargs="+")
     ap.add_argument("--title", default="kernel statistics")
     ap.add_argument("--command", default="")
@@ -99,6 +132,8 @@ if __name__ == "__main__":
     a = ap.parse_args()
     if a.mode == "stats":
         stats(a.inputs[0], a.inputs[1], a.title, a.command)
+    elif a.mode == "mfma":
+        mfma(a.inputs[0], a.inputs[1], a.title, a.command)
     else:
         s = traffic(a.inputs[0], a.inputs[1], a.workload, a.out, a.command)
         for k, (fb, wb) in sorted(s.items()):
