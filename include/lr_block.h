@@ -91,7 +91,10 @@ lr_status rmsnorm_online(const lr_dims* dims, const void* x, const void* gamma, 
  *   y[i] [T, d]  for i < n_up                                (dtype)
  *   h_save [T, g*r] (dtype): the rank-r pre-activation h, the only activation the
  *   backward needs besides x (low-rank activation checkpointing, §2.2).  NULL for
- *   inference. */
+ *   inference.
+ * For bf16 with g == 1, r in {64, 128, 256} and identity or SiLU, the forward is
+ * one kernel and z never reaches device memory; otherwise z is written once to
+ * the workspace between the two projections. */
 lr_status lr_block_fwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
                        const void* const* B, void* const* y, void* h_save,
                        void* ws, size_t ws_bytes, hipStream_t stream);
@@ -135,8 +138,9 @@ size_t lr_block_workspace_size(const lr_dims* dims, int backward);
  * Between lr_trace_begin and lr_trace_end, every kernel that an entry point
  * launches from the CALLING THREAD whose name matches `kernel` (NULL: all) is
  * bracketed by two hipEvents recorded on the launch stream, up to
- * `max_launches` launches.  Kernel names: "fold_gamma", "down", "up", "finish",
- * "rms_stats", "dz", "wgrad", "wgrad_reduce", "sum_parts", "dx".  This
+ * `max_launches` launches.  Kernel names: "fold_gamma" (every weight fold),
+ * "down", "up", "fused" (the one-kernel forward), "finish", "rms_stats", "dz",
+ * "wgrad", "wgrad_reduce", "sum_parts", "dx".  This
  * per-thread trace is the only state the library keeps between calls; it owns
  * its events.
  *   lr_trace_begin: LR_EINVAL if max_launches < 1 or a trace is already active,
