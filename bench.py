@@ -68,9 +68,10 @@ def kernel_work(wl, name: str):
         return 0.0, 4 * (d * gr + nu * r * d)
     if name == "dx":
         return 2.0 * T * gr * d, e * (T * gr + d * gr + 2 * T * d) + 4 * T
-    if name == "fold_gamma":   # the one-kernel small-rank path also transposes B
-        fused = wl.dtype == "bf16" and g == 1 and r in (64, 128, 256) and wl.act != "swiglu" and not wl.seam
-        return 0.0, e * ((4 if fused else 2) * d * gr + d)
+    if name == "fold_gamma":   # the one-kernel small-rank path also reorders B
+        fused = wl.dtype == "bf16" and not wl.seam and (
+            (g == 1 and r in (64, 128, 256) and wl.act != "swiglu") or (wl.act == "swiglu" and r in (64, 128)))
+        return 0.0, e * (2 * d * gr + d + (2 * nu * r * d if fused else 0))
     if name == "rms_stats":
         return 0.0, e * T * d + 4 * T
     if name == "finish":

@@ -1,5 +1,7 @@
-// Small-rank forward of the block in one kernel (g = 1, g*r in {64, 128, 256}):
-//   h = diag(rstd) . ((x (.) gamma) . A),  z = sigma(h),  y = z . B
+// Small-rank forward of the block in one kernel (g = 1, r in {64, 128, 256}, and
+// SwiGLU's grouped gate/up pair, g = 2, r in {64, 128}):
+//   h = diag(rstd) . ((x (.) gamma) . A),  z = sigma(h) (SwiGLU: SiLU(h_gate) * h_up),
+//   y = z . B
 // BOOST's low-rank layer pairs a d x r and an r x d projection with the
 // operations between them (summary, section 2.1) and normalizes with statistics
 // accumulated alongside the projection (section 2.2, Online RMSNorm).  At small r
@@ -38,7 +40,9 @@
 
 namespace lr {
 
-template <int GR>
+// GR = g*r columns of h (phase 1), K3 = rows of B, the up-projection's depth
+// (r; GR for g = 1)
+template <int GR, int K3>
 struct FusedGeo {
   static constexpr int BM = 64;
   static constexpr int BK1 = GR == 256 ? 32 : 64;
@@ -57,10 +61,10 @@ struct FusedGeo {
   // columns; the B fragments of PF column tiles ahead in flight (register
   // buffers NBUF = PF + 1), 48-64 KB per CU
   static constexpr int BN3 = 128;
-  static constexpr int PF = GR == 64 ? 3 : (GR == 128 ? 2 : 1);
+  static constexpr int PF = K3 == 64 ? 3 : (K3 == 128 ? 2 : 1);
   static constexpr int NBUF = PF + 1;
   using C3 = PipeCfg<BM, 128, 64, 2, 2, 2>;  // z fragment geometry (BK = 64)
-  static constexpr int KT = GR / 64;  // 64-deep k blocks of z
+  static constexpr int KT = K3 / 64;  // 64-deep k blocks of z
   static constexpr int THREADS = 512;
 
   static constexpr int P1 = S1 * C1::STAGE_BYTES + C1::SINK_BYTES;
@@ -76,7 +80,7 @@ struct FusedGeo {
   static constexpr int P2 = STG + NSP * STG2_BYTES;
   static constexpr int LDS = P1 > P3 ? (P1 > P2 ? P1 : P2) : (P3 > P2 ? P3 : P2);
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(GR % 64 == 0 && GR <= 256, "rank");
+  static_assert(GR % 64 == 0 && GR <= 256 && K3 % 64 == 0 && K3 <= GR, "rank");
   static constexpr int Q1X = DmaTile<C1, BM, false>::Q, Q1A = DmaTile<C1, GR, false>::Q;
   static_assert((S1 - 2) * (Q1X + Q1A) <= 63, "vmcnt range");
 };
@@ -85,7 +89,9 @@ __device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0
 
 template <int GR, int ACT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fused_fwd(FusedArgs a) {
-  using G = FusedGeo<GR>;
+  constexpr bool SW = ACT == ACT_SWIGLU;
+  constexpr int K3 = SW ? GR / 2 : GR;  // z columns: gate and up pair up in SwiGLU
+  using G = FusedGeo<GR, K3>;
   using C1 = typename G::C1;
   using C3 = typename G::C3;
   __shared__ uint4 lds[G::LDS / 16];
@@ -205,7 +211,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lgkm_wait0();
   block_barrier();
   if (!mma) {
-    constexpr int LPR = GR / 4, RPI = 256 / LPR;
+    // each lane 4 consecutive z columns of a row (SwiGLU: gate columns c.. and
+    // the up columns K3 + c..)
+    constexpr int LPR = K3 / 4, RPI = 256 / LPR;
     bf16* h = static_cast<bf16*>(a.h);
     const int c = (u % LPR) * 4;
     // z tile of column c: [BM][64] K-contiguous, 16-byte chunks swizzled as the
@@ -214,20 +222,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll 4
     for (int p = 0; p < G::BM / RPI; ++p) {
       const int rl = p * RPI + u / LPR;
-      float4 v = lds_f4(stg + rl * G::STG2_PITCH + c * 4);
+      // x . A' at (rl, col): the NSP partials added in order
+      auto acc_at = [&](int col) {
+        float4 v = lds_f4(stg + rl * G::STG2_PITCH + col * 4);
+#pragma unroll
+        for (int pp = 1; pp < G::NSP; ++pp) {
+          const float4 v2 = lds_f4(stg + pp * G::STG2_BYTES + rl * G::STG2_PITCH + col * 4);
+          v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+        }
+        return v;
+      };
       float ssr = ssp[rl];
 #pragma unroll
-      for (int pp = 1; pp < G::NSP; ++pp) {
-        const float4 v2 = lds_f4(stg + pp * G::STG2_BYTES + rl * G::STG2_PITCH + c * 4);
-        v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
-        ssr += ssp[pp * G::BM + rl];
-      }
+      for (int pp = 1; pp < G::NSP; ++pp) ssr += ssp[pp * G::BM + rl];
       const float rs = __builtin_amdgcn_rsqf(ssr * a.invD + a.eps);
+      const float4 v = acc_at(c);
       float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
-      if (h && m0 + rl < a.T) store4(h + (int64_t)(m0 + rl) * GR + c, hv[0], hv[1], hv[2], hv[3]);
-      if constexpr (ACT == ACT_SILU) {
+      const bool keep = h && m0 + rl < a.T;
+      if (keep) store4(h + (int64_t)(m0 + rl) * GR + c, hv[0], hv[1], hv[2], hv[3]);
+      if constexpr (ACT == ACT_SILU || SW) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) hv[e] = hv[e] * sigmoidf_(hv[e]);
+      }
+      if constexpr (SW) {
+        const float4 w4 = acc_at(K3 + c);
+        const float hu[4] = {w4.x * rs, w4.y * rs, w4.z * rs, w4.w * rs};
+        if (keep) store4(h + (int64_t)(m0 + rl) * GR + K3 + c, hu[0], hu[1], hu[2], hu[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] *= hu[e];
       }
       const bf16x4 zv = {(bf16)hv[0], (bf16)hv[1], (bf16)hv[2], (bf16)hv[3]};
       const int slot = (kk / 8) ^ kc_swz<128>(rl);
@@ -243,18 +265,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   // z fragments (both 32-row blocks) in registers up to r = 128; at r = 256 they
   // are read from LDS (z stays there through phase 3) to leave registers for B
-  constexpr bool ZREG = GR <= 128;
+  constexpr bool ZREG = K3 <= 128;
   uint4 zf[ZREG ? 2 : 1][ZREG ? G::KT : 1][4];
   f32x16 acc3[2];
   uint4 bb[G::NBUF][G::KT][4];
   const bf16* Bf = static_cast<const bf16*>(a.Bf);
   // B fragments of this wave's 32 columns of column tile nt: fragment (column
-  // block cb, k16 block kb) starts at element ((cb * GR/16 + kb) * 64) * 8; a
+  // block cb, k16 block kb) starts at element ((cb * K3/16 + kb) * 64) * 8; a
   // column block past d (the last tile's upper half when d is an odd multiple of
   // 64) reads the last one and feeds y columns that are never stored
   auto load_b = [&](int nt, uint4 (&bf)[G::KT][4]) {
     const int cb = min(nt * (G::BN3 / 32) + w, d / 32 - 1);
-    const bf16* fp = Bf + ((int64_t)cb * (GR / 16) * 64 + lane) * 8;
+    const bf16* fp = Bf + ((int64_t)cb * (K3 / 16) * 64 + lane) * 8;
 #pragma unroll
     for (int kt = 0; kt < G::KT; ++kt)
 #pragma unroll
@@ -352,30 +374,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// A'^T = (diag(gamma) A)^T [n, d] for A [d, n], and B [n, d] in MFMA fragment
+// A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and B [nb, d] in MFMA fragment
 // order, in one launch; one thread per 16-byte output chunk (8 elements), the
-// first n*d/8 threads for A'^T, the rest for B.
-//   A'^T chunk t: column c = t % n of A, rows j0 = 8 (t / n) .. +7 (lanes read
+// first na*d/8 threads for A'^T, the next nb*d/8 for B.
+//   A'^T chunk t: column c = t % na of A, rows j0 = 8 (t / na) .. +7 (lanes read
 //     consecutive columns of a row).
-//   B chunk t: fragment f = t / 64 = cb * (n/16) + kb, lane l = t % 64: column
+//   B chunk t: fragment f = t / 64 = cb * (nb/16) + kb, lane l = t % 64: column
 //     32 cb + l%32, k values 16 kb + 8(l/32) .. +7.
 __global__ __launch_bounds__(256) void k_fold_fused(const bf16* __restrict__ A, const bf16* __restrict__ gamma,
                                                     const bf16* __restrict__ B, bf16* __restrict__ Apt,
-                                                    bf16* __restrict__ Bf, int d, int n) {
+                                                    bf16* __restrict__ Bf, int d, int na, int nb) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t chunks = (int64_t)n * d / 8;
+  const int64_t ca = (int64_t)na * d / 8, cbn = (int64_t)nb * d / 8;
   bf16x8 v;
-  if (t < chunks) {
-    const int c = (int)(t % n), j0 = (int)(t / n) * 8;
+  if (t < ca) {
+    const int c = (int)(t % na), j0 = (int)(t / na) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)A[(int64_t)(j0 + i) * n + c] * (float)gamma[j0 + i]);
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)A[(int64_t)(j0 + i) * na + c] * (float)gamma[j0 + i]);
     *reinterpret_cast<bf16x8*>(Apt + (int64_t)c * d + j0) = v;
-  } else if (t < 2 * chunks) {
-    const int64_t tb = t - chunks;
+  } else if (t < ca + cbn) {
+    const int64_t tb = t - ca;
     const int l = (int)(tb % 64);
     const int64_t f = tb / 64;
-    const int kb = (int)(f % (n / 16)), cb = (int)(f / (n / 16));
+    const int kb = (int)(f % (nb / 16)), cb = (int)(f / (nb / 16));
     const int col = cb * 32 + (l & 31), k0 = kb * 16 + 8 * (l >> 5);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = B[(int64_t)(k0 + i) * d + col];
@@ -383,12 +405,12 @@ __global__ __launch_bounds__(256) void k_fold_fused(const bf16* __restrict__ A, 
   }
 }
 
-hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int n,
-                             hipStream_t s) {
-  const int64_t chunks = (int64_t)n * d / 8;
-  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)((2 * chunks + 255) / 256)), dim3(256), 0, s,
+hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int na,
+                             int nb, hipStream_t s) {
+  const int64_t chunks = ((int64_t)na + nb) * d / 8;
+  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16*>(A), static_cast<const bf16*>(gamma), static_cast<const bf16*>(B),
-                     static_cast<bf16*>(Apt), static_cast<bf16*>(Bf), d, n);
+                     static_cast<bf16*>(Apt), static_cast<bf16*>(Bf), d, na, nb);
   return hipGetLastError();
 }
 
@@ -399,12 +421,15 @@ static hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
 }
 
 bool fused_fwd_supported(int r, int g, int act) {
+  if (act == ACT_SWIGLU) return g == 2 && (r == 64 || r == 128);
   return g == 1 && (r == 64 || r == 128 || r == 256) && (act == ACT_IDENTITY || act == ACT_SILU);
 }
 
 hipError_t launch_fused_fwd(const FusedArgs& a, int act, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (!fused_fwd_supported(a.r, 1, act)) return hipErrorInvalidValue;
+  if (!fused_fwd_supported(a.r, act == ACT_SWIGLU ? 2 : 1, act)) return hipErrorInvalidValue;
+  if (act == ACT_SWIGLU)
+    return a.r == 64 ? launch_fused_g<128, ACT_SWIGLU>(a, s) : launch_fused_g<256, ACT_SWIGLU>(a, s);
   const bool silu = act == ACT_SILU;
   switch (a.r) {
     case 64: return silu ? launch_fused_g<64, ACT_SILU>(a, s) : launch_fused_g<64, ACT_IDENTITY>(a, s);

@@ -34,13 +34,14 @@ struct SplitDownArgs {
   float* sumsq;       // [nsplit][T]
 };
 
-// Small-rank forward in one kernel (g = 1): x, A'^T [r, d] (gamma folded in), B [r, d]
+// Small-rank forward in one kernel (g = 1, or SwiGLU's g = 2): x, A'^T [g*r, d]
+// (gamma folded in), B [r, d]
 struct FusedArgs {
   const void* x;      // [T, d]
-  const void* Apt;    // [r, d]: (diag(gamma) A)^T, K-contiguous
+  const void* Apt;    // [g*r, d]: (diag(gamma) A)^T, K-contiguous
   const void* Bf;     // B [r, d] in MFMA fragment order (launch_fold_fused)
   void* y;            // [T, d]
-  void* h;            // [T, r] or null
+  void* h;            // [T, g*r] or null
   int T, d, r;
   float invD, eps;
 };
@@ -132,10 +133,10 @@ template <typename E> hipError_t launch_down_split(const SplitDownArgs& a, hipSt
 // whether the one-kernel small-rank forward serves these dims (bf16 only)
 bool fused_fwd_supported(int r, int g, int act);
 hipError_t launch_fused_fwd(const FusedArgs& a, int act, hipStream_t s);
-// A'^T = (diag(gamma) A)^T [n, d] for A [d, n], and B [n, d] in MFMA fragment
+// A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and B [nb, d] in MFMA fragment
 // order (fragment of 32 columns x 16 k values = 64 lanes x 8 consecutive k) (bf16)
-hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int n,
-                             hipStream_t s);
+hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int na,
+                             int nb, hipStream_t s);
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 // sums the split partials of launch_wgrad (nothing to do when nsplit == 1)

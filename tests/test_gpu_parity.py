@@ -55,6 +55,8 @@ SMALL = [
     # last column tile, a normalization width other than d)
     Workload("bf16_g1_r256", 257, 448, 256, 1, "silu", "bf16"),
     Workload("bf16_g1_r128_dnorm", 130, 192, 128, 1, "silu", "bf16", d_norm=768),
+    # SwiGLU's gate/up pair at small rank: the one-kernel forward as well
+    Workload("bf16_swiglu_r128_small", 333, 320, 128, 2, "swiglu", "bf16"),
 ]
 
 
@@ -125,16 +127,18 @@ def test_inference_forward_without_checkpoint(wl):
 
 
 @pytest.mark.parametrize("T,d,r,act", [(1, 64, 64, "silu"), (63, 128, 128, "identity"), (65, 192, 256, "silu"),
-                                        (64, 64, 256, "identity"), (129, 128, 64, "silu")])
+                                        (64, 64, 256, "identity"), (129, 128, 64, "silu"), (1, 64, 64, "swiglu"),
+                                        (97, 192, 128, "swiglu")])
 def test_fused_forward_edges(T, d, r, act):
     """The one-kernel small-rank forward at its edges: a single token, a partly
     filled last row block, widths where every column tile past the first is
     padding (d = 64, 128) or half filled (d = 192), with and without the
     checkpoint."""
-    wl = Workload("fused_edge", T, d, r, 1, act, "bf16")
+    g = 2 if act == "swiglu" else 1
+    wl = Workload("fused_edge", T, d, r, g, act, "bf16")
     _say("fused edge", wl)
     inp = make_inputs(wl, seed=6, with_dy=False)
-    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], r, 1, act, wl.eps, wl.D)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], r, g, act, wl.eps, wl.D)
     for save_h in (True, False):
         _, _, y, h = _run_fwd(wl, inp, save_h=save_h)
         if save_h:
@@ -268,7 +272,7 @@ def test_status_on_bad_call_launches_nothing():
 
 # ------------------------------------------------------------------ full-size shapes
 FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r128", "small_r256",
-            "vanilla_tp_shard"]
+            "small_swiglu_r64", "small_swiglu_r128", "vanilla_tp_shard"]
 
 
 def _sample_rows(T, n=192, seed=0):

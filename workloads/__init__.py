@@ -92,6 +92,10 @@ WORKLOADS: Dict[str, Workload] = {
 for _r in (64, 128, 256):
     WORKLOADS[f"small_r{_r}"] = Workload(f"small_r{_r}", T=16384, d=4096, r=_r, g=1, act="silu",
                                          dtype="bf16", fwd_only=True, hbm_metric=True)
+# the same sweep for a SwiGLU bottleneck: gate and up grouped (g = 2) at rank r
+for _r in (64, 128):
+    WORKLOADS[f"small_swiglu_r{_r}"] = Workload(f"small_swiglu_r{_r}", T=16384, d=4096, r=_r, g=2, act="swiglu",
+                                                dtype="bf16", fwd_only=True, hbm_metric=True)
 # contrast to btp_shard: the same d=8192, r=2048 block under vanilla low-rank TP=4
 WORKLOADS["vanilla_tp_shard"] = Workload(
     "vanilla_tp_shard", T=8192, d=8192, r=512, g=1, act="silu", dtype="bf16", fwd_only=True,
