@@ -43,6 +43,16 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def one_kernel_forward(wl) -> bool:
+    """Whether the library runs this workload's forward as its one-kernel
+    small-rank path (the shapes it documents for that path)."""
+    if wl.dtype != "bf16" or wl.seam:
+        return False
+    if wl.act == "swiglu":
+        return wl.g == 2 and wl.r in (64, 128)
+    return (wl.r == 64 and wl.g <= 4) or (wl.r == 128 and wl.g <= 2) or (wl.r == 256 and wl.g == 1)
+
+
 def kernel_work(wl, name: str):
     """Algorithmic (flops, HBM bytes) of one launch of kernel `name`: every
     operand read once and every result written once; GEMM flops only."""
@@ -69,9 +79,7 @@ def kernel_work(wl, name: str):
     if name == "dx":
         return 2.0 * T * gr * d, e * (T * gr + d * gr + 2 * T * d) + 4 * T
     if name == "fold_gamma":   # the one-kernel small-rank path also reorders B
-        fused = wl.dtype == "bf16" and not wl.seam and (
-            (g == 1 and r in (64, 128, 256) and wl.act != "swiglu") or (wl.act == "swiglu" and r in (64, 128)))
-        return 0.0, e * (2 * d * gr + d + (2 * nu * r * d if fused else 0))
+        return 0.0, e * (2 * d * gr + d + (2 * nu * r * d if one_kernel_forward(wl) else 0))
     if name == "rms_stats":
         return 0.0, e * T * d + 4 * T
     if name == "finish":

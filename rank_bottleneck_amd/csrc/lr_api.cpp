@@ -125,13 +125,14 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
   if (fused_fwd(d)) {
-    // small rank, g = 1 or SwiGLU's pair: x . A', deferred rstd, sigma and the
-    // up-projection in one kernel; z stays in LDS
+    // small g*r: x . A', deferred rstd, sigma and the up-projections in one
+    // kernel; z stays in LDS
     void* Bf = cv.take<void>((size_t)D * gr * sizeof(E));
-    LR_LAUNCH("fold_gamma", s, lr::launch_fold_fused(A, gamma, B[0], Ap, Bf, D, gr, r, s));
+    LR_LAUNCH("fold_gamma", s, lr::launch_fold_fused(A, gamma, B, n_up, Ap, Bf, D, gr, r, s));
     lr::FusedArgs fa{};
-    fa.x = x; fa.Apt = Ap; fa.Bf = Bf; fa.y = y[0]; fa.h = h_save;
-    fa.T = T; fa.d = D; fa.r = r; fa.invD = inv_width(d); fa.eps = d->eps;
+    fa.x = x; fa.Apt = Ap; fa.Bf = Bf; fa.h = h_save;
+    for (int i = 0; i < n_up; ++i) fa.y[i] = y[i];
+    fa.T = T; fa.d = D; fa.r = r; fa.g = g; fa.invD = inv_width(d); fa.eps = d->eps;
     LR_LAUNCH("fused", s, lr::launch_fused_fwd(fa, d->act, s));
     return LR_OK;
   }

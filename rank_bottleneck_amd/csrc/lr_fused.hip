@@ -1,7 +1,8 @@
-// Small-rank forward of the block in one kernel (g = 1, r in {64, 128, 256}, and
-// SwiGLU's grouped gate/up pair, g = 2, r in {64, 128}):
-//   h = diag(rstd) . ((x (.) gamma) . A),  z = sigma(h) (SwiGLU: SiLU(h_gate) * h_up),
-//   y = z . B
+// Small-rank forward of the block in one kernel (bf16, g*r <= 256: r = 64 with
+// g <= 4, r = 128 with g <= 2, r = 256 with g = 1; SwiGLU's gate/up pair at
+// r = 64, 128):
+//   h = diag(rstd) . ((x (.) gamma) . A),  z_i = sigma(h_i) (SwiGLU: SiLU(h_gate) * h_up),
+//   y_i = z_i . B_i
 // BOOST's low-rank layer pairs a d x r and an r x d projection with the
 // operations between them (summary, section 2.1) and normalizes with statistics
 // accumulated alongside the projection (section 2.2, Online RMSNorm).  At small r
@@ -32,26 +33,26 @@
 //
 // LDS (bytes from 0):
 //   phase 1: ring of S1 stages [x tile | A'^T tile] and the sink of dead stages;
-//   phases 2-3 (after the ring is drained): z as KT tiles of [BM][64] (K
-//     contiguous, swizzled as an MFMA A tile), BM floats of rstd, then the fp32
-//     staging of h (phase 2) or two bf16 y tiles (phase 3).
+//   phases 2-3 (after the ring is drained): z as [BM][64] tiles (K contiguous,
+//     swizzled as an MFMA A tile), the partial row sums of squares, then the
+//     fp32 staging of h (phase 2) or two bf16 y tiles (phase 3).
 #include "lr_kernels.h"
 #include "lr_pipe.h"
 
 namespace lr {
 
-// GR = g*r columns of h (phase 1), K3 = rows of B, the up-projection's depth
-// (r; GR for g = 1)
-template <int GR, int K3>
+// GR = g*r columns of h (phase 1), K3 = rows of each B_i, the up-projection's
+// depth (r), NBR = up-projection branches (1 for SwiGLU, else g)
+template <int GR, int K3, int NBR>
 struct FusedGeo {
   static constexpr int BM = 64;
-  static constexpr int BK1 = GR == 256 ? 32 : 64;
-  static constexpr int S1 = GR == 64 ? 8 : (GR == 128 ? 6 : 7);
-  // phase 1 tile [BM, GR].  Up to r = 128 (k split): each MMA wave the whole
+  static constexpr int BK1 = GR > 128 ? 32 : 64;
+  static constexpr int S1 = GR == 64 ? 8 : (GR == 128 ? 6 : (GR == 192 ? 8 : 7));
+  // phase 1 tile [BM, GR].  Up to g*r = 128 (k split): each MMA wave the whole
   // tile over one of the four 16-deep k sub-steps of every stage, NSP = 4
   // partial sums added in phase 2; every LDS fragment is read once and each wave
-  // has 4-8 independent accumulators.  r = 256: MMA waves 2 x 2, wave tile
-  // 32 x GR/2, one partial (four of 64 x 256 would not fit in LDS).
+  // has 4-8 independent accumulators.  Wider: MMA waves 2 x 2, wave tile
+  // 32 x GR/2, one partial (four of 64 x GR would not fit in LDS).
   using C1 = PipeCfg<BM, GR, BK1, 2, 2, S1>;
   static constexpr bool KSPLIT = GR <= 128;
   static constexpr int NSP = KSPLIT ? 4 : 1;
@@ -64,12 +65,12 @@ struct FusedGeo {
   static constexpr int PF = K3 == 64 ? 3 : (K3 == 128 ? 2 : 1);
   static constexpr int NBUF = PF + 1;
   using C3 = PipeCfg<BM, 128, 64, 2, 2, 2>;  // z fragment geometry (BK = 64)
-  static constexpr int KT = K3 / 64;  // 64-deep k blocks of z
+  static constexpr int KT = K3 / 64;  // 64-deep k blocks of one branch's z
   static constexpr int THREADS = 512;
 
   static constexpr int P1 = S1 * C1::STAGE_BYTES + C1::SINK_BYTES;
   static constexpr int ZT = BM * 128;                  // one [BM][64] bf16 z tile
-  static constexpr int ZB = KT * ZT;
+  static constexpr int ZB = NBR * KT * ZT;
   static constexpr int ROWSS = ZB;                     // NSP x BM partial sums of squares
   static constexpr int STG = ZB + 4 * BM * 4;
   static constexpr int STG2_PITCH = GR * 4 + 16;       // fp32 h row + pad
@@ -80,18 +81,19 @@ struct FusedGeo {
   static constexpr int P2 = STG + NSP * STG2_BYTES;
   static constexpr int LDS = P1 > P3 ? (P1 > P2 ? P1 : P2) : (P3 > P2 ? P3 : P2);
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(GR % 64 == 0 && GR <= 256 && K3 % 64 == 0 && K3 <= GR, "rank");
+  static_assert(GR % 64 == 0 && GR <= 256 && K3 % 64 == 0 && NBR * K3 <= GR && NBR <= MAX_G, "rank");
   static constexpr int Q1X = DmaTile<C1, BM, false>::Q, Q1A = DmaTile<C1, GR, false>::Q;
   static_assert((S1 - 2) * (Q1X + Q1A) <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int GR, int ACT>
+template <int GR, int K3, int ACT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fused_fwd(FusedArgs a) {
   constexpr bool SW = ACT == ACT_SWIGLU;
-  constexpr int K3 = SW ? GR / 2 : GR;  // z columns: gate and up pair up in SwiGLU
-  using G = FusedGeo<GR, K3>;
+  constexpr int NBR = SW ? 1 : GR / K3;  // up-projection branches
+  constexpr int ZC = NBR * K3;           // z columns (SwiGLU: gate and up pair up)
+  using G = FusedGeo<GR, K3, NBR>;
   using C1 = typename G::C1;
   using C3 = typename G::C3;
   __shared__ uint4 lds[G::LDS / 16];
@@ -211,17 +213,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lgkm_wait0();
   block_barrier();
   if (!mma) {
-    // each lane 4 consecutive z columns of a row (SwiGLU: gate columns c.. and
+    // each item 4 consecutive z columns of a row (SwiGLU: gate columns c.. and
     // the up columns K3 + c..)
-    constexpr int LPR = K3 / 4, RPI = 256 / LPR;
+    constexpr int LPR = ZC / 4;
     bf16* h = static_cast<bf16*>(a.h);
-    const int c = (u % LPR) * 4;
-    // z tile of column c: [BM][64] K-contiguous, 16-byte chunks swizzled as the
-    // MFMA A-operand reads expect
-    const int zt = c / 64, kk = c % 64;
 #pragma unroll 4
-    for (int p = 0; p < G::BM / RPI; ++p) {
-      const int rl = p * RPI + u / LPR;
+    for (int it = u; it < G::BM * LPR; it += 256) {
+      const int rl = it / LPR, c = (it % LPR) * 4;
+      // z tile of column c: [BM][64] K-contiguous, 16-byte chunks swizzled as
+      // the MFMA A-operand reads expect
+      const int zt = c / 64, kk = c % 64;
       // x . A' at (rl, col): the NSP partials added in order
       auto acc_at = [&](int col) {
         float4 v = lds_f4(stg + rl * G::STG2_PITCH + col * 4);
@@ -260,23 +261,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   block_barrier();  // z complete; the h staging and the sums of squares are dead
 
   // ---------------------------------------------------------------- phase 3: y = z . B
-  const int nt_count = (d + G::BN3 - 1) / G::BN3;
-  bf16* y = static_cast<bf16*>(a.y);
+  // column tiles walk branch by branch: tile nt is tile nt % ntpb of branch
+  // nt / ntpb; tiles past the end count as tiles past d of the last branch
+  const int ntpb = (d + G::BN3 - 1) / G::BN3;
+  const int nt_count = NBR * ntpb;
+  auto branch_of = [&](int nt) { return min(nt / ntpb, NBR - 1); };
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  // z fragments (both 32-row blocks) in registers up to r = 128; at r = 256 they
-  // are read from LDS (z stays there through phase 3) to leave registers for B
-  constexpr bool ZREG = K3 <= 128;
+  // z fragments (both 32-row blocks) in registers for one branch up to r = 128;
+  // otherwise (r = 256, or several branches, whose z the tiles walk in turn)
+  // they are read from LDS, where z stays through phase 3
+  constexpr bool ZREG = K3 <= 128 && NBR == 1;
   uint4 zf[ZREG ? 2 : 1][ZREG ? G::KT : 1][4];
   f32x16 acc3[2];
   uint4 bb[G::NBUF][G::KT][4];
   const bf16* Bf = static_cast<const bf16*>(a.Bf);
-  // B fragments of this wave's 32 columns of column tile nt: fragment (column
-  // block cb, k16 block kb) starts at element ((cb * K3/16 + kb) * 64) * 8; a
-  // column block past d (the last tile's upper half when d is an odd multiple of
-  // 64) reads the last one and feeds y columns that are never stored
+  // B fragments of this wave's 32 columns of column tile nt: branch br's
+  // fragment (column block cb, k16 block kb) starts at element
+  // br*d*K3 + ((cb * K3/16 + kb) * 64) * 8; a column block past d (the last
+  // tile's upper half when d is an odd multiple of 64, or a tile past the end)
+  // reads the last one and feeds y columns that are never stored
   auto load_b = [&](int nt, uint4 (&bf)[G::KT][4]) {
-    const int cb = min(nt * (G::BN3 / 32) + w, d / 32 - 1);
-    const bf16* fp = Bf + ((int64_t)cb * (K3 / 16) * 64 + lane) * 8;
+    const int br = branch_of(nt);
+    const int cb = min((nt - br * ntpb) * (G::BN3 / 32) + w, d / 32 - 1);
+    const bf16* fp = Bf + (int64_t)br * d * K3 + ((int64_t)cb * (K3 / 16) * 64 + lane) * 8;
 #pragma unroll
     for (int kt = 0; kt < G::KT; ++kt)
 #pragma unroll
@@ -304,7 +311,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto store_tile = [&](int nt) {
     constexpr int LPR = G::BN3 / 8, RPI = 256 / LPR;
     const char LR_LDS* buf = stg + (nt & 1) * G::STG3_BUF;
-    const int ch = u % LPR, col = nt * G::BN3 + ch * 8;
+    const int br = branch_of(nt);
+    bf16* y = static_cast<bf16*>(a.y[br]);
+    const int ch = u % LPR, col = (nt - br * ntpb) * G::BN3 + ch * 8;
 #pragma unroll
     for (int p = 0; p < G::BM / RPI; ++p) {
       const int rl = p * RPI + u / LPR;
@@ -319,6 +328,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // copies, and each copy of a load target waits for every load in flight.
   auto mma_tile = [&](int nt, const uint4 (&bc)[G::KT][4], uint4 (&bn)[G::KT][4]) {
     load_b(nt + G::PF, bn);
+    const char LR_LDS* zb = ldsp + branch_of(nt) * G::KT * G::ZT;  // this branch's z
 #pragma unroll
     for (int kt = 0; kt < G::KT; ++kt)
 #pragma unroll
@@ -329,7 +339,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if constexpr (ZREG)
             za = zf[mb][kt][s];
           else
-            za = frag<C3, G::BM, false>(ldsp + kt * G::ZT, mb * 32, s, lane);
+            za = frag<C3, G::BM, false>(zb + kt * G::ZT, mb * 32, s, lane);
           mfma_chunk(acc3[mb], bc[kt][s], za, (bf16*)nullptr);
         }
     // lane l holds row l%32 of row block mb, columns 8q + 4(l/32) + 0..3 of the
@@ -374,68 +384,95 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and B [nb, d] in MFMA fragment
-// order, in one launch; one thread per 16-byte output chunk (8 elements), the
-// first na*d/8 threads for A'^T, the next nb*d/8 for B.
+// A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and the nbr matrices B_i
+// [nb, d] in MFMA fragment order one after another, in one launch; one thread
+// per 16-byte output chunk (8 elements), the first na*d/8 threads for A'^T, the
+// next nbr*nb*d/8 for B.
 //   A'^T chunk t: column c = t % na of A, rows j0 = 8 (t / na) .. +7 (lanes read
 //     consecutive columns of a row).
-//   B chunk t: fragment f = t / 64 = cb * (nb/16) + kb, lane l = t % 64: column
-//     32 cb + l%32, k values 16 kb + 8(l/32) .. +7.
-__global__ __launch_bounds__(256) void k_fold_fused(const bf16* __restrict__ A, const bf16* __restrict__ gamma,
-                                                    const bf16* __restrict__ B, bf16* __restrict__ Apt,
-                                                    bf16* __restrict__ Bf, int d, int na, int nb) {
+//   B chunk t: branch i = t / (nb*d/8); within it fragment f = t' / 64 =
+//     cb * (nb/16) + kb, lane l = t' % 64: column 32 cb + l%32, k values
+//     16 kb + 8(l/32) .. +7.
+struct FoldArgs {
+  const bf16* A;
+  const bf16* gamma;
+  const bf16* B[MAX_G];
+  bf16* Apt;
+  bf16* Bf;
+  int d, na, nb, nbr;
+};
+
+__global__ __launch_bounds__(256) void k_fold_fused(FoldArgs a) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t ca = (int64_t)na * d / 8, cbn = (int64_t)nb * d / 8;
+  const int64_t ca = (int64_t)a.na * a.d / 8, per = (int64_t)a.nb * a.d / 8;
   bf16x8 v;
   if (t < ca) {
-    const int c = (int)(t % na), j0 = (int)(t / na) * 8;
+    const int c = (int)(t % a.na), j0 = (int)(t / a.na) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)A[(int64_t)(j0 + i) * na + c] * (float)gamma[j0 + i]);
-    *reinterpret_cast<bf16x8*>(Apt + (int64_t)c * d + j0) = v;
-  } else if (t < ca + cbn) {
+    for (int i = 0; i < 8; ++i)
+      v[i] = (bf16)((float)a.A[(int64_t)(j0 + i) * a.na + c] * (float)a.gamma[j0 + i]);
+    *reinterpret_cast<bf16x8*>(a.Apt + (int64_t)c * a.d + j0) = v;
+  } else if (t < ca + a.nbr * per) {
     const int64_t tb = t - ca;
-    const int l = (int)(tb % 64);
-    const int64_t f = tb / 64;
-    const int kb = (int)(f % (nb / 16)), cb = (int)(f / (nb / 16));
+    const int br = (int)(tb / per);
+    const int64_t tl = tb % per;
+    const int l = (int)(tl % 64);
+    const int64_t f = tl / 64;
+    const int kb = (int)(f % (a.nb / 16)), cb = (int)(f / (a.nb / 16));
     const int col = cb * 32 + (l & 31), k0 = kb * 16 + 8 * (l >> 5);
+    const bf16* B = a.B[br];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = B[(int64_t)(k0 + i) * d + col];
-    *reinterpret_cast<bf16x8*>(Bf + tb * 8) = v;
+    for (int i = 0; i < 8; ++i) v[i] = B[(int64_t)(k0 + i) * a.d + col];
+    *reinterpret_cast<bf16x8*>(a.Bf + tb * 8) = v;
   }
 }
 
-hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int na,
-                             int nb, hipStream_t s) {
-  const int64_t chunks = ((int64_t)na + nb) * d / 8;
-  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const bf16*>(A), static_cast<const bf16*>(gamma), static_cast<const bf16*>(B),
-                     static_cast<bf16*>(Apt), static_cast<bf16*>(Bf), d, na, nb);
+hipError_t launch_fold_fused(const void* A, const void* gamma, const void* const* B, int nbr, void* Apt, void* Bf,
+                             int d, int na, int nb, hipStream_t s) {
+  if (nbr < 1 || nbr > MAX_G) return hipErrorInvalidValue;
+  FoldArgs f{};
+  f.A = static_cast<const bf16*>(A);
+  f.gamma = static_cast<const bf16*>(gamma);
+  for (int i = 0; i < nbr; ++i) f.B[i] = static_cast<const bf16*>(B[i]);
+  f.Apt = static_cast<bf16*>(Apt);
+  f.Bf = static_cast<bf16*>(Bf);
+  f.d = d; f.na = na; f.nb = nb; f.nbr = nbr;
+  const int64_t chunks = ((int64_t)na + (int64_t)nbr * nb) * d / 8;
+  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, f);
   return hipGetLastError();
 }
 
-template <int GR, int ACT>
+template <int GR, int K3, int ACT>
 static hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_fused_fwd<GR, ACT>), dim3((a.T + 63) / 64), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((k_fused_fwd<GR, K3, ACT>), dim3((a.T + 63) / 64), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 bool fused_fwd_supported(int r, int g, int act) {
   if (act == ACT_SWIGLU) return g == 2 && (r == 64 || r == 128);
-  return g == 1 && (r == 64 || r == 128 || r == 256) && (act == ACT_IDENTITY || act == ACT_SILU);
+  if (act != ACT_IDENTITY && act != ACT_SILU) return false;
+  return (r == 64 && g >= 1 && g <= 4) || (r == 128 && (g == 1 || g == 2)) || (r == 256 && g == 1);
+}
+
+template <int ACT>
+static hipError_t launch_fused_act(const FusedArgs& a, hipStream_t s) {
+  switch (a.g * a.r) {
+    case 64: return launch_fused_g<64, 64, ACT>(a, s);
+    case 128: return a.r == 64 ? launch_fused_g<128, 64, ACT>(a, s) : launch_fused_g<128, 128, ACT>(a, s);
+    case 192: return launch_fused_g<192, 64, ACT>(a, s);
+    default:
+      return a.r == 64 ? launch_fused_g<256, 64, ACT>(a, s)
+                       : (a.r == 128 ? launch_fused_g<256, 128, ACT>(a, s) : launch_fused_g<256, 256, ACT>(a, s));
+  }
 }
 
 hipError_t launch_fused_fwd(const FusedArgs& a, int act, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (!fused_fwd_supported(a.r, act == ACT_SWIGLU ? 2 : 1, act)) return hipErrorInvalidValue;
+  if (!fused_fwd_supported(a.r, a.g, act)) return hipErrorInvalidValue;
   if (act == ACT_SWIGLU)
-    return a.r == 64 ? launch_fused_g<128, ACT_SWIGLU>(a, s) : launch_fused_g<256, ACT_SWIGLU>(a, s);
-  const bool silu = act == ACT_SILU;
-  switch (a.r) {
-    case 64: return silu ? launch_fused_g<64, ACT_SILU>(a, s) : launch_fused_g<64, ACT_IDENTITY>(a, s);
-    case 128: return silu ? launch_fused_g<128, ACT_SILU>(a, s) : launch_fused_g<128, ACT_IDENTITY>(a, s);
-    default: return silu ? launch_fused_g<256, ACT_SILU>(a, s) : launch_fused_g<256, ACT_IDENTITY>(a, s);
-  }
+    return a.r == 64 ? launch_fused_g<128, 64, ACT_SWIGLU>(a, s) : launch_fused_g<256, 128, ACT_SWIGLU>(a, s);
+  return act == ACT_SILU ? launch_fused_act<ACT_SILU>(a, s) : launch_fused_act<ACT_IDENTITY>(a, s);
 }
 
 }  // namespace lr

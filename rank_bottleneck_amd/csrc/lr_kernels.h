@@ -34,15 +34,15 @@ struct SplitDownArgs {
   float* sumsq;       // [nsplit][T]
 };
 
-// Small-rank forward in one kernel (g = 1, or SwiGLU's g = 2): x, A'^T [g*r, d]
-// (gamma folded in), B [r, d]
+// Small-rank forward in one kernel (g*r <= 256, see fused_fwd_supported): x,
+// A'^T [g*r, d] (gamma folded in), the B_i [r, d] in MFMA fragment order
 struct FusedArgs {
   const void* x;      // [T, d]
   const void* Apt;    // [g*r, d]: (diag(gamma) A)^T, K-contiguous
-  const void* Bf;     // B [r, d] in MFMA fragment order (launch_fold_fused)
-  void* y;            // [T, d]
+  const void* Bf;     // the n_up matrices B_i [r, d] in MFMA fragment order, one after another
+  void* y[MAX_G];     // n_up x [T, d]
   void* h;            // [T, g*r] or null
-  int T, d, r;
+  int T, d, r, g;
   float invD, eps;
 };
 
@@ -130,13 +130,16 @@ template <typename E> hipError_t launch_fold_gamma_t(const void* A, const void* 
 // regular down-projection is used.
 template <typename E> int small_rank_splits(int T, int d, int r, int g, int act);
 template <typename E> hipError_t launch_down_split(const SplitDownArgs& a, hipStream_t s);
-// whether the one-kernel small-rank forward serves these dims (bf16 only)
+// whether the one-kernel small-rank forward serves these dims (bf16 only):
+// identity / SiLU with g*r <= 256 (r = 64: g <= 4; r = 128: g <= 2; r = 256:
+// g = 1), SwiGLU with r = 64 or 128
 bool fused_fwd_supported(int r, int g, int act);
 hipError_t launch_fused_fwd(const FusedArgs& a, int act, hipStream_t s);
-// A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and B [nb, d] in MFMA fragment
-// order (fragment of 32 columns x 16 k values = 64 lanes x 8 consecutive k) (bf16)
-hipError_t launch_fold_fused(const void* A, const void* gamma, const void* B, void* Apt, void* Bf, int d, int na,
-                             int nb, hipStream_t s);
+// A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and the nbr matrices B[i]
+// [nb, d] in MFMA fragment order (fragment of 32 columns x 16 k values = 64
+// lanes x 8 consecutive k), one after another (bf16)
+hipError_t launch_fold_fused(const void* A, const void* gamma, const void* const* B, int nbr, void* Apt, void* Bf,
+                             int d, int na, int nb, hipStream_t s);
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 // sums the split partials of launch_wgrad (nothing to do when nsplit == 1)

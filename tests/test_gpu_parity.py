@@ -57,6 +57,12 @@ SMALL = [
     Workload("bf16_g1_r128_dnorm", 130, 192, 128, 1, "silu", "bf16", d_norm=768),
     # SwiGLU's gate/up pair at small rank: the one-kernel forward as well
     Workload("bf16_swiglu_r128_small", 333, 320, 128, 2, "swiglu", "bf16"),
+    # grouped branches at small g*r in the one-kernel forward (g*r = 192, 256)
+    Workload("bf16_g3_r64", 519, 320, 64, 3, "silu", "bf16"),
+    Workload("bf16_g4_r64", 200, 256, 64, 4, "identity", "bf16"),
+    # a small g*r that the one-kernel forward does not take (r = 192): the
+    # split-K down-projection, the finish kernel and the short-K up-projection
+    Workload("bf16_g1_r192_split", 600, 384, 192, 1, "silu", "bf16"),
 ]
 
 
