@@ -48,16 +48,20 @@ struct FusedGeo {
   static constexpr int BM = 64;
   static constexpr int BK1 = GR > 128 ? 32 : 64;
   static constexpr int S1 = GR == 64 ? 8 : (GR == 128 ? 6 : (GR == 192 ? 8 : 7));
-  // phase 1 tile [BM, GR].  Up to g*r = 128 (k split): each MMA wave the whole
-  // tile over one of the four 16-deep k sub-steps of every stage, NSP = 4
-  // partial sums added in phase 2; every LDS fragment is read once and each wave
-  // has 4-8 independent accumulators.  Wider: MMA waves 2 x 2, wave tile
-  // 32 x GR/2, one partial (four of 64 x GR would not fit in LDS).
+  // phase 1 tile [BM, GR], k split inside the work-group, so that each wave has
+  // 6-8 independent accumulators and every LDS fragment is read by one wave (or
+  // one wave pair):
+  //   g*r <= 128 (BK = 64, four 16-deep sub-steps per stage): MMA wave w the
+  //     whole tile over sub-step w; NSP = 4 partials, added in phase 2;
+  //   wider (BK = 32, two sub-steps): MMA wave w sub-step w/2 and column half
+  //     w%2, all BM rows; the sub-step-1 waves add their partial into the
+  //     sub-step-0 waves' staging in place (four partials would not fit in LDS).
+  // NSS = partial row sums of squares (one per sub-step).
   using C1 = PipeCfg<BM, GR, BK1, 2, 2, S1>;
   static constexpr bool KSPLIT = GR <= 128;
-  static constexpr int NSP = KSPLIT ? 4 : 1;
-  static constexpr int MB1 = KSPLIT ? 2 : 1, NB1 = KSPLIT ? GR / 32 : C1::NB;
-  static_assert(!KSPLIT || C1::KS == 4, "one k sub-step per MMA wave");
+  static constexpr int NSP = KSPLIT ? 4 : 1, NSS = KSPLIT ? 4 : 2;
+  static constexpr int MB1 = 2, NB1 = KSPLIT ? GR / 32 : GR / 64;
+  static_assert(C1::KS == (KSPLIT ? 4 : 2), "one k sub-step per MMA wave (pair)");
   // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of 32
   // columns; the B fragments of PF column tiles ahead in flight (register
   // buffers NBUF = PF + 1), 48-64 KB per CU
@@ -71,7 +75,7 @@ struct FusedGeo {
   static constexpr int P1 = S1 * C1::STAGE_BYTES + C1::SINK_BYTES;
   static constexpr int ZT = BM * 128;                  // one [BM][64] bf16 z tile
   static constexpr int ZB = NBR * KT * ZT;
-  static constexpr int ROWSS = ZB;                     // NSP x BM partial sums of squares
+  static constexpr int ROWSS = ZB;                     // NSS x BM partial sums of squares
   static constexpr int STG = ZB + 4 * BM * 4;
   static constexpr int STG2_PITCH = GR * 4 + 16;       // fp32 h row + pad
   static constexpr int STG2_BYTES = BM * STG2_PITCH;
@@ -153,30 +157,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (mma) {
       issue1(kt + G::S1 - 1);
       const char LR_LDS* tb = ta + C1::A_BYTES;
-      if constexpr (G::KSPLIT) {
-        // sub-step w of the stage, all BM rows and GR columns
-        uint4 fa[MB1], fb[NB1];
+      // sub-step s1 of the stage, all BM rows, columns col0 .. col0 + 32*NB1
+      const int s1 = G::KSPLIT ? w : wm, col0 = G::KSPLIT ? 0 : wn * (GR / 2);
+      uint4 fa[MB1], fb[NB1];
 #pragma unroll
-        for (int mb = 0; mb < MB1; ++mb) fa[mb] = frag<C1, G::BM, false>(ta, mb * 32, w, lane);
+      for (int mb = 0; mb < MB1; ++mb) fa[mb] = frag<C1, G::BM, false>(ta, mb * 32, s1, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB1; ++nb) fb[nb] = frag<C1, GR, false>(tb, nb * 32, w, lane);
+      for (int nb = 0; nb < NB1; ++nb) fb[nb] = frag<C1, GR, false>(tb, col0 + nb * 32, s1, lane);
 #pragma unroll
-        for (int mb = 0; mb < MB1; ++mb) {
-          ss[mb] = frag_sumsq(fa[mb], ss[mb]);
+      for (int mb = 0; mb < MB1; ++mb) {
+        ss[mb] = frag_sumsq(fa[mb], ss[mb]);
 #pragma unroll
-          for (int nb = 0; nb < NB1; ++nb) mfma_chunk(acc1[mb][nb], fb[nb], fa[mb], (bf16*)nullptr);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < C1::KS; ++s) {
-          const uint4 fa = frag<C1, G::BM, false>(ta, wm * 32, s, lane);
-          ss[0] = frag_sumsq(fa, ss[0]);
-#pragma unroll
-          for (int nb = 0; nb < NB1; ++nb) {
-            const uint4 fb = frag<C1, GR, false>(tb, wn * C1::WTN + nb * 32, s, lane);
-            mfma_chunk(acc1[0][nb], fb, fa, (bf16*)nullptr);
-          }
-        }
+        for (int nb = 0; nb < NB1; ++nb) mfma_chunk(acc1[mb][nb], fb[nb], fa[mb], (bf16*)nullptr);
       }
     }
   }
@@ -185,30 +177,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   block_barrier();  // the ring is dead from here on
 
   // ---------------------------------------------------------------- phase 2: h, z
-  // NSP fp32 partials of x . A' ([BM][GR] each, padded rows) and NSP x BM
+  // NSP fp32 partials of x . A' ([BM][GR] each, padded rows) and NSS x BM
   // partial sums of squares; the store role adds them in partial order
   float LR_LDS* ssp = reinterpret_cast<float LR_LDS*>(ldsp + G::ROWSS);
   char LR_LDS* stg = ldsp + G::STG;
-  if (mma) {
-    // lane l holds row l%32 of each 32-row block, columns 8q + 4(l/32) + 0..3 of
-    // each 32-column block nb (the swapped operand order of mfma_chunk)
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const int part = G::KSPLIT ? w : 0, r0 = G::KSPLIT ? 0 : wm * 32, c0 = G::KSPLIT ? 0 : wn * C1::WTN;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  // lane l holds row l%32 of each 32-row block, columns 8q + 4(l/32) + 0..3 of
+  // each 32-column block nb (the swapped operand order of mfma_chunk); ADD:
+  // add into what the staging already holds
+  auto stage_acc1 = [&](int part, int c0, bool add) {
 #pragma unroll
     for (int mb = 0; mb < MB1; ++mb) {
-      char LR_LDS* rowp =
-          stg + part * G::STG2_BYTES + (r0 + mb * 32 + (lane & 31)) * G::STG2_PITCH + 16 * (lane >> 5);
+      char LR_LDS* rowp = stg + part * G::STG2_BYTES + (mb * 32 + (lane & 31)) * G::STG2_PITCH + 16 * (lane >> 5);
 #pragma unroll
       for (int nb = 0; nb < NB1; ++nb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f4 v = {acc1[mb][nb][4 * q], acc1[mb][nb][4 * q + 1], acc1[mb][nb][4 * q + 2],
-                        acc1[mb][nb][4 * q + 3]};
-          *reinterpret_cast<f4 LR_LDS*>(rowp + (c0 + nb * 32 + 8 * q) * 4) = v;
+          f4 v = {acc1[mb][nb][4 * q], acc1[mb][nb][4 * q + 1], acc1[mb][nb][4 * q + 2], acc1[mb][nb][4 * q + 3]};
+          f4 LR_LDS* dst = reinterpret_cast<f4 LR_LDS*>(rowp + (c0 + nb * 32 + 8 * q) * 4);
+          if (add) v = *dst + v;
+          *dst = v;
         }
-      ss[mb] += __shfl_xor(ss[mb], 32);
-      if ((G::KSPLIT || wn == 0) && lane < 32) ssp[part * G::BM + r0 + mb * 32 + lane] = ss[mb];
     }
+  };
+  if (mma) {
+    if (G::KSPLIT || wm == 0) stage_acc1(G::KSPLIT ? w : 0, G::KSPLIT ? 0 : wn * (GR / 2), false);
+#pragma unroll
+    for (int mb = 0; mb < MB1; ++mb) {
+      ss[mb] += __shfl_xor(ss[mb], 32);
+      // sub-step s1's partial (KSPLIT: every wave; else the column-half-0 waves)
+      if ((G::KSPLIT || wn == 0) && lane < 32) ssp[(G::KSPLIT ? w : wm) * G::BM + mb * 32 + lane] = ss[mb];
+    }
+  }
+  if constexpr (!G::KSPLIT) {
+    lgkm_wait0();
+    block_barrier();  // the sub-step-0 partial is staged
+    if (mma && wm == 1) stage_acc1(0, wn * (GR / 2), true);
   }
   lgkm_wait0();
   block_barrier();
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       };
       float ssr = ssp[rl];
 #pragma unroll
-      for (int pp = 1; pp < G::NSP; ++pp) ssr += ssp[pp * G::BM + rl];
+      for (int pp = 1; pp < G::NSS; ++pp) ssr += ssp[pp * G::BM + rl];
       const float rs = __builtin_amdgcn_rsqf(ssr * a.invD + a.eps);
       const float4 v = acc_at(c);
       float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
