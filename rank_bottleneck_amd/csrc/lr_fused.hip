@@ -14,11 +14,11 @@
 // Work-group of 8 waves in two roles, because on this chip the vector memory
 // counter counts stores as well as loads: a wave that waits for a DMA stage
 // after issuing output stores also waits for those stores.
-//   MMA waves (0-3): all global loads (x and A' tiles by DMA into LDS in phase 1;
-//     B fragments straight into registers in phase 3) and the MFMAs.
-//   store waves (4-7): h and z (phase 2) and the y stores (phase 3, from bf16
-//     tiles the MMA waves stage in LDS, double-buffered).  They issue no global
-//     loads; in phase 1 they only keep the barrier count.
+//   MMA waves (0-3): the x tiles' DMA into LDS (phase 1), the B fragments'
+//     loads into registers (phase 3) and the MFMAs.
+//   store waves (4-7): the A'^T tiles' DMA (phase 1), h and z (phase 2) and the
+//     y stores (phase 3, from bf16 tiles the MMA waves stage in LDS,
+//     double-buffered).  After phase 1 they issue no global loads.
 // The row sum of squares comes from the x fragments of the MMA waves.
 // Both roles run the same sequence of barriers (one per k step of phase 1, one
 // per column tile of phase 3, and the phase boundaries), with every branch on
@@ -32,7 +32,8 @@
 // up-projection needs no LDS ring and no wait on other waves' loads.
 //
 // LDS (bytes from 0):
-//   phase 1: ring of S1 stages [x tile | A'^T tile] and the sink of dead stages;
+//   phase 1: a ring of SX x tiles and its sink, then a ring of SA A'^T tiles and
+//     its sink;
 //   phases 2-3 (after the ring is drained): z as [BM][64] tiles (K contiguous,
 //     swizzled as an MFMA A tile), the partial row sums of squares, then the
 //     fp32 staging of h (phase 2) or two bf16 y tiles (phase 3).
@@ -47,7 +48,12 @@ template <int GR, int K3, int NBR>
 struct FusedGeo {
   static constexpr int BM = 64;
   static constexpr int BK1 = GR > 128 ? 32 : 64;
-  static constexpr int S1 = GR == 64 ? 8 : (GR == 128 ? 6 : (GR == 192 ? 8 : 7));
+  // phase-1 rings: x tiles (from HBM, the MMA waves' DMA) SX stages deep, A'^T
+  // tiles (L2-resident, the store waves' DMA) SA deep; each role waits only for
+  // its own loads, so the x stream keeps 7-15 stages in flight whatever A''s
+  // share of a stage
+  static constexpr int SX = GR == 64 ? 12 : (GR == 128 ? 8 : 16);
+  static constexpr int SA = 4;
   // phase 1 tile [BM, GR], k split inside the work-group, so that each wave has
   // 6-8 independent accumulators and every LDS fragment is read by one wave (or
   // one wave pair):
@@ -57,7 +63,7 @@ struct FusedGeo {
   //     w%2, all BM rows; the sub-step-1 waves add their partial into the
   //     sub-step-0 waves' staging in place (four partials would not fit in LDS).
   // NSS = partial row sums of squares (one per sub-step).
-  using C1 = PipeCfg<BM, GR, BK1, 2, 2, S1>;
+  using C1 = PipeCfg<BM, GR, BK1, 2, 2, 2>;  // tile and fragment geometry
   static constexpr bool KSPLIT = GR <= 128;
   static constexpr int NSP = KSPLIT ? 4 : 1, NSS = KSPLIT ? 4 : 2;
   static constexpr int MB1 = 2, NB1 = KSPLIT ? GR / 32 : GR / 64;
@@ -72,7 +78,9 @@ struct FusedGeo {
   static constexpr int KT = K3 / 64;  // 64-deep k blocks of one branch's z
   static constexpr int THREADS = 512;
 
-  static constexpr int P1 = S1 * C1::STAGE_BYTES + C1::SINK_BYTES;
+  static constexpr int XB = C1::A_BYTES, AB = C1::B_BYTES;  // one x / A'^T stage
+  static constexpr int X_SINK = SX * XB, A_RING = X_SINK + XB, A_SINK = A_RING + SA * AB;
+  static constexpr int P1 = A_SINK + AB;
   static constexpr int ZT = BM * 128;                  // one [BM][64] bf16 z tile
   static constexpr int ZB = NBR * KT * ZT;
   static constexpr int ROWSS = ZB;                     // NSS x BM partial sums of squares
@@ -87,7 +95,7 @@ struct FusedGeo {
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(GR % 64 == 0 && GR <= 256 && K3 % 64 == 0 && NBR * K3 <= GR && NBR <= MAX_G, "rank");
   static constexpr int Q1X = DmaTile<C1, BM, false>::Q, Q1A = DmaTile<C1, GR, false>::Q;
-  static_assert((S1 - 2) * (Q1X + Q1A) <= 63, "vmcnt range");
+  static_assert((SX - 2) * Q1X <= 63 && (SA - 2) * Q1A <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -135,28 +143,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const Opnd oa{a.Apt, d, GR, d};
   if (mma) {
     dxt.init(ox, MapId{}, m0, w, lane);
-    dat.init(oa, MapId{}, 0, w, lane);
     dxt.init_range(ox, m0, 0);
+  } else {
+    dat.init(oa, MapId{}, 0, w, lane);
     dat.init_range(oa, 0, 0);
   }
-  auto issue1 = [&](int st) {
+  // stages past the end read an empty range into the ring's sink, which keeps
+  // each role's load count per k step the same
+  auto issue_x = [&](int st) {
     const bool live = st < nk1;
-    const uint32_t base = lds0 + (live ? (st % G::S1) * C1::STAGE_BYTES : G::S1 * C1::STAGE_BYTES);
-    dxt.issue(dxt.rsrc(st, live), base, w);
-    dat.issue(dat.rsrc(st, live), live ? base + C1::A_BYTES : base, w);
+    dxt.issue(dxt.rsrc(st, live), lds0 + (live ? (st % G::SX) * G::XB : G::X_SINK), w);
+  };
+  auto issue_a = [&](int st) {
+    const bool live = st < nk1;
+    dat.issue(dat.rsrc(st, live), lds0 + (live ? G::A_RING + (st % G::SA) * G::AB : G::A_SINK), w);
   };
   if (mma) {
 #pragma unroll
-    for (int st = 0; st < G::S1 - 1; ++st) issue1(st);
+    for (int st = 0; st < G::SX - 1; ++st) issue_x(st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < G::SA - 1; ++st) issue_a(st);
   }
   for (int kt = 0; kt < nk1; ++kt) {
-    if (mma) wait_vmcnt<(G::S1 - 2) * (G::Q1X + G::Q1A)>();
+    if (mma)
+      wait_vmcnt<(G::SX - 2) * G::Q1X>();
+    else
+      wait_vmcnt<(G::SA - 2) * G::Q1A>();
     lgkm_wait0();
-    block_barrier();  // stage kt landed for every wave; stage kt-1's buffer is free
-    const char LR_LDS* ta = ldsp + (kt % G::S1) * C1::STAGE_BYTES;
+    block_barrier();  // stage kt landed for every wave; stage kt-1's buffers are free
+    if (!mma) issue_a(kt + G::SA - 1);
     if (mma) {
-      issue1(kt + G::S1 - 1);
-      const char LR_LDS* tb = ta + C1::A_BYTES;
+      issue_x(kt + G::SX - 1);
+      const char LR_LDS* ta = ldsp + (kt % G::SX) * G::XB;
+      const char LR_LDS* tb = ldsp + G::A_RING + (kt % G::SA) * G::AB;
       // sub-step s1 of the stage, all BM rows, columns col0 .. col0 + 32*NB1
       const int s1 = G::KSPLIT ? w : wm, col0 = G::KSPLIT ? 0 : wn * (GR / 2);
       uint4 fa[MB1], fb[NB1];
@@ -172,9 +192,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  if (mma) wait_vmcnt<0>();  // the sink loads of dead stages
+  wait_vmcnt<0>();  // the sink loads of dead stages (both roles)
   lgkm_wait0();
-  block_barrier();  // the ring is dead from here on
+  block_barrier();  // the rings are dead from here on
 
   // ---------------------------------------------------------------- phase 2: h, z
   // NSP fp32 partials of x . A' ([BM][GR] each, padded rows) and NSS x BM
