@@ -409,14 +409,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // A'^T = (diag(gamma) A)^T [na, d] for A [d, na], and the nbr matrices B_i
-// [nb, d] in MFMA fragment order one after another, in one launch; one thread
-// per 16-byte output chunk (8 elements), the first na*d/8 threads for A'^T, the
-// next nbr*nb*d/8 for B.
-//   A'^T chunk t: column c = t % na of A, rows j0 = 8 (t / na) .. +7 (lanes read
-//     consecutive columns of a row).
-//   B chunk t: branch i = t / (nb*d/8); within it fragment f = t' / 64 =
-//     cb * (nb/16) + kb, lane l = t' % 64: column 32 cb + l%32, k values
-//     16 kb + 8(l/32) .. +7.
+// [nb, d] in MFMA fragment order one after another, in one launch.
+//   Blocks [0, d/64 * na/64): one 64 x 64 tile of A each, read as rows of
+//     16-byte chunks, scaled by gamma, rounded to bf16 once, transposed
+//     through LDS and written as rows of A'^T (whole 128-byte runs both ways).
+//   The other blocks: one thread per 16-byte chunk of the reordered B: branch
+//     i = t / (nb*d/8); within it fragment f = t' / 64 = cb * (nb/16) + kb,
+//     lane l = t' % 64: column 32 cb + l%32, k values 16 kb + 8(l/32) .. +7.
 struct FoldArgs {
   const bf16* A;
   const bf16* gamma;
@@ -428,17 +427,36 @@ struct FoldArgs {
 
 __global__ __launch_bounds__(256) void k_fold_fused(FoldArgs a) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t ca = (int64_t)a.na * a.d / 8, per = (int64_t)a.nb * a.d / 8;
-  bf16x8 v;
-  if (t < ca) {
-    const int c = (int)(t % a.na), j0 = (int)(t / a.na) * 8;
+  __shared__ bf16 tile[64][64 + 8];  // [j][c]; rows padded by 16 bytes
+  const int tiles_c = a.na / 64, tiles_a = (a.d / 64) * tiles_c;
+  if ((int)blockIdx.x < tiles_a) {
+    const int j0 = ((int)blockIdx.x / tiles_c) * 64, c0 = ((int)blockIdx.x % tiles_c) * 64;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = (bf16)((float)a.A[(int64_t)(j0 + i) * a.na + c] * (float)a.gamma[j0 + i]);
-    *reinterpret_cast<bf16x8*>(a.Apt + (int64_t)c * a.d + j0) = v;
-  } else if (t < ca + a.nbr * per) {
-    const int64_t tb = t - ca;
+    for (int i = 0; i < 2; ++i) {
+      const int q = threadIdx.x + 256 * i, jj = q / 8, cc = (q % 8) * 8;
+      const bf16x8 in = *reinterpret_cast<const bf16x8*>(a.A + (int64_t)(j0 + jj) * a.na + c0 + cc);
+      const float gj = (float)a.gamma[j0 + jj];
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)in[e] * gj);
+      *reinterpret_cast<bf16x8*>(&tile[jj][cc]) = o;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = threadIdx.x + 256 * i, cr = q / 8, jc = (q % 8) * 8;
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = tile[jc + e][cr];
+      *reinterpret_cast<bf16x8*>(a.Apt + (int64_t)(c0 + cr) * a.d + j0 + jc) = o;
+    }
+    return;
+  }
+  const int64_t t = (int64_t)((int)blockIdx.x - tiles_a) * 256 + threadIdx.x;
+  const int64_t per = (int64_t)a.nb * a.d / 8;
+  bf16x8 v;
+  if (t < a.nbr * per) {
+    const int64_t tb = t;
     const int br = (int)(tb / per);
     const int64_t tl = tb % per;
     const int l = (int)(tl % 64);
@@ -462,8 +480,8 @@ hipError_t launch_fold_fused(const void* A, const void* gamma, const void* const
   f.Apt = static_cast<bf16*>(Apt);
   f.Bf = static_cast<bf16*>(Bf);
   f.d = d; f.na = na; f.nb = nb; f.nbr = nbr;
-  const int64_t chunks = ((int64_t)na + (int64_t)nbr * nb) * d / 8;
-  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, f);
+  const int64_t tiles_a = (int64_t)(d / 64) * (na / 64), chunks_b = (int64_t)nbr * nb * d / 8;
+  hipLaunchKernelGGL(k_fold_fused, dim3((unsigned)(tiles_a + (chunks_b + 255) / 256)), dim3(256), 0, s, f);
   return hipGetLastError();
 }
 
