@@ -71,8 +71,12 @@ struct FusedGeo {
   // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of 32
   // columns; the B fragments of PF column tiles ahead in flight (register
   // buffers NBUF = PF + 1), 48-64 KB per CU
-  static constexpr int BN3 = 128;
-  static constexpr int PF = K3 == 64 ? 3 : (K3 == 128 ? 2 : 1);
+  // NB3 32-column blocks per wave and tile: two for g*r = 64 (256-column tiles,
+  // half the tiles and barriers; measured 3-4% faster), else one (the wider
+  // phase-1 shapes need the registers: two measured 5% slower for SwiGLU at 64)
+  static constexpr int NB3 = GR == 64 ? 2 : 1;
+  static constexpr int BN3 = 128 * NB3;
+  static constexpr int PF = GR == 64 ? 2 : (K3 == 64 ? 3 : (K3 == 128 ? 2 : 1));
   static constexpr int NBUF = PF + 1;
   using C3 = PipeCfg<BM, 128, 64, 2, 2, 2>;  // z fragment geometry (BK = 64)
   static constexpr int KT = K3 / 64;  // 64-deep k blocks of one branch's z
@@ -296,23 +300,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // they are read from LDS, where z stays through phase 3
   constexpr bool ZREG = K3 <= 128 && NBR == 1;
   uint4 zf[ZREG ? 2 : 1][ZREG ? G::KT : 1][4];
-  f32x16 acc3[2];
-  uint4 bb[G::NBUF][G::KT][4];
+  constexpr int NB3 = G::NB3;
+  f32x16 acc3[2][NB3];
+  uint4 bb[G::NBUF][G::KT][4][NB3];
   const bf16* Bf = static_cast<const bf16*>(a.Bf);
   // B fragments of this wave's 32 columns of column tile nt: branch br's
   // fragment (column block cb, k16 block kb) starts at element
   // br*d*K3 + ((cb * K3/16 + kb) * 64) * 8; a column block past d (the last
   // tile's upper half when d is an odd multiple of 64, or a tile past the end)
   // reads the last one and feeds y columns that are never stored
-  auto load_b = [&](int nt, uint4 (&bf)[G::KT][4]) {
+  auto load_b = [&](int nt, uint4 (&bf)[G::KT][4][NB3]) {
     const int br = branch_of(nt);
-    const int cb = min((nt - br * ntpb) * (G::BN3 / 32) + w, d / 32 - 1);
-    const bf16* fp = Bf + (int64_t)br * d * K3 + ((int64_t)cb * (K3 / 16) * 64 + lane) * 8;
 #pragma unroll
-    for (int kt = 0; kt < G::KT; ++kt)
+    for (int nb = 0; nb < NB3; ++nb) {
+      const int cb = min((nt - br * ntpb) * (G::BN3 / 32) + w * NB3 + nb, d / 32 - 1);
+      const bf16* fp = Bf + (int64_t)br * d * K3 + ((int64_t)cb * (K3 / 16) * 64 + lane) * 8;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        bf[kt][s] = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4*>(fp + (kt * 4 + s) * 64 * 8));
+      for (int kt = 0; kt < G::KT; ++kt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          bf[kt][s][nb] = __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4*>(fp + (kt * 4 + s) * 64 * 8));
+    }
   };
   if (mma) {
     if constexpr (ZREG) {
@@ -326,12 +334,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc3[mb][v] = 0.f;
+      for (int nb = 0; nb < NB3; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc3[mb][nb][v] = 0.f;
 #pragma unroll
     for (int j = 0; j < G::PF; ++j) load_b(j, bb[j]);
   }
-  // store role: one staged [BM][BN3] bf16 tile -> y (16 lanes per row, 16 bytes
-  // each); write-back stores, which stream faster than nontemporal ones here
+  // store role: one staged [BM][BN3] bf16 tile -> y (BN3/8 lanes per row, 16
+  // bytes each); write-back stores, which stream faster than nontemporal ones here
   auto store_tile = [&](int nt) {
     constexpr int LPR = G::BN3 / 8, RPI = 256 / LPR;
     const char LR_LDS* buf = stg + (nt & 1) * G::STG3_BUF;
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Loads and tiles past the end are not skipped but clamped or masked (see
   // below): a skipped load would make the compiler merge register values with
   // copies, and each copy of a load target waits for every load in flight.
-  auto mma_tile = [&](int nt, const uint4 (&bc)[G::KT][4], uint4 (&bn)[G::KT][4]) {
+  auto mma_tile = [&](int nt, const uint4 (&bc)[G::KT][4][NB3], uint4 (&bn)[G::KT][4][NB3]) {
     load_b(nt + G::PF, bn);
     const char LR_LDS* zb = ldsp + branch_of(nt) * G::KT * G::ZT;  // this branch's z
 #pragma unroll
@@ -364,21 +374,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             za = zf[mb][kt][s];
           else
             za = frag<C3, G::BM, false>(zb + kt * G::ZT, mb * 32, s, lane);
-          mfma_chunk(acc3[mb], bc[kt][s], za, (bf16*)nullptr);
+#pragma unroll
+          for (int nb = 0; nb < NB3; ++nb) mfma_chunk(acc3[mb][nb], bc[kt][s][nb], za, (bf16*)nullptr);
         }
-    // lane l holds row l%32 of row block mb, columns 8q + 4(l/32) + 0..3 of the
-    // wave's 32 columns
+    // lane l holds row l%32 of row block mb, columns 8q + 4(l/32) + 0..3 of each
+    // of the wave's 32-column blocks
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       char LR_LDS* rowp = stg + (nt & 1) * G::STG3_BUF + (mb * 32 + (lane & 31)) * G::STG3_PITCH + 8 * (lane >> 5);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x4 v = {(bf16)acc3[mb][4 * q], (bf16)acc3[mb][4 * q + 1], (bf16)acc3[mb][4 * q + 2],
-                          (bf16)acc3[mb][4 * q + 3]};
-        *reinterpret_cast<bf16x4 LR_LDS*>(rowp + (w * 32 + 8 * q) * 2) = v;
-      }
+      for (int nb = 0; nb < NB3; ++nb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc3[mb][v] = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4 v = {(bf16)acc3[mb][nb][4 * q], (bf16)acc3[mb][nb][4 * q + 1], (bf16)acc3[mb][nb][4 * q + 2],
+                            (bf16)acc3[mb][nb][4 * q + 3]};
+          *reinterpret_cast<bf16x4 LR_LDS*>(rowp + ((w * NB3 + nb) * 32 + 8 * q) * 2) = v;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc3[mb][nb][v] = 0.f;
+      }
     }
   };
   // NBUF tiles per outer step so that every buffer index is a constant.  The
