@@ -50,12 +50,12 @@ struct FusedGeo {
   static constexpr int BK1 = GR > 128 ? 32 : 64;
   // phase-1 rings: x tiles (from HBM, the MMA waves' DMA) SX stages deep, A'^T
   // tiles (L2-resident, the store waves' DMA) SA deep; each role waits only for
-  // its own loads, so the x stream keeps 7-15 stages in flight whatever A''s
-  // share of a stage
+  // its own loads, so the x stream keeps 7-15 stages in flight however large
+  // the A'^T tiles are
   static constexpr int SX = GR == 64 ? 12 : (GR == 128 ? 8 : 16);
   static constexpr int SA = 4;
   // phase 1 tile [BM, GR], k split inside the work-group, so that each wave has
-  // 6-8 independent accumulators and every LDS fragment is read by one wave (or
+  // 4-8 independent accumulators and every LDS fragment is read by one wave (or
   // one wave pair):
   //   g*r <= 128 (BK = 64, four 16-deep sub-steps per stage): MMA wave w the
   //     whole tile over sub-step w; NSP = 4 partials, added in phase 2;
@@ -68,19 +68,18 @@ struct FusedGeo {
   static constexpr int NSP = KSPLIT ? 4 : 1, NSS = KSPLIT ? 4 : 2;
   static constexpr int MB1 = 2, NB1 = KSPLIT ? GR / 32 : GR / 64;
   static_assert(C1::KS == (KSPLIT ? 4 : 2), "one k sub-step per MMA wave (pair)");
-  // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of 32
-  // columns; the B fragments of PF column tiles ahead in flight (register
-  // buffers NBUF = PF + 1), 48-64 KB per CU
-  // NB3 32-column blocks per wave and tile: two for g*r = 64 (256-column tiles,
-  // half the tiles and barriers; measured 3-4% faster), else one (the wider
-  // phase-1 shapes need the registers: two measured 5% slower for SwiGLU at 64)
+  // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of NB3
+  // 32-column blocks; the B fragments of PF column tiles ahead in flight
+  // (register buffers NBUF = PF + 1), 48-64 KB per CU.  NB3 = 2 for g*r = 64
+  // (256-column tiles, half the tiles and barriers; measured 2-4% faster), else
+  // 1 (the wider phase-1 shapes need the registers: 2 measured slower for
+  // SwiGLU at r = 64)
   static constexpr int NB3 = GR == 64 ? 2 : 1;
   static constexpr int BN3 = 128 * NB3;
   static constexpr int PF = GR == 64 ? 2 : (K3 == 64 ? 3 : (K3 == 128 ? 2 : 1));
   static constexpr int NBUF = PF + 1;
   using C3 = PipeCfg<BM, 128, 64, 2, 2, 2>;  // z fragment geometry (BK = 64)
   static constexpr int KT = K3 / 64;  // 64-deep k blocks of one branch's z
-  static constexpr int THREADS = 512;
 
   static constexpr int XB = C1::A_BYTES, AB = C1::B_BYTES;  // one x / A'^T stage
   static constexpr int X_SINK = SX * XB, A_RING = X_SINK + XB, A_SINK = A_RING + SA * AB;
@@ -120,7 +119,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool mma = wave < 4;
   const int w = wave & 3;                 // index within the role
-  const int wm = w >> 1, wn = w & 1;      // MMA wave position (2 x 2)
+  const int wm = w >> 1, wn = w & 1;      // wide phase 1: k sub-step wm, column half wn
   const int u = w * 64 + lane;            // store-role thread index 0..255
   const int m0 = blockIdx.x * G::BM;
   const int d = a.d;
