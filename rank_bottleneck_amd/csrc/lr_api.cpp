@@ -60,8 +60,8 @@ bool fused_fwd(const lr_dims* d) {
 }
 
 // A' (or A'^T), z, then for the small-rank forward the split partials and sums of
-// squares.  The one-kernel path uses A'^T and B in fragment order; z stays reserved for the shard
-// seam (lr_up_finish), which shares this size.
+// squares.  The one-kernel path uses A'^T and the B_i in fragment order; z stays
+// reserved for the shard seam (lr_up_finish), which shares this size.
 size_t fwd_ws(const lr_dims* d) {
   const size_t es = esize(d->dtype), gr = (size_t)(d->g * d->r), T = (size_t)d->T;
   if (fused_fwd(d)) return 2 * align_up((size_t)d->d * gr * es) + align_up(T * gr * es);
