@@ -236,8 +236,11 @@ def test_exact_selection_case_bitwise(T, d, r, g):
                     assert np.max(np.abs(got - exp)) <= tol, (dtype, act, i, np.max(np.abs(got - exp)))
 
 
-def test_deterministic_rerun():
-    wl = SMALL[4]
+@pytest.mark.parametrize("wl", [SMALL[4], Workload("bf16_g3_r64_rerun", 300, 256, 64, 3, "silu", "bf16")],
+                         ids=lambda w: w.name)
+def test_deterministic_rerun(wl):
+    """Bitwise-equal outputs on a second call (the grouped GEMM path, and the
+    one-kernel forward with its fixed partial-sum order)."""
     inp = make_inputs(wl, seed=5)
     dims, (x, gamma, A, B), y1, h1 = _run_fwd(wl, inp)
     y2, h2 = rb.fwd(dims, x, gamma, A, B)
