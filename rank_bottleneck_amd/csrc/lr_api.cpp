@@ -201,7 +201,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   wa.z = d->act == LR_ACT_IDENTITY ? h : z;
   wa.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
   for (int i = 0; i < n_up; ++i) { wa.dy[i] = dy[i]; wa.dB[i] = dB[i]; }
-  wa.x = x; wa.dh = dh; wa.A = A; wa.gamma = gamma; wa.dA = dA; wa.gpart = gpart; wa.ngpart = ngp;
+  wa.x = x; wa.dh = dh; wa.A = A; wa.gamma = gamma; wa.dA = dA; wa.dgamma = dgamma; wa.gpart = gpart; wa.ngpart = ngp;
   wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
   wa.nsplit = ns; wa.wpart = wpart; wa.part_stride = pstride; wa.part_offA = (int64_t)n_up * r * D;
   wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
@@ -212,8 +212,10 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
     wa.ksplit = ((ksteps + ns - 1) / ns) * BK;
   }
   LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
-  if (reduced) LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
-  LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, reduced), ngp, s));
+  if (reduced)  // the reduction also forms dgamma
+    LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
+  else          // one pass: the kernel left per-tile dgamma partials
+    LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, false), ngp, s));
 
   lr::DxArgs xa{};
   xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp; xa.spstride = sps;

@@ -77,7 +77,8 @@ struct WgradArgs {
   const void* A;
   const void* gamma;
   float* dA;
-  float* gpart;       // [d, ngpart]
+  float* dgamma;      // [d]: written by the reductions (launch_wgrad_reduce)
+  float* gpart;       // [d, ngpart]: dgamma partials of an unsplit launch_wgrad
   int ngpart;
   int T, d, r, g, n_up;
   int nsplit, ksplit;       // token splits and tokens per split (a multiple of the k step)
@@ -142,7 +143,8 @@ hipError_t launch_fold_fused(const void* A, const void* gamma, const void* const
                              int d, int na, int nb, hipStream_t s);
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
-// sums the split partials of launch_wgrad (nothing to do when nsplit == 1)
+// sums the split partials (or stream-K slots) of launch_wgrad into dB and dA and
+// forms dgamma (nothing to do when nsplit == 1 without stream-K)
 template <typename E> hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s);
 template <typename E> hipError_t launch_dx(const DxArgs& a, hipStream_t s);
 hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, int stride, hipStream_t s);

@@ -653,18 +653,51 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   }
 }
 
-// Sum the split partials in split order.  Elements [0, nB) are the dB tensors
-// (job-major), the rest dA; one thread per 4 consecutive outputs.  dA rows get
-// gamma_j and the row partial sum_c A_jc M_jc (one partial per 64-column group).
+// Reductions of the weight gradients: the dB elements one thread per 4
+// consecutive outputs; dA one work-group per row, which also forms
+// dgamma_j = sum_c A_jc M_jc (the row's partial sums added over the work-group
+// in a fixed order) and writes it, so no separate pass sums partials per row.
+__device__ __forceinline__ int64_t wred_blocks_b(const WgradArgs& a) {
+  return ((int64_t)a.n_up * a.r * a.d / 4 + 255) / 256;
+}
+__device__ __forceinline__ float wred_block_sum(float s) {
+  __shared__ float red[4];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+// dA row `row` from sum4(col) (the column's 4 summed values): dA = gamma_j * M,
+// dgamma_j = sum_c A_jc M_jc
+template <typename E, class F>
+__device__ __forceinline__ void wred_row_a(const WgradArgs& a, int row, F&& sum4) {
+  const int gr = a.g * a.r;
+  const E* Aw = static_cast<const E*>(a.A);
+  const float gj = to_f32(static_cast<const E*>(a.gamma)[row]);
+  float s = 0.f;
+  for (int c = threadIdx.x * 4; c < gr; c += 256 * 4) {
+    const float4 acc = sum4(c);
+    const float4 a4 = load4(Aw + (int64_t)row * gr + c);
+    s += a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
+    *reinterpret_cast<float4*>(a.dA + (int64_t)row * gr + c) =
+        make_float4(gj * acc.x, gj * acc.y, gj * acc.z, gj * acc.w);
+  }
+  s = wred_block_sum(s);
+  if (threadIdx.x == 0) a.dgamma[row] = s;
+}
+
+// Sum the split partials in split order.  Partial element i: [0, nB) the dB
+// tensors (job-major), then dA.  Work-groups [0, wred_blocks_b) take dB, one
+// thread per 4 consecutive outputs; the next d take one dA row each.
 template <typename E>
 __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
   const int gr = a.g * a.r;
-  const int64_t nB = (int64_t)a.n_up * a.r * a.d, nA = (int64_t)a.d * gr;
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const bool active = i < nB + nA;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (active) {
-    // up to U partial loads in flight, then added in split order
+  const int64_t nB = (int64_t)a.n_up * a.r * a.d;
+  // the 4 outputs from element i, the split partials added in split order (up
+  // to U loads in flight)
+  auto sum4 = [&](int64_t i) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     constexpr int U = 8;
     for (int s0 = 0; s0 < a.nsplit; s0 += U) {
       float4 p[U];
@@ -678,29 +711,19 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
         acc.x += p[u].x; acc.y += p[u].y; acc.z += p[u].z; acc.w += p[u].w;
       }
     }
-  }
-  if (active && i < nB) {
+    return acc;
+  };
+  const int64_t nbb = wred_blocks_b(a);
+  if ((int64_t)blockIdx.x < nbb) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= nB) return;
     const int job = (int)(i / ((int64_t)a.r * a.d));
     const int64_t k = i % ((int64_t)a.r * a.d);
-    *reinterpret_cast<float4*>(a.dB[job] + k) = acc;
+    *reinterpret_cast<float4*>(a.dB[job] + k) = sum4(i);
     return;
   }
-  // dA part: 16 threads share one 64-column group of a row (gr is a multiple of 64)
-  const int64_t k = active ? i - nB : 0;
-  const int row = (int)(k / gr), col = (int)(k % gr);
-  float s = 0.f;
-  if (active) {
-    const E* Aw = static_cast<const E*>(a.A);
-    const float gj = to_f32(static_cast<const E*>(a.gamma)[row]);
-    const float4 a4 = load4(Aw + k);
-    s = a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
-    *reinterpret_cast<float4*>(a.dA + k) = make_float4(gj * acc.x, gj * acc.y, gj * acc.z, gj * acc.w);
-  }
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  s += __shfl_xor(s, 8);
-  if (active && (threadIdx.x & 15) == 0) a.gpart[(int64_t)row * a.ngpart + col / 64] = s;
+  const int row = (int)((int64_t)blockIdx.x - nbb);
+  wred_row_a<E>(a, row, [&](int c) { return sum4(nB + (int64_t)row * gr + c); });
 }
 
 // Stream-K weight gradients.  Tiles are numbered job-major (dB_0 .. dB_{n_up-1},
@@ -783,30 +806,16 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   }
 }
 
-// Sum of each tile's stream-K slots in work-group order; one thread per 4
-// consecutive outputs, the dB tensors (job-major) first, then dA, which also gets
-// gamma_j and the row partial sum_c A_jc M_jc (one partial per 64-column group).
+// Sum of each tile's stream-K slots in work-group order.  Work-groups
+// [0, wred_blocks_b) take the dB tensors (job-major), one thread per 4
+// consecutive outputs; the next d take one dA row each.
 template <class C>
 __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
   using E = typename C::E;
   const int gr = a.g * a.r;
-  const int64_t nB = (int64_t)a.n_up * a.r * a.d, nA = (int64_t)a.d * gr;
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const bool active = i < nB + nA;
-  int job = 0, row = 0, col = 0;
-  if (active) {
-    if (i < nB) {
-      job = (int)(i / ((int64_t)a.r * a.d));
-      const int64_t k = i % ((int64_t)a.r * a.d);
-      row = (int)(k / a.d); col = (int)(k % a.d);
-    } else {
-      job = a.n_up;
-      const int64_t k = i - nB;
-      row = (int)(k / gr); col = (int)(k % gr);
-    }
-  }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (active) {
+  const int64_t nB = (int64_t)a.n_up * a.r * a.d;
+  // the 4 outputs at (job, row, col): the slots of the covering work-groups
+  auto sum4 = [&](int job, int row, int col) {
     const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
     const int tnA = (gr + C::BN - 1) / C::BN;
     const int tm = row / C::BM, tn = col / C::BN;
@@ -815,30 +824,25 @@ __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
     const int last = sk_owner((int64_t)(t + 1) * a.sk_KS - 1, a.sk_Q, a.sk_R);
     const float* slot = a.wpart + (int64_t)t * a.sk_maxseg * (C::BM * C::BN) +
                         (int64_t)(row - tm * C::BM) * C::BN + (col - tn * C::BN);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j <= last - first; ++j) {
       const float4 p = *reinterpret_cast<const float4*>(slot + (int64_t)j * (C::BM * C::BN));
       acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
     }
-  }
-  if (active && job < a.n_up) {
-    *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.d + col) = acc;
+    return acc;
+  };
+  const int64_t nbb = wred_blocks_b(a);
+  if ((int64_t)blockIdx.x < nbb) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= nB) return;
+    const int job = (int)(i / ((int64_t)a.r * a.d));
+    const int64_t k = i % ((int64_t)a.r * a.d);
+    const int row = (int)(k / a.d), col = (int)(k % a.d);
+    *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.d + col) = sum4(job, row, col);
     return;
   }
-  float s = 0.f;
-  if (active) {
-    const E* Aw = static_cast<const E*>(a.A);
-    const float gj = to_f32(static_cast<const E*>(a.gamma)[row]);
-    const float4 a4 = load4(Aw + (int64_t)row * gr + col);
-    s = a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
-    *reinterpret_cast<float4*>(a.dA + (int64_t)row * gr + col) =
-        make_float4(gj * acc.x, gj * acc.y, gj * acc.z, gj * acc.w);
-  }
-  // 16 threads share one 64-column group of a row (gr is a multiple of 64)
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  s += __shfl_xor(s, 8);
-  if (active && (threadIdx.x & 15) == 0) a.gpart[(int64_t)row * a.ngpart + col / 64] = s;
+  const int row = (int)((int64_t)blockIdx.x - nbb);
+  wred_row_a<E>(a, row, [&](int c) { return sum4(a.n_up, row, c); });
 }
 
 // rstd * S' / D of a tile's rows, one row per thread.  The S' partials of the
@@ -1299,15 +1303,16 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
 
 template <typename E>
 hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
-  const int64_t n4 = ((int64_t)a.n_up * a.r * a.d + (int64_t)a.d * a.g * a.r) / 4;
+  // dB work-groups (one thread per 4 outputs), then one work-group per dA row
+  const int64_t blocks = cdiv((int64_t)a.n_up * a.r * a.d / 4, 256) + a.d;
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (a.streamk) {
-      hipLaunchKernelGGL((k_wgrad_sk_reduce<typename Cfgs<E>::Wgrad>), dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((k_wgrad_sk_reduce<typename Cfgs<E>::Wgrad>), dim3(blocks), dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
   if (a.nsplit == 1) return hipSuccess;
-  hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
