@@ -205,7 +205,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
   wa.nsplit = ns; wa.wpart = wpart; wa.part_stride = pstride; wa.part_offA = (int64_t)n_up * r * D;
   wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
-  wa.sk_maxseg = wp.maxseg;
+  wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles;
   {
     const int BK = lr::gemm_bk<E>();   // split lengths are whole k steps
     const int ksteps = (T + BK - 1) / BK;

@@ -86,9 +86,10 @@ struct WgradArgs {
   int64_t part_stride;      // n_up*r*d + d*g*r
   int64_t part_offA;        // n_up*r*d
   // stream-K (streamk != 0): G work-groups split tiles*KS k steps evenly, the first R
-  // taking Q+1 and the rest Q; each (tile, covering work-group) writes a BM x BN
-  // fp32 slot at wpart[(tile*maxseg + ordinal) * BM*BN]
-  int streamk, sk_G, sk_Q, sk_R, sk_KS, sk_maxseg;
+  // taking Q+1 and the rest Q; each (sequence position, covering work-group) writes a
+  // BM x BN fp32 slot at wpart[(position*maxseg + ordinal) * BM*BN].  Position p
+  // holds tile (p % S) * (tiles / S) + p / S (S = 1: tile p).
+  int streamk, sk_G, sk_Q, sk_R, sk_KS, sk_maxseg, sk_S, sk_tiles;
 };
 
 // How the token-reduced weight gradients are split.
@@ -96,6 +97,7 @@ struct WgradPlan {
   int streamk;        // 1: stream-K over (tile, k step); 0: nsplit equal token splits
   int nsplit;         // token splits when !streamk (1 = one pass, no reduction)
   int G, Q, R, KS, maxseg, tiles;
+  int S;              // stream-K tile interleave (see WgradArgs)
   int64_t part_floats;  // fp32 partial floats the plan needs in the workspace
 };
 

@@ -735,6 +735,20 @@ __device__ __forceinline__ int sk_owner(int64_t q, int Q, int R) {
   return q < big ? (int)(q / (Q + 1)) : (int)(R + (q - big) / Q);
 }
 
+// The tile at sequence position p, and the position of tile t.  Work-groups w,
+// w+8, ... share an XCD (ids are dealt to the 8 XCDs in turn); when they sit S
+// tiles apart in the sequence and start at one k offset, the interleave puts the
+// tiles they run concurrently into one contiguous block of the tile order, whose
+// operand panels the XCD's L2 then shares for the token rows they stream.
+__device__ __forceinline__ int sk_tile_at(int p, int S, int tiles) {
+  const int n = tiles / S;
+  return (p % S) * n + p / S;
+}
+__device__ __forceinline__ int sk_pos_of(int t, int S, int tiles) {
+  const int n = tiles / S;
+  return (t % n) * S + t / n;
+}
+
 struct SkTile {
   int job, tm, tn, M, N;
 };
@@ -770,11 +784,11 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   const int64_t s1 = s0 + a.sk_Q + (w < a.sk_R ? 1 : 0);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   for (int64_t cur = s0; cur < s1;) {
-    const int t = (int)(cur / a.sk_KS);
+    const int t = (int)(cur / a.sk_KS);   // sequence position
     const int64_t tend = min(s1, (int64_t)(t + 1) * a.sk_KS);
     const int kk0 = (int)(cur - (int64_t)t * a.sk_KS), kk1 = (int)(tend - (int64_t)t * a.sk_KS);
     const int ord = w - sk_owner((int64_t)t * a.sk_KS, a.sk_Q, a.sk_R);
-    const SkTile st = sk_tile<C>(a, t);
+    const SkTile st = sk_tile<C>(a, sk_tile_at(t, a.sk_S, a.sk_tiles));
     const int m0 = st.tm * C::BM, n0 = st.tn * C::BN;
     const int kbeg = kk0 * C::BK;
     const int klen = min(kk1 * C::BK, a.T) - kbeg;
@@ -819,7 +833,8 @@ __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
     const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
     const int tnA = (gr + C::BN - 1) / C::BN;
     const int tm = row / C::BM, tn = col / C::BN;
-    const int t = job < a.n_up ? job * tmB * tnB + tm * tnB + tn : a.n_up * tmB * tnB + tm * tnA + tn;
+    const int t = sk_pos_of(job < a.n_up ? job * tmB * tnB + tm * tnB + tn : a.n_up * tmB * tnB + tm * tnA + tn,
+                            a.sk_S, a.sk_tiles);
     const int first = sk_owner((int64_t)t * a.sk_KS, a.sk_Q, a.sk_R);
     const int last = sk_owner((int64_t)(t + 1) * a.sk_KS - 1, a.sk_Q, a.sk_R);
     const float* slot = a.wpart + (int64_t)t * a.sk_maxseg * (C::BM * C::BN) +
@@ -1252,6 +1267,7 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
   using C = typename Cfgs<E>::Wgrad;
   const int gr = g * r;
   WgradPlan p{};
+  p.S = 1;
   p.tiles = n_up * cdiv(r, C::BM) * cdiv(d, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
   p.KS = cdiv(T, C::BK);
   const int64_t total = (int64_t)p.tiles * p.KS;
@@ -1262,6 +1278,11 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
     p.G = (int)(total / 8 < kNumCu ? total / 8 : kNumCu);
     p.Q = (int)(total / p.G);
     p.R = (int)(total % p.G);
+    // interleave S: with R == 0, work-groups w and w+8 (one XCD) start 8Q steps
+    // apart, S = 8Q / KS whole tiles when that divides, and tiles == S * G / 8
+    p.S = 1;
+    if (p.R == 0 && p.G % 8 == 0 && (8 * (int64_t)p.Q) % p.KS == 0) p.S = (int)(8 * (int64_t)p.Q / p.KS);
+    if (p.S < 1 || p.tiles % p.S != 0) p.S = 1;
     p.maxseg = 0;
     for (int t = 0; t < p.tiles; ++t) {
       const int64_t q0 = (int64_t)t * p.KS, q1 = q0 + p.KS - 1;

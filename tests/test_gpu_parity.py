@@ -122,6 +122,26 @@ def test_backward_256_tiles_ragged():
     assert_close(host(g["dB"][0]), rb_["dB"][0], wl.dtype, "dB0")
 
 
+@pytest.mark.parametrize("wl", [Workload("bf16_sk_interleave3", 2048, 2048, 512, 3, "identity", "bf16"),
+                                Workload("bf16_sk_interleave2", 2048, 1024, 1024, 1, "silu", "bf16")],
+                         ids=lambda w: w.name)
+def test_backward_streamk_interleaved(wl):
+    """Stream-K weight gradients whose tile sequence is interleaved: 96 tiles of 32
+    k steps on 256 work-groups (3 tiles between work-groups of one XCD), and 32
+    tiles of 32 k steps on 128 (2 tiles); every gradient compared in full."""
+    _say("stream-K interleave bwd", wl)
+    inp = make_inputs(wl, seed=5)
+    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy])
+    torch.cuda.synchronize()
+    ref = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), ref[k], wl.dtype, k)
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), ref["dB"][i], wl.dtype, f"dB{i}")
+
+
 @pytest.mark.parametrize("wl", [SMALL[1], SMALL[4], SMALL[5], SMALL[8], SMALL[9], SMALL[10]], ids=lambda w: w.name)
 def test_inference_forward_without_checkpoint(wl):
     inp = make_inputs(wl, seed=2, with_dy=False)
