@@ -181,7 +181,7 @@ def main():
         flops = wl.fwd_flops()
     elif wl.fwd_only:
         def step():
-            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, wsf)
+            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, None, wsf)
         flops = wl.fwd_flops()
     else:
         wsb = rb.workspace(dims, True)
@@ -189,10 +189,11 @@ def main():
         dgamma = torch.empty(wl.d, dtype=torch.float32, device="cuda")
         dA = torch.empty((wl.d, gr), dtype=torch.float32, device="cuda")
         dB = [torch.empty((wl.r, wl.d), dtype=torch.float32, device="cuda") for _ in range(nu)]
+        rstd = torch.empty(wl.T, dtype=torch.float32, device="cuda")  # kept with h for the backward
 
         def step():
-            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, wsf)
-            rb.lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, wsb)
+            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, rstd, wsf)
+            rb.lr_block_bwd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
         flops = wl.fwd_flops() + wl.bwd_flops()
 
     if args.copy_calibration:

@@ -92,21 +92,27 @@ lr_status rmsnorm_online(const lr_dims* dims, const void* x, const void* gamma, 
  *   h_save [T, g*r] (dtype): the rank-r pre-activation h, the only activation the
  *   backward needs besides x (low-rank activation checkpointing, §2.2).  NULL for
  *   inference.
- * For bf16 with g == 1, r in {64, 128, 256} and identity or SiLU, the forward is
- * one kernel and z never reaches device memory; otherwise z is written once to
- * the workspace between the two projections. */
+ *   rstd_save [T] (fp32): the RMSNorm statistic rstd_t = (sum_j x_tj^2 / D + eps)^(-1/2)
+ *   that scaled h, for lr_block_bwd to reuse instead of recomputing it from x.
+ *   NULL when not wanted.
+ * For bf16 with small g*r (r = 64 and g <= 4, r = 128 and g <= 2, r = 256 and
+ * g == 1, identity or SiLU; SwiGLU's pair at r = 64 or 128) the forward is one
+ * kernel and z never reaches device memory; otherwise z is written once to the
+ * workspace between the two projections. */
 lr_status lr_block_fwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
-                       const void* const* B, void* const* y, void* h_save,
+                       const void* const* B, void* const* y, void* h_save, float* rstd_save,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the block from the saved pre-activation.
  *   inputs : x, gamma, A, B[i] as in the forward; h_saved [T, g*r] (dtype), the
- *            forward's h_save; dy[i] [T, d] (dtype), the upstream gradients.
+ *            forward's h_save; rstd_saved [T] (fp32), the forward's rstd_save, or
+ *            NULL; dy[i] [T, d] (dtype), the upstream gradients.
  *   outputs: dx [T, d] (dtype); dgamma [d], dA [d, g*r], dB[i] [r, d] (fp32).
- * sigma is recomputed from h_saved; rstd is recomputed from x. */
+ * sigma is recomputed from h_saved; rstd is taken from rstd_saved, or recomputed
+ * from x when it is NULL (one extra pass over x). */
 lr_status lr_block_bwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
-                       const void* const* B, const void* h_saved, const void* const* dy,
-                       void* dx, float* dgamma, float* dA, float* const* dB,
+                       const void* const* B, const void* h_saved, const float* rstd_saved,
+                       const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Shard seam of bottleneck-aware tensor parallelism (§2.1: the d x r factor runs

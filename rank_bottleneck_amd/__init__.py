@@ -59,8 +59,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i64, f32p, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
     dims = ctypes.POINTER(LrDims)
     lib.rmsnorm_online.argtypes = [dims, vp, vp, vp, vp, vp, vp]
-    lib.lr_block_fwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.lr_block_bwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_fwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_bwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_down_partial.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_up_finish.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_partial", "lr_up_finish"):
@@ -135,17 +135,18 @@ def rmsnorm_online(dims: LrDims, x, gamma=None, y=None, sumsq=None, rstd=None, s
                                                     _ptr(rstd), _stream(stream)))
 
 
-def lr_block_fwd(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, ws, stream=None) -> None:
+def lr_block_fwd(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, rstd_save, ws, stream=None) -> None:
     _check("lr_block_fwd", load().lr_block_fwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
-                                                _ptr_array(y), _ptr(h_save), _ptr(ws), _ws_nbytes(ws),
-                                                _stream(stream)))
+                                                _ptr_array(y), _ptr(h_save), _ptr(rstd_save), _ptr(ws),
+                                                _ws_nbytes(ws), _stream(stream)))
 
 
-def lr_block_bwd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, dy: Sequence, dx, dgamma, dA, dB: Sequence, ws,
-                 stream=None) -> None:
+def lr_block_bwd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, rstd_saved, dy: Sequence, dx, dgamma, dA,
+                 dB: Sequence, ws, stream=None) -> None:
     _check("lr_block_bwd", load().lr_block_bwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
-                                                _ptr(h_saved), _ptr_array(dy), _ptr(dx), _ptr(dgamma), _ptr(dA),
-                                                _ptr_array(dB), _ptr(ws), _ws_nbytes(ws), _stream(stream)))
+                                                _ptr(h_saved), _ptr(rstd_saved), _ptr_array(dy), _ptr(dx),
+                                                _ptr(dgamma), _ptr(dA), _ptr_array(dB), _ptr(ws), _ws_nbytes(ws),
+                                                _stream(stream)))
 
 
 def lr_down_partial(dims: LrDims, x, gamma, A, partial, sumsq, ws, stream=None) -> None:
@@ -185,18 +186,20 @@ def workspace(dims: LrDims, backward: bool, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def fwd(dims: LrDims, x, gamma, A, B: Sequence, save_h: bool = True, ws=None, stream=None):
-    """Allocating forward: returns (list of y_i, h or None)."""
+def fwd(dims: LrDims, x, gamma, A, B: Sequence, save_h: bool = True, ws=None, stream=None, rstd=None):
+    """Allocating forward: returns (list of y_i, h or None).  rstd: an fp32 [T]
+    tensor that receives the rows' rstd, or None."""
     dt = TORCH_DTYPE[dims.dtype]
     y = [torch.empty((dims.T, dims.d), dtype=dt, device=x.device) for _ in range(n_up(dims))]
     h = torch.empty((dims.T, dims.g * dims.r), dtype=dt, device=x.device) if save_h else None
     ws = workspace(dims, False, x.device) if ws is None else ws
-    lr_block_fwd(dims, x, gamma, A, B, y, h, ws, stream)
+    lr_block_fwd(dims, x, gamma, A, B, y, h, rstd, ws, stream)
     return y, h
 
 
-def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream=None):
-    """Allocating backward: returns dict(dx, dgamma, dA, dB)."""
+def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream=None, rstd=None):
+    """Allocating backward: returns dict(dx, dgamma, dA, dB).  rstd: the forward's
+    saved rstd, or None to recompute it from x."""
     dt = TORCH_DTYPE[dims.dtype]
     dev = x.device
     dx = torch.empty((dims.T, dims.d), dtype=dt, device=dev)
@@ -204,7 +207,7 @@ def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream
     dA = torch.empty((dims.d, dims.g * dims.r), dtype=torch.float32, device=dev)
     dB = [torch.empty((dims.r, dims.d), dtype=torch.float32, device=dev) for _ in range(n_up(dims))]
     ws = workspace(dims, True, dev) if ws is None else ws
-    lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, ws, stream)
+    lr_block_bwd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, ws, stream)
     return {"dx": dx, "dgamma": dgamma, "dA": dA, "dB": dB}
 
 

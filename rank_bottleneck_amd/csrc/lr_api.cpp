@@ -120,7 +120,7 @@ struct TraceGuard {
 
 template <typename E>
 lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                   void* const* y, void* h_save, void* ws, hipStream_t s) {
+                   void* const* y, void* h_save, float* rstd_save, void* ws, hipStream_t s) {
   const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
@@ -130,7 +130,7 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
     void* Bf = cv.take<void>((size_t)D * gr * sizeof(E));
     LR_LAUNCH("fold_gamma", s, lr::launch_fold_fused(A, gamma, B, n_up, Ap, Bf, D, gr, r, s));
     lr::FusedArgs fa{};
-    fa.x = x; fa.Apt = Ap; fa.Bf = Bf; fa.h = h_save;
+    fa.x = x; fa.Apt = Ap; fa.Bf = Bf; fa.h = h_save; fa.rstd = rstd_save;
     for (int i = 0; i < n_up; ++i) fa.y[i] = y[i];
     fa.T = T; fa.d = D; fa.r = r; fa.g = g; fa.invD = inv_width(d); fa.eps = d->eps;
     LR_LAUNCH("fused", s, lr::launch_fused_fwd(fa, d->act, s));
@@ -151,12 +151,13 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
       sa.ksplit = (((D + BK - 1) / BK + ns - 1) / ns) * BK;
     }
     LR_LAUNCH("down", s, lr::launch_down_split<E>(sa, s));
-    LR_LAUNCH("finish", s, lr::launch_finish<E>(part, ssp, h_save, z, T, r, g, d->act, inv_width(d), d->eps, ns, s));
+    LR_LAUNCH("finish", s, lr::launch_finish<E>(part, ssp, h_save, z, rstd_save, T, r, g, d->act, inv_width(d),
+                                                d->eps, ns, s));
   } else {
     LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma<E>(A, gamma, Ap, D, gr, s));
-      lr::DownArgs da{};
+    lr::DownArgs da{};
     da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = g; da.act = d->act; da.mode = lr::DOWN_BLOCK;
-    da.invD = inv_width(d); da.eps = d->eps; da.h = h_save; da.z = z;
+    da.invD = inv_width(d); da.eps = d->eps; da.h = h_save; da.z = z; da.rstd = rstd_save;
     LR_LAUNCH("down", s, lr::launch_down<E>(da, s));
   }
   lr::UpArgs ua{};
@@ -171,13 +172,13 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
 
 template <typename E>
 lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                   const void* h, const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB,
-                   void* ws, hipStream_t s) {
+                   const void* h, const float* rstd_saved, const void* const* dy, void* dx, float* dgamma, float* dA,
+                   float* const* dB, void* ws, hipStream_t s) {
   const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
   const int nsp = n_up * lr::dz_nparts<E>(r);
   const int ngp = lr::wgrad_nparts<E>(gr);
   Carve cv{static_cast<char*>(ws)};
-  float* rstd = cv.take<float>((size_t)T * 4);
+  float* rstd_ws = cv.take<float>((size_t)T * 4);
   void* dh = cv.take<void>((size_t)T * gr * sizeof(E));
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
   const int sps = lr::spart_stride(nsp);
@@ -189,7 +190,13 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   const int64_t pstride = (int64_t)n_up * r * D + (int64_t)D * gr;
   float* wpart = cv.take<float>((size_t)wp.part_floats * 4);
 
-  LR_LAUNCH("rms_stats", s, lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd, T, D, inv_width(d), d->eps, s));
+  // the forward's rstd when the caller kept it, else recomputed from x
+  const float* rstd = rstd_saved;
+  if (!rstd) {
+    LR_LAUNCH("rms_stats", s,
+              lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd_ws, T, D, inv_width(d), d->eps, s));
+    rstd = rstd_ws;
+  }
 
   lr::DzArgs za{};
   for (int i = 0; i < n_up; ++i) { za.dy[i] = dy[i]; za.B[i] = B[i]; }
@@ -245,7 +252,8 @@ lr_status finish_impl(const lr_dims* d, const float* partial, const float* sumsq
   Carve cv{static_cast<char*>(ws)};
   cv.take<void>((size_t)D * gr * sizeof(E));  // same layout as the forward
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  LR_LAUNCH("finish", s, lr::launch_finish<E>(partial, sumsq, h_save, z, T, r, g, d->act, inv_width(d), d->eps, 1, s));
+  LR_LAUNCH("finish", s, lr::launch_finish<E>(partial, sumsq, h_save, z, nullptr, T, r, g, d->act, inv_width(d),
+                                              d->eps, 1, s));
   lr::UpArgs ua{};
   const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
   ua.z = z_is_h ? h_save : z;
@@ -317,33 +325,34 @@ lr_status rmsnorm_online(const lr_dims* d, const void* x, const void* gamma, voi
 }
 
 lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                       void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
+                       void* const* y, void* h_save, float* rstd_save, void* ws, size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
-  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save)) return LR_EINVAL;
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save) || !opt(rstd_save)) return LR_EINVAL;
   const int n_up = n_up_of(d);
   if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
   if ((st = check_rows_ptrs(reinterpret_cast<const void* const*>(y), n_up, d->T)) != LR_OK) return st;
   if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
-  return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, y, h_save, ws, s)
-                             : fwd_impl<float>(d, x, gamma, A, B, y, h_save, ws, s);
+  return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, y, h_save, rstd_save, ws, s)
+                             : fwd_impl<float>(d, x, gamma, A, B, y, h_save, rstd_save, ws, s);
 }
 
 lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                       const void* h_saved, const void* const* dy, void* dx, float* dgamma, float* dA,
-                       float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
+                       const void* h_saved, const float* rstd_saved, const void* const* dy, void* dx,
+                       float* dgamma, float* dA, float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
-  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(h_saved, d->T) || !req_rows(dx, d->T) ||
-      !req(dgamma) || !req(dA))
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(h_saved, d->T) || !opt(rstd_saved) ||
+      !req_rows(dx, d->T) || !req(dgamma) || !req(dA))
     return LR_EINVAL;
   const int n_up = n_up_of(d);
   if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
   if ((st = check_rows_ptrs(dy, n_up, d->T)) != LR_OK) return st;
   if ((st = check_ptrs(reinterpret_cast<const void* const*>(dB), n_up)) != LR_OK) return st;
   if ((st = check_ws(ws, ws_bytes, bwd_ws(d))) != LR_OK) return st;
-  return d->dtype == LR_BF16 ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, dy, dx, dgamma, dA, dB, ws, s)
-                             : bwd_impl<float>(d, x, gamma, A, B, h_saved, dy, dx, dgamma, dA, dB, ws, s);
+  return d->dtype == LR_BF16 ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx, dgamma, dA, dB, ws, s)
+                             : bwd_impl<float>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx, dgamma, dA, dB, ws,
+                                               s);
 }
 
 lr_status lr_down_partial(const lr_dims* d, const void* x, const void* gamma, const void* A, float* partial,

@@ -264,6 +264,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int pp = 1; pp < G::NSS; ++pp) ssr += ssp[pp * G::BM + rl];
       const float rs = __builtin_amdgcn_rsqf(ssr * a.invD + a.eps);
+      if (a.rstd && c == 0 && m0 + rl < a.T) a.rstd[m0 + rl] = rs;
       const float4 v = acc_at(c);
       float hv[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
       const bool keep = h && m0 + rl < a.T;

@@ -21,6 +21,7 @@ struct DownArgs {
   void* z;            // [T, g*r] (SwiGLU: [T, r]); identity: used only when h is null
   float* partial;     // DOWN_PARTIAL: [T, g*r]
   float* sumsq;       // DOWN_PARTIAL: [T]
+  float* rstd;        // DOWN_BLOCK: [T], the rows' rstd (tile column 0 writes it), or null
   int tile0;          // first tile of this launch (launch_down sets it)
 };
 
@@ -42,6 +43,7 @@ struct FusedArgs {
   const void* Bf;     // the n_up matrices B_i [r, d] in MFMA fragment order, one after another
   void* y[MAX_G];     // n_up x [T, d]
   void* h;            // [T, g*r] or null
+  float* rstd;        // [T] or null: the rows' rstd
   int T, d, r, g;
   float invD, eps;
 };
@@ -122,10 +124,11 @@ template <typename E> hipError_t launch_down(const DownArgs& a, hipStream_t s);
 // whether launch_down picks its 64-row tiles for this shape (fewer 256 x 256 tiles than CUs)
 template <typename E> bool down_uses_skinny(int T, int r, int g, bool gateup);
 template <typename E> hipError_t launch_up(const UpArgs& a, int n_up, hipStream_t s);
-// h = rstd * sum of the nsplit partials, z = sigma(h); partial [nsplit][T][g*r], sumsq [nsplit][T]
-template <typename E> hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, int T,
-                                               int r, int g, int act, float invD, float eps, int nsplit,
-                                               hipStream_t s);
+// h = rstd * sum of the nsplit partials, z = sigma(h); partial [nsplit][T][g*r], sumsq [nsplit][T];
+// rstd [T] written when non-null
+template <typename E> hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z,
+                                               float* rstd, int T, int r, int g, int act, float invD, float eps,
+                                               int nsplit, hipStream_t s);
 // A'^T [n, d] = (diag(gamma) A)^T for A [d, n]
 template <typename E> hipError_t launch_fold_gamma_t(const void* A, const void* gamma, void* Apt, int d, int n,
                                                      hipStream_t s);

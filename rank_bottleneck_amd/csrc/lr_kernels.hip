@@ -5,11 +5,11 @@
 //   down       : acc = x . A'  with the per-token sum of squares of x accumulated
 //                from the same x tiles on their way to LDS (Online-RMSNorm: the
 //                statistic is local, the normalisation is applied late), then
-//                h = rstd * acc, sigma(h) in fp32 registers; writes h (checkpoint)
-//                and z = sigma(h).  SwiGLU pairs gate/up columns in one lane.
+//                h = rstd * acc, sigma(h) in fp32 registers; writes h (checkpoint),
+//                rstd when kept, and z = sigma(h).  SwiGLU pairs gate/up columns in one lane.
 //   up         : y_i = z_i . B_i, batched over branches (one launch).
-// Backward (lr_block_bwd), with h' = rstd * dh (rstd recomputed from x):
-//   stats      : rstd from x
+// Backward (lr_block_bwd), with h' = rstd * dh (rstd the forward's, or recomputed):
+//   stats      : rstd from x, when the forward's was not kept
 //   dz         : dz_i = dy_i . B_i^T; epilogue: dh from sigma'(h_saved), writes
 //                dh' = rstd*dh, z = sigma(h) and per-row partials of
 //                S'_t = sum_c dh'_tc h_tc
@@ -120,8 +120,8 @@ __global__ __launch_bounds__(256) void k_fold_gamma_t(const E* __restrict__ A, c
 // one thread per 4 consecutive output columns of a row
 template <typename E>
 __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partial, const float* __restrict__ sumsq,
-                                                E* __restrict__ h, E* __restrict__ z, int T, int r, int g,
-                                                int act, float invD, float eps, int nsplit) {
+                                                E* __restrict__ h, E* __restrict__ z, float* __restrict__ rstd,
+                                                int T, int r, int g, int act, float invD, float eps, int nsplit) {
   const int gr = g * r;
   const int ncols = (act == ACT_SWIGLU) ? r : gr;
   const int q4 = ncols / 4;
@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
   float ss = 0.f;
   for (int k = 0; k < nsplit; ++k) ss += sumsq[(int64_t)k * T + t];
   const float rs = 1.0f / sqrtf(ss * invD + eps);
+  if (rstd && c == 0) rstd[t] = rs;
   const float* pr = partial + (int64_t)t * gr;
   auto col4 = [&](int cc) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -245,7 +246,9 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, uint4* lds, int bid
     if (a.mode == DOWN_PARTIAL) {
       if (tn == 0 && m0 + i < a.T) a.sumsq[m0 + i] = ssv;
     } else {
-      rowss[i] = __builtin_amdgcn_rsqf(ssv * a.invD + a.eps);
+      const float rs = __builtin_amdgcn_rsqf(ssv * a.invD + a.eps);
+      rowss[i] = rs;
+      if (a.rstd && tn == 0 && m0 + i < a.T) a.rstd[m0 + i] = rs;
     }
   }
   __syncthreads();
@@ -1195,12 +1198,12 @@ hipError_t launch_down_split(const SplitDownArgs& a, hipStream_t s) {
 }
 
 template <typename E>
-hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, int T, int r, int g, int act,
-                         float invD, float eps, int nsplit, hipStream_t s) {
+hipError_t launch_finish(const float* partial, const float* sumsq, void* h, void* z, float* rstd, int T, int r,
+                         int g, int act, float invD, float eps, int nsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int ncols = act == ACT_SWIGLU ? r : g * r;
   hipLaunchKernelGGL(k_finish<E>, dim3(cdiv((int64_t)T * (ncols / 4), 256)), dim3(256), 0, s, partial, sumsq,
-                     static_cast<E*>(h), static_cast<E*>(z), T, r, g, act, invD, eps, nsplit);
+                     static_cast<E*>(h), static_cast<E*>(z), rstd, T, r, g, act, invD, eps, nsplit);
   return hipGetLastError();
 }
 
@@ -1360,8 +1363,10 @@ template hipError_t launch_down<bf16>(const DownArgs&, hipStream_t);
 template hipError_t launch_down<float>(const DownArgs&, hipStream_t);
 template hipError_t launch_up<bf16>(const UpArgs&, int, hipStream_t);
 template hipError_t launch_up<float>(const UpArgs&, int, hipStream_t);
-template hipError_t launch_finish<bf16>(const float*, const float*, void*, void*, int, int, int, int, float, float, int, hipStream_t);
-template hipError_t launch_finish<float>(const float*, const float*, void*, void*, int, int, int, int, float, float, int, hipStream_t);
+template hipError_t launch_finish<bf16>(const float*, const float*, void*, void*, float*, int, int, int, int, float,
+                                        float, int, hipStream_t);
+template hipError_t launch_finish<float>(const float*, const float*, void*, void*, float*, int, int, int, int, float,
+                                         float, int, hipStream_t);
 template hipError_t launch_fold_gamma_t<bf16>(const void*, const void*, void*, int, int, hipStream_t);
 template hipError_t launch_fold_gamma_t<float>(const void*, const void*, void*, int, int, hipStream_t);
 template int small_rank_splits<bf16>(int, int, int, int, int);

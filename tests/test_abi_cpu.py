@@ -49,12 +49,12 @@ def test_workspace_sizes():
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its host checks
 
 
-def _call_fwd(dims, x=FAKE, gamma=FAKE, A=FAKE, nB=None, h=None, ws=FAKE, ws_bytes=1 << 40):
+def _call_fwd(dims, x=FAKE, gamma=FAKE, A=FAKE, nB=None, h=None, rstd=None, ws=FAKE, ws_bytes=1 << 40):
     lib = rb.load()
     n = rb.n_up(dims) if nB is None else nB
     B = (ctypes.c_void_p * max(n, 1))(*([FAKE] * n))
     y = (ctypes.c_void_p * max(n, 1))(*([FAKE] * n))
-    return lib.lr_block_fwd(ctypes.byref(dims), x, gamma, A, B, y, h, ws, ws_bytes, None)
+    return lib.lr_block_fwd(ctypes.byref(dims), x, gamma, A, B, y, h, rstd, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -80,7 +80,7 @@ def test_bad_enums_rejected():
     dims = rb.make_dims(64, 128, 64, 1)
     dims.act = 5
     assert _call_fwd(dims) == rb.LR_EINVAL
-    assert rb.load().lr_block_fwd(None, FAKE, FAKE, FAKE, None, None, None, FAKE, 1, None) == rb.LR_EINVAL
+    assert rb.load().lr_block_fwd(None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, 1, None) == rb.LR_EINVAL
 
 
 def test_bad_pointers_rejected():
@@ -88,6 +88,7 @@ def test_bad_pointers_rejected():
     assert _call_fwd(dims, x=None) == rb.LR_EINVAL
     assert _call_fwd(dims, A=FAKE + 2) == rb.LR_EINVAL           # misaligned
     assert _call_fwd(dims, h=FAKE + 8) == rb.LR_EINVAL
+    assert _call_fwd(dims, rstd=FAKE + 4) == rb.LR_EINVAL
     assert _call_fwd(dims, nB=1) == rb.LR_EINVAL                 # second B pointer null
 
 
@@ -99,8 +100,10 @@ def test_workspace_checked():
     lib = rb.load()
     z = ctypes.c_void_p(FAKE)
     arr = (ctypes.c_void_p * 1)(FAKE)
-    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, arr, FAKE, FAKE, FAKE, arr,
+    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, None, arr, FAKE, FAKE, FAKE, arr,
                             FAKE, rb.lr_block_workspace_size(dims, True) - 1, None) == rb.LR_EWORKSPACE
+    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, FAKE + 4, arr, FAKE, FAKE, FAKE, arr,
+                            FAKE, 1 << 40, None) == rb.LR_EINVAL   # misaligned rstd_saved
     assert lib.lr_down_partial(ctypes.byref(dims), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == rb.LR_EINVAL
     assert lib.lr_up_finish(ctypes.byref(dims), FAKE, FAKE, arr, arr, None, None, 0, None) == rb.LR_EWORKSPACE
 

@@ -122,6 +122,34 @@ def test_backward_256_tiles_ragged():
     assert_close(host(g["dB"][0]), rb_["dB"][0], wl.dtype, "dB0")
 
 
+@pytest.mark.parametrize("wl", [SMALL[1], SMALL[2], SMALL[4], SMALL[5], SMALL[6], SMALL[7], SMALL[8], SMALL[13],
+                                SMALL[15]], ids=lambda w: w.name)
+def test_saved_rstd(wl):
+    """The forward's rstd output (every forward path: 256 x 256 tiles, SwiGLU's
+    gate/up tiles, fp32, the one-kernel forward alone and with grouped branches,
+    the split-K small-rank path, a normalisation width other than d) against the
+    oracle's statistic, and the backward fed that saved rstd."""
+    _say("saved rstd", wl)
+    inp = make_inputs(wl, seed=7)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    rstd = torch.full((wl.T,), float("nan"), dtype=torch.float32, device="cuda")
+    y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd)
+    torch.cuda.synchronize()
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(rstd), ref["rstd"], "f32", "rstd")
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy], rstd=rstd)
+    torch.cuda.synchronize()
+    rb_ = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), rb_[k], wl.dtype, k)
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
+
+
 @pytest.mark.parametrize("wl", [Workload("bf16_sk_interleave3", 2048, 2048, 512, 3, "identity", "bf16"),
                                 Workload("bf16_sk_interleave2", 2048, 1024, 1024, 1, "silu", "bf16")],
                          ids=lambda w: w.name)
@@ -295,7 +323,7 @@ def test_status_on_bad_call_launches_nothing():
     dims = rb.make_dims(64, 100, 64, 1)
     x = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rb.LrError) as e:
-        rb.lr_block_fwd(dims, x, x, x, [x], [x], None, x)
+        rb.lr_block_fwd(dims, x, x, x, [x], [x], None, None, x)
     assert e.value.status == rb.LR_EUNSUPPORTED
 
 
@@ -348,12 +376,18 @@ def test_full_size_backward(name):
     wl = WORKLOADS[name]
     _say("full bwd", wl)
     inp = make_inputs(wl, seed=0)
-    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    # as the benchmark runs the step: rstd kept from the forward
+    rstd = torch.full((wl.T,), float("nan"), dtype=torch.float32, device="cuda")
+    y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd)
     del y
-    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy])
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy], rstd=rstd)
     torch.cuda.synchronize()
     ref = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
                            wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(rstd), ref["rstd"], "f32", "rstd")
     assert_close(host(g["dx"]), ref["dx"], wl.dtype, "dx")
     assert_close(host(g["dgamma"]), ref["dgamma"], wl.dtype, "dgamma")
     assert_close(host(g["dA"]), ref["dA"], wl.dtype, "dA")
