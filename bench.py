@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -27,6 +28,8 @@ METRIC = "low-rank block fwd+bwd TFLOP/s (bf16) and % MFMA peak; tokens/s per bl
 METRIC_FWD = "low-rank block forward HBM GB/s (small-rank, memory-bound sweep)"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (published)
 PEAK_GBS = 8000.0                                # MI355X HBM3E (published)
+WARM_S = 0.5     # default untimed warm-up, seconds of steps
+TIMED_S = 0.25   # default timed region, seconds of steps
 KERNEL_SOURCES = ["rank_bottleneck_amd/csrc/lr_kernels.hip", "rank_bottleneck_amd/csrc/lr_device.h",
                   "rank_bottleneck_amd/csrc/lr_kernels.h", "rank_bottleneck_amd/csrc/lr_pipe.h",
                   "rank_bottleneck_amd/csrc/lr_fused.hip"]
@@ -133,8 +136,10 @@ def cpu_baseline(wl, budget_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: about %.2f s of steps, at least 20)" % TIMED_S)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: about %.1f s of steps, at least 20)" % WARM_S)
     ap.add_argument("--workload", default="qkv_identity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work on the host")
@@ -204,9 +209,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Default step counts follow time: the GPU raises its clocks over the first
+    # tens of milliseconds of sustained work (a 20-step run after 5 warm-up steps
+    # measured ~10% below the steady rate), so the untimed warm-up lasts about
+    # WARM_S and the timed region about TIMED_S.  Three calibration steps count
+    # as warm-up.
+    done = 0
+    if args.warmup is None or args.steps is None:
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - c0) / 3
+        done = 3
+        if args.warmup is None:
+            args.warmup = max(20, math.ceil(WARM_S / per))
+        if args.steps is None:
+            args.steps = max(20, math.ceil(TIMED_S / per))
     # warm-up; the last warm-up step is traced per kernel to find the dominant one
-    for i in range(max(args.warmup - 1, 0)):
+    for i in range(max(args.warmup - done - 1, 0)):
         step()
+    args.warmup = done + max(args.warmup - done - 1, 0) + 1
     rb.lr_trace_begin(None, 64)
     step()
     per_kernel = {}
