@@ -311,8 +311,9 @@ def test_empty_batch():
     gamma = torch.ones(256, dtype=dt, device="cuda")
     A = torch.randn(256, 192, device="cuda").to(dt)
     B = [torch.randn(64, 256, device="cuda").to(dt) for _ in range(3)]
-    y, h = rb.fwd(dims, x, gamma, A, B)
-    g = rb.bwd(dims, x, gamma, A, B, h, [torch.empty((0, 256), dtype=dt, device="cuda")] * 3)
+    rstd = torch.empty(0, dtype=torch.float32, device="cuda")
+    y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd)
+    g = rb.bwd(dims, x, gamma, A, B, h, [torch.empty((0, 256), dtype=dt, device="cuda")] * 3, rstd=rstd)
     torch.cuda.synchronize()
     assert y[0].shape == (0, 256) and h.shape == (0, 192)
     assert float(g["dA"].abs().max()) == 0.0 and float(g["dgamma"].abs().max()) == 0.0
