@@ -101,10 +101,8 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
 
-    def run(rows):
-        inp = make_inputs(wl, seed=0, rows=rows)
+    def oracle_pass(inp):
         args = (inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B])
-        t0 = time.perf_counter()
         if wl.seam:
             p, ss = oracle.down_partial(*args[:3])
             oracle.up_finish(p, ss, args[3], wl.r, wl.g, wl.act, wl.eps, wl.D)
@@ -113,23 +111,38 @@ def cpu_baseline(wl, budget_s: float = 15.0):
         else:
             oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D)
             oracle.block_bwd(*args, [t.v for t in inp.dy], wl.r, wl.g, wl.act, wl.eps, wl.D)
+
+    def run(inp, reps=1):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle_pass(inp)
         return time.perf_counter() - t0
 
     probe = min(wl.T, 256)
-    tp = run(probe)
+    tp = run(make_inputs(wl, seed=0, rows=probe))
     rows = int(min(wl.T, max(probe, probe * budget_s / max(tp, 1e-3))))
     rows = max(probe, rows // 64 * 64) if rows < wl.T else wl.T
     log(f"cpu oracle: probe {probe} rows {tp:.2f}s -> sample {rows} rows")
-    t = run(rows)
+    inp = make_inputs(wl, seed=0, rows=rows)
+    total, passes = run(inp), 1
+    # a sample that is the whole workload and ends well inside the budget is
+    # repeated on the same inputs until the budget is spent; t is per pass
+    if rows == wl.T and total < budget_s / 2:
+        more = min(int(budget_s / total) - 1, 50)
+        total += run(inp, more)
+        passes += more
+    t = total / passes
+    what = (f"first {rows} of {wl.T} tokens" if rows < wl.T else
+            f"all {wl.T} tokens, {passes} pass{'es' if passes > 1 else ''}")
     sub = wl.replace(T=rows)
     if wl.fwd_only and wl.hbm_metric:
         return {"value": sub.fwd_bytes() / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy forward, {t:.1f} s",
+                "sample": f"{what}, seed 0, float64 NumPy forward, {t:.2f} s per pass ({total:.1f} s)",
                 "tokens_per_s": rows / t}
     flops = sub.fwd_flops() + (0 if (wl.seam or wl.fwd_only) else sub.bwd_flops())
     step = "forward" if (wl.seam or wl.fwd_only) else "fwd+bwd"
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {wl.T} tokens, seed 0, float64 NumPy {step}, {t:.1f} s",
+            "sample": f"{what}, seed 0, float64 NumPy {step}, {t:.2f} s per pass ({total:.1f} s)",
             "tokens_per_s": rows / t}
 
 
