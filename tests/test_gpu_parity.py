@@ -344,10 +344,17 @@ def test_full_size_forward_sampled_rows(name):
     wl = WORKLOADS[name]
     _say("full fwd", wl)
     inp = make_inputs(wl, seed=0, with_dy=False)
-    _, _, y, h = _run_fwd(wl, inp)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    rstd = torch.full((wl.T,), float("nan"), dtype=torch.float32, device="cuda")
+    y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd)
+    torch.cuda.synchronize()
     rows = _sample_rows(wl.T)
     ref = oracle.block_fwd(inp.x.v[rows], inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act,
                            wl.eps, wl.D)
+    assert_close(host(rstd[torch.as_tensor(rows, device="cuda")]), ref["rstd"], "f32", "rstd rows")
+    assert np.all(np.isfinite(host(rstd))), "rstd: a row was not written"
     assert_close(host(h[torch.as_tensor(rows, device="cuda")]), ref["h"], wl.dtype, "h rows")
     for i, yi in enumerate(y):
         assert_close(host(yi[torch.as_tensor(rows, device="cuda")]), ref["y"][i], wl.dtype, f"y{i} rows")
