@@ -225,17 +225,18 @@ def main():
     # Default step counts follow time: the GPU raises its clocks over the first
     # tens of milliseconds of sustained work (a 20-step run after 5 warm-up steps
     # measured ~10% below the steady rate), so the untimed warm-up lasts about
-    # WARM_S and the timed region about TIMED_S.  Three calibration steps count
-    # as warm-up.
+    # WARM_S and the timed region about TIMED_S.  The calibration (one step for
+    # first-call costs, then three timed on the host clock) counts as warm-up.
     done = 0
     if args.warmup is None or args.steps is None:
+        step()
         torch.cuda.synchronize()
         c0 = time.perf_counter()
         for _ in range(3):
             step()
         torch.cuda.synchronize()
         per = (time.perf_counter() - c0) / 3
-        done = 3
+        done = 4
         if args.warmup is None:
             args.warmup = max(20, math.ceil(WARM_S / per))
         if args.steps is None:
