@@ -21,7 +21,7 @@ and library routines (see each test's docstring).  No function is "parity
 unpinned".
 """
 from .block import (act_forward, act_backward, rms_stats, rmsnorm, block_fwd, block_bwd,
-                    down_partial, up_finish, branch_slices)
+                    down_partial, up_finish, branch_slices, working_precision)
 
 __all__ = ["act_forward", "act_backward", "rms_stats", "rmsnorm", "block_fwd", "block_bwd",
-           "down_partial", "up_finish", "branch_slices"]
+           "down_partial", "up_finish", "branch_slices", "working_precision"]

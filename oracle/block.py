@@ -21,17 +21,45 @@ residual):
     y_i    = z_i . B_i                            [T, d]
 
 Everything is float64 with no intermediate rounding; library matmuls are used as
-steps and nothing is blocked, fused or reordered.
+steps and nothing is blocked, fused or reordered.  ``working_precision`` runs the
+same code in another NumPy float type (float32 for the CPU speed baseline); the
+tests and the parity checks use the float64 default.
+
+Residual variant (reading: the block is the body of a pre-norm transformer
+sublayer of the LLaMA-2 models the pages train, technical summary §4, whose
+output adds the sublayer's input back):
+
+    y_i    = residual_i + z_i . B_i              (residual_i [T, d], given)
+    dx     = (the block's dx) + dx_residual      (dx_residual [T, d], given: the
+                                                   gradient reaching x through the
+                                                   residual path, e.g. dy_0 when
+                                                   residual_0 = x)
 """
 from __future__ import annotations
 
 from typing import Dict, List, Sequence, Tuple
 
+import contextlib
+
 import numpy as np
+
+_DTYPE = np.float64
+
+
+@contextlib.contextmanager
+def working_precision(dtype):
+    """Run the oracle's arithmetic in `dtype` (np.float64 by default) inside the
+    block; the formulas are unchanged, only the arrays' float type."""
+    global _DTYPE
+    old, _DTYPE = _DTYPE, np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _DTYPE = old
 
 
 def _f64(a) -> np.ndarray:
-    return np.asarray(a, dtype=np.float64)
+    return np.asarray(a, dtype=_DTYPE)
 
 
 def branch_slices(r: int, g: int) -> List[slice]:
@@ -113,24 +141,32 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, D: int = 0):
 
 
 # ----------------------------------------------------------------------------- block
-def block_fwd(x, gamma, A, B: Sequence, r: int, g: int, act: str, eps: float, D: int = 0) -> Dict:
+def block_fwd(x, gamma, A, B: Sequence, r: int, g: int, act: str, eps: float, D: int = 0,
+              residual: Sequence = None) -> Dict:
     """Forward of the block.  Returns y (list of [T, d]), h (the checkpoint),
-    z (list), xn and rstd."""
+    z (list), xn and rstd.  With `residual` (a list of n_up [T, d] arrays),
+    y_i = residual_i + z_i . B_i."""
     x, gamma, A = _f64(x), _f64(gamma), _f64(A)
     xn, ss, rstd = rmsnorm(x, gamma, eps, D)
     h = xn @ A                                           # grouped down-projection
     z = act_forward(h, act, r, g)
     y = [zi @ _f64(Bi) for zi, Bi in zip(z, B)]          # batched up-projection
+    if residual is not None:
+        if len(residual) != len(y):
+            raise ValueError("one residual per up-projection")
+        y = [yi + _f64(ri) for yi, ri in zip(y, residual)]
     return {"y": y, "h": h, "z": z, "xn": xn, "rstd": rstd, "ss": ss}
 
 
 def block_bwd(x, gamma, A, B: Sequence, dy: Sequence, r: int, g: int, act: str, eps: float,
-              D: int = 0) -> Dict:
+              D: int = 0, dx_residual=None) -> Dict:
     """Backward of the block for upstream gradients dy_i.  The activation is
     recomputed from the rank-r pre-activation h (§2.2 "low-rank activation
     checkpointing": only the narrow tensor is kept); in float64 the recomputed
     h equals the forward one.  Returns dx, dgamma, dA, dB (list) and the
-    intermediates dz, dh, dxn."""
+    intermediates dz, dh, dxn.  `dx_residual` ([T, d]), when given, is added to
+    dx: the gradient that reaches x through the residual path (the residual
+    added in the forward does not change dB, dz or anything upstream of y)."""
     x, gamma, A = _f64(x), _f64(gamma), _f64(A)
     T, d = x.shape
     D = D or d
@@ -145,6 +181,8 @@ def block_bwd(x, gamma, A, B: Sequence, dy: Sequence, r: int, g: int, act: str, 
     dgamma = np.sum(dxn * x * rstd[:, None], axis=0)
     dot = np.sum(dxn * gamma[None, :] * x, axis=1)       # sum_k gamma_k dxn_tk x_tk
     dx = rstd[:, None] * (gamma[None, :] * dxn - x * (rstd * rstd * dot / D)[:, None])
+    if dx_residual is not None:
+        dx = dx + _f64(dx_residual)
     return {"dx": dx, "dgamma": dgamma, "dA": dA, "dB": dB, "dz": dz, "dh": dh, "dxn": dxn,
             "h": h, "rstd": rstd}
 

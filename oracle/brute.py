@@ -14,7 +14,9 @@ def silu(v: float) -> float:
 
 def block_fwd_loops(x: List[List[float]], gamma: List[float], A: List[List[float]],
                     B: List[List[List[float]]], r: int, g: int, act: str, eps: float,
-                    D: int = 0) -> List[List[List[float]]]:
+                    D: int = 0, residual=None) -> List[List[List[float]]]:
+    """y_i[t][j] for every up-projection i; `residual` (n_up lists [T][d]) is
+    added to each output element when given."""
     T, d = len(x), len(x[0])
     D = D or d
     ys = []
@@ -45,5 +47,7 @@ def block_fwd_loops(x: List[List[float]], gamma: List[float], A: List[List[float
                 s = 0.0
                 for k in range(r):
                     s += zs[i][k] * B[i][k][j]
+                if residual is not None:
+                    s += residual[i][t][j]
                 ys[i][t][j] = s
     return ys

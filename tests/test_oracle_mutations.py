@@ -31,6 +31,9 @@ MUTATIONS = {
                             "return x * rstd[:, None] * np.abs(_f64(gamma))[None, :], ss, rstd"),
     "branch_offset": ("return [slice(i * r, (i + 1) * r) for i in range(g)]",
                       "return [slice(i * r, (i + 1) * r) for i in range(g)][::-1]"),
+    "residual_dropped": ("y = [yi + _f64(ri) for yi, ri in zip(y, residual)]",
+                         "y = [yi + 0.0 * _f64(ri) for yi, ri in zip(y, residual)]"),
+    "dx_residual_dropped": ("dx = dx + _f64(dx_residual)", "dx = dx - 0.0 * _f64(dx_residual)"),
 }
 
 
@@ -85,6 +88,21 @@ def _pins_hold(o) -> bool:
         ok &= all(_rel(a, b) < 1e-12 for a, b in zip(u["y"], f["y"]))
         y_lib = torch.nn.functional.rms_norm(torch.tensor(x), (d,), weight=torch.tensor(gamma), eps=eps)
         ok &= _rel(o.rmsnorm(x, gamma, eps)[0], y_lib.numpy()) < 1e-13
+        # residual sublayer out = x + block(x) (first branch): loops and autograd
+        res = [x] * n_up
+        fr = o.block_fwd(x, gamma, A, B, r, g, act, eps, residual=res)
+        ylr = brute.block_fwd_loops(x.tolist(), gamma.tolist(), A.tolist(), [b.tolist() for b in B], r, g, act, eps,
+                                    residual=[x.tolist()] * n_up)
+        ok &= all(_rel(a, b) < 1e-12 for a, b in zip(fr["y"], ylr))
+        tx2 = torch.tensor(x, requires_grad=True)
+        xn2 = torch.nn.functional.rms_norm(tx2, (d,), weight=torch.tensor(gamma), eps=eps)
+        h2 = xn2 @ torch.tensor(A)
+        hs2 = [h2[:, i * r:(i + 1) * r] for i in range(g)]
+        z2 = hs2 if act == "identity" else ([torch.nn.functional.silu(v) for v in hs2] if act == "silu"
+                                            else [torch.nn.functional.silu(hs2[0]) * hs2[1]])
+        ((tx2 + z2[0] @ torch.tensor(B[0])) * torch.tensor(dy[0])).sum().backward()
+        bwr = o.block_bwd(x, gamma, A, B, [dy[0]] + [0 * t for t in dy[1:]], r, g, act, eps, dx_residual=dy[0])
+        ok &= _rel(bwr["dx"], tx2.grad.numpy()) < 1e-10
     return bool(ok)
 
 

@@ -318,3 +318,84 @@ def test_btp_shard_decomposition(act, g):
         u = oracle.up_finish(P, SS, [b[:, cols] for b in B], r, g, act, eps, d)
         for i in range(len(B)):
             assert _rel(u["y"][i], f["y"][i][:, cols]) < 1e-13
+
+
+# --------------------------------------------------------------------- residual variant
+@pytest.mark.parametrize("act,g", [("identity", 3), ("silu", 1), ("swiglu", 2)])
+def test_residual_forward_matches_loops(act, g):
+    """y_i = residual_i + z_i . B_i: oracle vs the element-by-element loops."""
+    T, d, r = 5, 8, 2
+    rng = np.random.default_rng(31 + g)
+    x, gamma, A, B, _ = _rand(rng, T, d, r, g, act)
+    res = [rng.standard_normal((T, d)) for _ in B]
+    f = oracle.block_fwd(x, gamma, A, B, r, g, act, 1e-6, residual=res)
+    yl = brute.block_fwd_loops(x.tolist(), gamma.tolist(), A.tolist(), [b.tolist() for b in B], r, g, act, 1e-6,
+                               residual=[t.tolist() for t in res])
+    for yo, yb in zip(f["y"], yl):
+        assert _rel(yo, yb) < 1e-12
+
+
+@pytest.mark.parametrize("act,g", [("silu", 1), ("swiglu", 2)])
+def test_residual_sublayer_matches_torch_autograd(act, g):
+    """The pre-norm sublayer out = x + block(x) through torch autograd (torch's
+    own rms_norm and silu): the oracle forward with residual_0 = x gives out, and
+    its backward with dx_residual = dy_0 gives x.grad; the residual leaves dgamma,
+    dA and dB as they are."""
+    T, d, r, eps = 4, 12, 3, 1e-6
+    rng = np.random.default_rng(41 + g)
+    x, gamma, A, B, dy = _rand(rng, T, d, r, g, act)
+    tx = torch.tensor(x, requires_grad=True)
+    tg = torch.tensor(gamma, requires_grad=True)
+    tA = torch.tensor(A, requires_grad=True)
+    tB = [torch.tensor(b, requires_grad=True) for b in B]
+    xn = torch.nn.functional.rms_norm(tx, (d,), weight=tg, eps=eps)
+    h = xn @ tA
+    hs = [h[:, i * r:(i + 1) * r] for i in range(g)]
+    z = [torch.nn.functional.silu(hs[0])] if act == "silu" else [torch.nn.functional.silu(hs[0]) * hs[1]]
+    out = tx + z[0] @ tB[0]
+    (out * torch.tensor(dy[0])).sum().backward()
+    f = oracle.block_fwd(x, gamma, A, B, r, g, act, eps, residual=[x])
+    assert _rel(f["y"][0], out.detach().numpy()) < 1e-13
+    bw = oracle.block_bwd(x, gamma, A, B, dy, r, g, act, eps, dx_residual=dy[0])
+    assert _rel(bw["dx"], tx.grad.numpy()) < 1e-12
+    assert _rel(bw["dgamma"], tg.grad.numpy()) < 1e-12
+    assert _rel(bw["dA"], tA.grad.numpy()) < 1e-12
+    assert _rel(bw["dB"][0], tB[0].grad.numpy()) < 1e-12
+
+
+def test_residual_sublayer_central_differences():
+    """dx of out = x + block(x) (residual_0 = x, dx_residual = dy_0) vs central
+    differences of the loop forward."""
+    T, d, r, eps, act, g = 3, 6, 2, 1e-6, "silu", 1
+    rng = np.random.default_rng(53)
+    x, gamma, A, B, dy = _rand(rng, T, d, r, g, act)
+
+    def loss(xv):
+        ys = brute.block_fwd_loops(xv.tolist(), gamma.tolist(), A.tolist(), [b.tolist() for b in B], r, g, act,
+                                   eps, residual=[xv.tolist()])
+        return float(np.sum(np.asarray(ys[0]) * dy[0]))
+
+    fd = np.zeros_like(x)
+    step = 1e-6
+    for idx in np.ndindex(x.shape):
+        p = x.copy(); p[idx] += step
+        m = x.copy(); m[idx] -= step
+        fd[idx] = (loss(p) - loss(m)) / (2 * step)
+    bw = oracle.block_bwd(x, gamma, A, B, dy, r, g, act, eps, dx_residual=dy[0])
+    assert _rel(bw["dx"], fd) < 1e-6
+
+
+# --------------------------------------------------------------------- working precision
+def test_working_precision_float32():
+    """The same oracle code in float32 (the CPU speed baseline's second leg)
+    returns float32 arrays within float32 rounding of the float64 result, and
+    the default stays float64 afterwards."""
+    rng = np.random.default_rng(61)
+    x, gamma, A, B, dy = _rand(rng, 64, 128, 16, 3, "silu")
+    ref = oracle.block_bwd(x, gamma, A, B, dy, 16, 3, "silu", 1e-6)
+    with oracle.working_precision(np.float32):
+        f32 = oracle.block_bwd(x, gamma, A, B, dy, 16, 3, "silu", 1e-6)
+    assert f32["dx"].dtype == np.float32 and f32["dA"].dtype == np.float32
+    for k in ("dx", "dgamma", "dA"):
+        assert _rel(f32[k], ref[k]) < 1e-5, k
+    assert oracle.block_fwd(x, gamma, A, B, 16, 3, "silu", 1e-6)["y"][0].dtype == np.float64
