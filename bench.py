@@ -199,7 +199,7 @@ def main():
         flops = wl.fwd_flops()
     elif wl.fwd_only:
         def step():
-            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, None, wsf)
+            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, wsf)
         flops = wl.fwd_flops()
     else:
         wsb = rb.workspace(dims, True)
@@ -210,8 +210,8 @@ def main():
         rstd = torch.empty(wl.T, dtype=torch.float32, device="cuda")  # kept with h for the backward
 
         def step():
-            rb.lr_block_fwd(dims, x, gamma, A, B, y, h, rstd, wsf)
-            rb.lr_block_bwd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
+            rb.lr_block_fwd_rstd(dims, x, gamma, A, B, y, h, rstd, wsf)
+            rb.lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
         flops = wl.fwd_flops() + wl.bwd_flops()
 
     if args.copy_calibration:

@@ -92,28 +92,44 @@ lr_status rmsnorm_online(const lr_dims* dims, const void* x, const void* gamma, 
  *   h_save [T, g*r] (dtype): the rank-r pre-activation h, the only activation the
  *   backward needs besides x (low-rank activation checkpointing, §2.2).  NULL for
  *   inference.
- *   rstd_save [T] (fp32): the RMSNorm statistic rstd_t = (sum_j x_tj^2 / D + eps)^(-1/2)
- *   that scaled h, for lr_block_bwd to reuse instead of recomputing it from x.
- *   NULL when not wanted.
  * For bf16 with small g*r (r = 64 and g <= 4, r = 128 and g <= 2, r = 256 and
  * g == 1, identity or SiLU; SwiGLU's pair at r = 64 or 128) the forward is one
  * kernel and z never reaches device memory; otherwise z is written once to the
  * workspace between the two projections. */
 lr_status lr_block_fwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
-                       const void* const* B, void* const* y, void* h_save, float* rstd_save,
+                       const void* const* B, void* const* y, void* h_save,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* lr_block_fwd that also keeps the RMSNorm statistic beside the checkpoint
+ * (Online-RMSNorm and low-rank activation checkpointing, §2.2: the statistic is
+ * 4 bytes a token against 2*g*r for h, and lets the backward skip a pass over x).
+ *   rstd_save [T] (fp32): rstd_t = (sum_j x_tj^2 / D + eps)^(-1/2), the factor
+ *   that scaled row t of h; NULL behaves as lr_block_fwd.
+ * Other arguments, workspace and errors as lr_block_fwd. */
+lr_status lr_block_fwd_rstd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                            const void* const* B, void* const* y, void* h_save, float* rstd_save,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the block from the saved pre-activation.
  *   inputs : x, gamma, A, B[i] as in the forward; h_saved [T, g*r] (dtype), the
- *            forward's h_save; rstd_saved [T] (fp32), the forward's rstd_save, or
- *            NULL; dy[i] [T, d] (dtype), the upstream gradients.
+ *            forward's h_save; dy[i] [T, d] (dtype), the upstream gradients.
  *   outputs: dx [T, d] (dtype); dgamma [d], dA [d, g*r], dB[i] [r, d] (fp32).
- * sigma is recomputed from h_saved; rstd is taken from rstd_saved, or recomputed
- * from x when it is NULL (one extra pass over x). */
+ * sigma is recomputed from h_saved (low-rank activation checkpointing, §2.2);
+ * rstd is recomputed from x (one pass over x). */
 lr_status lr_block_bwd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
-                       const void* const* B, const void* h_saved, const float* rstd_saved,
+                       const void* const* B, const void* h_saved,
                        const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* lr_block_bwd that takes the forward's RMSNorm statistic instead of recomputing
+ * it from x (§2.2, as lr_block_fwd_rstd).
+ *   rstd_saved [T] (fp32): lr_block_fwd_rstd's rstd_save for the same x; NULL
+ *   behaves as lr_block_bwd.
+ * Other arguments, workspace and errors as lr_block_bwd. */
+lr_status lr_block_bwd_rstd(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                            const void* const* B, const void* h_saved, const float* rstd_saved,
+                            const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Shard seam of bottleneck-aware tensor parallelism (§2.1: the d x r factor runs
  * row-parallel over this call's slice of d; §2.2: Online-RMSNorm keeps the local
@@ -149,7 +165,8 @@ size_t lr_block_workspace_size(const lr_dims* dims, int backward);
  * "wgrad", "wgrad_reduce", "sum_parts", "dx".  This
  * per-thread trace is the only state the library keeps between calls; it owns
  * its events.
- *   lr_trace_begin: LR_EINVAL if max_launches < 1 or a trace is already active,
+ *   lr_trace_begin: LR_EINVAL if max_launches is outside [1, 65536], a trace is
+ *                   already active or its host arrays cannot be allocated;
  *                   LR_EHIP if events cannot be created.
  *   lr_trace_count: launches recorded so far (0 when no trace is active).
  *   lr_trace_elapsed: waits for launch i's end event; writes its kernel name

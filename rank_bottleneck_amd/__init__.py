@@ -41,9 +41,9 @@ class LrError(RuntimeError):
 
 
 _lib = None
-ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_partial", "lr_up_finish",
-                "lr_block_workspace_size", "lr_status_str", "lr_trace_begin", "lr_trace_count",
-                "lr_trace_elapsed", "lr_trace_end")
+ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
+                "lr_down_partial", "lr_up_finish", "lr_block_workspace_size", "lr_status_str", "lr_trace_begin",
+                "lr_trace_count", "lr_trace_elapsed", "lr_trace_end")
 
 
 def load(path: Optional[str] = None) -> ctypes.CDLL:
@@ -59,11 +59,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i64, f32p, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
     dims = ctypes.POINTER(LrDims)
     lib.rmsnorm_online.argtypes = [dims, vp, vp, vp, vp, vp, vp]
-    lib.lr_block_fwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.lr_block_bwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_fwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_fwd_rstd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_bwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_bwd_rstd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_down_partial.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_up_finish.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_bwd", "lr_down_partial", "lr_up_finish"):
+    for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
+              "lr_down_partial", "lr_up_finish"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lr_block_workspace_size.argtypes = [dims, ctypes.c_int]
     lib.lr_block_workspace_size.restype = sz
@@ -135,18 +138,34 @@ def rmsnorm_online(dims: LrDims, x, gamma=None, y=None, sumsq=None, rstd=None, s
                                                     _ptr(rstd), _stream(stream)))
 
 
-def lr_block_fwd(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, rstd_save, ws, stream=None) -> None:
+def lr_block_fwd(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, ws, stream=None) -> None:
     _check("lr_block_fwd", load().lr_block_fwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
-                                                _ptr_array(y), _ptr(h_save), _ptr(rstd_save), _ptr(ws),
-                                                _ws_nbytes(ws), _stream(stream)))
-
-
-def lr_block_bwd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, rstd_saved, dy: Sequence, dx, dgamma, dA,
-                 dB: Sequence, ws, stream=None) -> None:
-    _check("lr_block_bwd", load().lr_block_bwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
-                                                _ptr(h_saved), _ptr(rstd_saved), _ptr_array(dy), _ptr(dx),
-                                                _ptr(dgamma), _ptr(dA), _ptr_array(dB), _ptr(ws), _ws_nbytes(ws),
+                                                _ptr_array(y), _ptr(h_save), _ptr(ws), _ws_nbytes(ws),
                                                 _stream(stream)))
+
+
+def lr_block_fwd_rstd(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, rstd_save, ws,
+                      stream=None) -> None:
+    _check("lr_block_fwd_rstd", load().lr_block_fwd_rstd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A),
+                                                          _ptr_array(B), _ptr_array(y), _ptr(h_save),
+                                                          _ptr(rstd_save), _ptr(ws), _ws_nbytes(ws),
+                                                          _stream(stream)))
+
+
+def lr_block_bwd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, dy: Sequence, dx, dgamma, dA, dB: Sequence, ws,
+                 stream=None) -> None:
+    _check("lr_block_bwd", load().lr_block_bwd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B),
+                                                _ptr(h_saved), _ptr_array(dy), _ptr(dx), _ptr(dgamma), _ptr(dA),
+                                                _ptr_array(dB), _ptr(ws), _ws_nbytes(ws), _stream(stream)))
+
+
+def lr_block_bwd_rstd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, rstd_saved, dy: Sequence, dx, dgamma, dA,
+                      dB: Sequence, ws, stream=None) -> None:
+    _check("lr_block_bwd_rstd", load().lr_block_bwd_rstd(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A),
+                                                          _ptr_array(B), _ptr(h_saved), _ptr(rstd_saved),
+                                                          _ptr_array(dy), _ptr(dx), _ptr(dgamma), _ptr(dA),
+                                                          _ptr_array(dB), _ptr(ws), _ws_nbytes(ws),
+                                                          _stream(stream)))
 
 
 def lr_down_partial(dims: LrDims, x, gamma, A, partial, sumsq, ws, stream=None) -> None:
@@ -193,7 +212,10 @@ def fwd(dims: LrDims, x, gamma, A, B: Sequence, save_h: bool = True, ws=None, st
     y = [torch.empty((dims.T, dims.d), dtype=dt, device=x.device) for _ in range(n_up(dims))]
     h = torch.empty((dims.T, dims.g * dims.r), dtype=dt, device=x.device) if save_h else None
     ws = workspace(dims, False, x.device) if ws is None else ws
-    lr_block_fwd(dims, x, gamma, A, B, y, h, rstd, ws, stream)
+    if rstd is None:
+        lr_block_fwd(dims, x, gamma, A, B, y, h, ws, stream)
+    else:
+        lr_block_fwd_rstd(dims, x, gamma, A, B, y, h, rstd, ws, stream)
     return y, h
 
 
@@ -207,7 +229,10 @@ def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream
     dA = torch.empty((dims.d, dims.g * dims.r), dtype=torch.float32, device=dev)
     dB = [torch.empty((dims.r, dims.d), dtype=torch.float32, device=dev) for _ in range(n_up(dims))]
     ws = workspace(dims, True, dev) if ws is None else ws
-    lr_block_bwd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, ws, stream)
+    if rstd is None:
+        lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, ws, stream)
+    else:
+        lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, ws, stream)
     return {"dx": dx, "dgamma": dgamma, "dA": dA, "dB": dB}
 
 

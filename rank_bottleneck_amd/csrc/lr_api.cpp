@@ -87,6 +87,7 @@ size_t bwd_ws(const lr_dims* d) { return d->dtype == LR_BF16 ? bwd_ws_t<bf16>(d)
 inline lr_status hip_status(hipError_t e) { return e == hipSuccess ? LR_OK : LR_EHIP; }
 
 // Per-thread launch trace (lr_trace_*): event pairs around matching launches.
+constexpr int kMaxTraceLaunches = 1 << 16;
 struct Trace {
   bool on = false;
   char filter[32] = {0};
@@ -324,8 +325,9 @@ lr_status rmsnorm_online(const lr_dims* d, const void* x, const void* gamma, voi
   return LR_OK;
 }
 
-lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                       void* const* y, void* h_save, float* rstd_save, void* ws, size_t ws_bytes, hipStream_t s) {
+lr_status lr_block_fwd_rstd(const lr_dims* d, const void* x, const void* gamma, const void* A,
+                            const void* const* B, void* const* y, void* h_save, float* rstd_save, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
   if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save) || !opt(rstd_save)) return LR_EINVAL;
@@ -337,9 +339,15 @@ lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const
                              : fwd_impl<float>(d, x, gamma, A, B, y, h_save, rstd_save, ws, s);
 }
 
-lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                       const void* h_saved, const float* rstd_saved, const void* const* dy, void* dx,
-                       float* dgamma, float* dA, float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
+lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                       void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
+  return lr_block_fwd_rstd(d, x, gamma, A, B, y, h_save, nullptr, ws, ws_bytes, s);
+}
+
+lr_status lr_block_bwd_rstd(const lr_dims* d, const void* x, const void* gamma, const void* A,
+                            const void* const* B, const void* h_saved, const float* rstd_saved,
+                            const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
   lr_status st = check_dims(d);
   if (st != LR_OK) return st;
   if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(h_saved, d->T) || !opt(rstd_saved) ||
@@ -353,6 +361,12 @@ lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const
   return d->dtype == LR_BF16 ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx, dgamma, dA, dB, ws, s)
                              : bwd_impl<float>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx, dgamma, dA, dB, ws,
                                                s);
+}
+
+lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                       const void* h_saved, const void* const* dy, void* dx, float* dgamma, float* dA,
+                       float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
+  return lr_block_bwd_rstd(d, x, gamma, A, B, h_saved, nullptr, dy, dx, dgamma, dA, dB, ws, ws_bytes, s);
 }
 
 lr_status lr_down_partial(const lr_dims* d, const void* x, const void* gamma, const void* A, float* partial,
@@ -381,9 +395,15 @@ lr_status lr_up_finish(const lr_dims* d, const float* partial, const float* sums
 
 lr_status lr_trace_begin(const char* kernel, int max_launches) {
   Trace& t = g_trace;
-  if (t.on || max_launches < 1) return LR_EINVAL;
-  t.ev = new hipEvent_t[2 * (size_t)max_launches];
-  t.names = new const char*[max_launches];
+  if (t.on || max_launches < 1 || max_launches > kMaxTraceLaunches) return LR_EINVAL;
+  t.ev = new (std::nothrow) hipEvent_t[2 * (size_t)max_launches];
+  t.names = new (std::nothrow) const char*[max_launches];
+  if (!t.ev || !t.names) {
+    delete[] t.ev;
+    delete[] t.names;
+    t = Trace{};
+    return LR_EINVAL;
+  }
   for (int i = 0; i < 2 * max_launches; ++i) {
     if (hipEventCreate(&t.ev[i]) != hipSuccess) {
       for (int j = 0; j < i; ++j) (void)hipEventDestroy(t.ev[j]);

@@ -49,12 +49,21 @@ def test_workspace_sizes():
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its host checks
 
 
-def _call_fwd(dims, x=FAKE, gamma=FAKE, A=FAKE, nB=None, h=None, rstd=None, ws=FAKE, ws_bytes=1 << 40):
+def _call_fwd(dims, x=FAKE, gamma=FAKE, A=FAKE, nB=None, h=None, rstd=None, ws=FAKE, ws_bytes=1 << 40,
+              form="plain"):
+    """lr_block_fwd (the scope table's signature, no rstd) or, with form="rstd",
+    lr_block_fwd_rstd; both must give the same status."""
     lib = rb.load()
     n = rb.n_up(dims) if nB is None else nB
     B = (ctypes.c_void_p * max(n, 1))(*([FAKE] * n))
     y = (ctypes.c_void_p * max(n, 1))(*([FAKE] * n))
-    return lib.lr_block_fwd(ctypes.byref(dims), x, gamma, A, B, y, h, rstd, ws, ws_bytes, None)
+    if form == "plain":
+        assert rstd is None
+        return lib.lr_block_fwd(ctypes.byref(dims), x, gamma, A, B, y, h, ws, ws_bytes, None)
+    return lib.lr_block_fwd_rstd(ctypes.byref(dims), x, gamma, A, B, y, h, rstd, ws, ws_bytes, None)
+
+
+FORMS = pytest.mark.parametrize("form", ["plain", "rstd"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -66,46 +75,64 @@ def _call_fwd(dims, x=FAKE, gamma=FAKE, A=FAKE, nB=None, h=None, rstd=None, ws=F
     (dict(eps=float("nan")), rb.LR_EINVAL),
     (dict(eps=-1.0), rb.LR_EINVAL),
 ])
-def test_bad_dims_rejected(kw, status):
+@FORMS
+def test_bad_dims_rejected(kw, status, form):
     args = dict(T=64, d=128, r=64, g=1, act="silu", dtype="bf16", eps=1e-6)
     args.update(kw)
     dims = rb.make_dims(**args)
-    assert _call_fwd(dims) == status
+    assert _call_fwd(dims, form=form) == status
 
 
-def test_bad_enums_rejected():
+@FORMS
+def test_bad_enums_rejected(form):
     dims = rb.make_dims(64, 128, 64, 1)
     dims.dtype = 7
-    assert _call_fwd(dims) == rb.LR_EINVAL
+    assert _call_fwd(dims, form=form) == rb.LR_EINVAL
     dims = rb.make_dims(64, 128, 64, 1)
     dims.act = 5
-    assert _call_fwd(dims) == rb.LR_EINVAL
-    assert rb.load().lr_block_fwd(None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, 1, None) == rb.LR_EINVAL
+    assert _call_fwd(dims, form=form) == rb.LR_EINVAL
+    lib = rb.load()
+    assert lib.lr_block_fwd(None, FAKE, FAKE, FAKE, None, None, None, FAKE, 1, None) == rb.LR_EINVAL
+    assert lib.lr_block_fwd_rstd(None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, 1, None) == rb.LR_EINVAL
 
 
-def test_bad_pointers_rejected():
+@FORMS
+def test_bad_pointers_rejected(form):
     dims = rb.make_dims(64, 128, 64, 2, "identity")
-    assert _call_fwd(dims, x=None) == rb.LR_EINVAL
-    assert _call_fwd(dims, A=FAKE + 2) == rb.LR_EINVAL           # misaligned
-    assert _call_fwd(dims, h=FAKE + 8) == rb.LR_EINVAL
-    assert _call_fwd(dims, rstd=FAKE + 4) == rb.LR_EINVAL
-    assert _call_fwd(dims, nB=1) == rb.LR_EINVAL                 # second B pointer null
+    assert _call_fwd(dims, x=None, form=form) == rb.LR_EINVAL
+    assert _call_fwd(dims, A=FAKE + 2, form=form) == rb.LR_EINVAL           # misaligned
+    assert _call_fwd(dims, h=FAKE + 8, form=form) == rb.LR_EINVAL
+    assert _call_fwd(dims, nB=1, form=form) == rb.LR_EINVAL                 # second B pointer null
+    if form == "rstd":
+        assert _call_fwd(dims, rstd=FAKE + 4, form=form) == rb.LR_EINVAL
 
 
 def test_workspace_checked():
     dims = rb.make_dims(64, 128, 64, 1)
     need = rb.lr_block_workspace_size(dims, False)
-    assert _call_fwd(dims, ws=None) == rb.LR_EWORKSPACE
-    assert _call_fwd(dims, ws_bytes=need - 1) == rb.LR_EWORKSPACE
+    for form in ("plain", "rstd"):
+        assert _call_fwd(dims, ws=None, form=form) == rb.LR_EWORKSPACE
+        assert _call_fwd(dims, ws_bytes=need - 1, form=form) == rb.LR_EWORKSPACE
     lib = rb.load()
-    z = ctypes.c_void_p(FAKE)
     arr = (ctypes.c_void_p * 1)(FAKE)
-    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, None, arr, FAKE, FAKE, FAKE, arr,
-                            FAKE, rb.lr_block_workspace_size(dims, True) - 1, None) == rb.LR_EWORKSPACE
-    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, FAKE + 4, arr, FAKE, FAKE, FAKE, arr,
-                            FAKE, 1 << 40, None) == rb.LR_EINVAL   # misaligned rstd_saved
+    need_b = rb.lr_block_workspace_size(dims, True)
+    # lr_block_bwd: the scope table's signature (no rstd argument)
+    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, arr, FAKE, FAKE, FAKE, arr,
+                            FAKE, need_b - 1, None) == rb.LR_EWORKSPACE
+    assert lib.lr_block_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, None, arr, FAKE, FAKE, FAKE, arr,
+                            FAKE, 1 << 40, None) == rb.LR_EINVAL   # h_saved missing
+    assert lib.lr_block_bwd_rstd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, None, arr, FAKE, FAKE, FAKE, arr,
+                                 FAKE, need_b - 1, None) == rb.LR_EWORKSPACE
+    assert lib.lr_block_bwd_rstd(ctypes.byref(dims), FAKE, FAKE, FAKE, arr, FAKE, FAKE + 4, arr, FAKE, FAKE, FAKE,
+                                 arr, FAKE, 1 << 40, None) == rb.LR_EINVAL   # misaligned rstd_saved
     assert lib.lr_down_partial(ctypes.byref(dims), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == rb.LR_EINVAL
     assert lib.lr_up_finish(ctypes.byref(dims), FAKE, FAKE, arr, arr, None, None, 0, None) == rb.LR_EWORKSPACE
+
+
+def test_trace_arguments():
+    assert rb.load().lr_trace_begin(None, 0) == rb.LR_EINVAL
+    assert rb.load().lr_trace_begin(None, (1 << 16) + 1) == rb.LR_EINVAL   # capped, nothing allocated
+    assert rb.lr_trace_count() == 0
 
 
 def test_rmsnorm_arguments():

@@ -324,7 +324,7 @@ def test_status_on_bad_call_launches_nothing():
     dims = rb.make_dims(64, 100, 64, 1)
     x = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rb.LrError) as e:
-        rb.lr_block_fwd(dims, x, x, x, [x], [x], None, None, x)
+        rb.lr_block_fwd(dims, x, x, x, [x], [x], None, x)
     assert e.value.status == rb.LR_EUNSUPPORTED
 
 
