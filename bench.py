@@ -70,8 +70,8 @@ def kernel_work(wl, name: str):
     if name == "fused":   # one-kernel small-rank forward: x, A'^T, B, y and h, each once
         return (2.0 * T * d * gr + 2.0 * T * r * d * nu,
                 e * (T * d + d * gr + nu * r * d + nu * T * d + T * gr))
-    if name == "up":
-        return 2.0 * T * r * d * nu, e * (T * r * nu + nu * r * d + nu * T * d)
+    if name == "up":   # the residual variant also reads residual_i
+        return 2.0 * T * r * d * nu, e * (T * r * nu + nu * r * d + nu * T * d * (2 if wl.residual else 1))
     if name == "dz":
         return 2.0 * T * d * r * nu, e * (nu * T * d + nu * r * d + T * gr + T * gr + T * zcols) + 4 * T
     if name == "wgrad":
@@ -79,8 +79,8 @@ def kernel_work(wl, name: str):
                 e * (T * (zcols or gr) + nu * T * d + T * d + T * gr + d * gr) + 4 * (d * gr + nu * r * d))
     if name == "wgrad_reduce":   # the split-K sum: only its fp32 results count
         return 0.0, 4 * (d * gr + nu * r * d)
-    if name == "dx":
-        return 2.0 * T * gr * d, e * (T * gr + d * gr + 2 * T * d) + 4 * T
+    if name == "dx":   # the residual variant also reads the residual path's gradient
+        return 2.0 * T * gr * d, e * (T * gr + d * gr + (3 if wl.residual else 2) * T * d) + 4 * T
     if name == "fold_gamma":   # the one-kernel small-rank path also reorders B
         return 0.0, e * (2 * d * gr + d + (2 * nu * r * d if one_kernel_forward(wl) else 0))
     if name == "rms_stats":
@@ -90,60 +90,103 @@ def kernel_work(wl, name: str):
     return 0.0, 0.0
 
 
-def cpu_baseline(wl, budget_s: float = 15.0):
-    """The oracle (float64 NumPy, as it stands) on a row sample of the same
-    workload, on the host cores; reported in the metric's unit."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def checkpoint_bytes(wl) -> dict:
+    """What the backward keeps per block: the rank-r pre-activation h (and the
+    4-byte-a-token RMSNorm statistic), against keeping the normalised input,
+    h and z as a plain autograd graph of the block would."""
+    e = 2 if wl.dtype == "bf16" else 4
+    gr = wl.g * wl.r
+    zc = wl.r if wl.act == "swiglu" else (0 if wl.act == "identity" else gr)
+    kept = e * wl.T * gr + 4 * wl.T
+    plain = e * wl.T * (wl.d + gr + zc)
+    return {"h_bytes": e * wl.T * gr, "rstd_bytes": 4 * wl.T, "kept_bytes": kept,
+            "xn_h_z_bytes": plain, "ratio": plain / kept}
+
+
+def cpu_baseline(wl, inp, budget_s: float = 24.0):
+    """The oracle as it stands (NumPy) on the host cores: float64 (the
+    correctness oracle) and the same code in float32, each timed for the
+    forward and for forward + backward, on a bounded sample of the workload's
+    tokens (the first rows of `inp`, the same seeded draw the GPU ran on; all of
+    them when they fit the budget).  `value` is the float64 leg of the step the
+    GPU figure times, in the metric's unit."""
     import oracle
-    from workloads import make_inputs
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    fwd_step = wl.seam or wl.fwd_only
 
-    def oracle_pass(inp):
-        args = (inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B])
+    def oracle_pass(rows, with_bwd):
+        x = inp.x.v[:rows]
+        args = (x, inp.gamma.v, inp.A.v, [b.v for b in inp.B])
         if wl.seam:
             p, ss = oracle.down_partial(*args[:3])
             oracle.up_finish(p, ss, args[3], wl.r, wl.g, wl.act, wl.eps, wl.D)
-        elif wl.fwd_only:
-            oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D)
-        else:
-            oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D)
-            oracle.block_bwd(*args, [t.v for t in inp.dy], wl.r, wl.g, wl.act, wl.eps, wl.D)
+            return
+        oracle.block_fwd(*args, wl.r, wl.g, wl.act, wl.eps, wl.D, residual=[x] if wl.residual else None)
+        if with_bwd:
+            dy = [t.v[:rows] for t in inp.dy]
+            oracle.block_bwd(*args, dy, wl.r, wl.g, wl.act, wl.eps, wl.D,
+                             dx_residual=dy[0] if wl.residual else None)
 
-    def run(inp, reps=1):
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            oracle_pass(inp)
-        return time.perf_counter() - t0
+    def timed(rows, with_bwd, prec, reps=1):
+        with oracle.working_precision(prec):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle_pass(rows, with_bwd)
+            return time.perf_counter() - t0
 
+    # legs: (precision, with backward, share of the budget)
+    legs = [("f64", False, 0.15), ("f32", False, 0.1)]
+    if not fwd_step:
+        legs = [("f64", True, 0.45), ("f64", False, 0.15), ("f32", True, 0.25), ("f32", False, 0.15)]
     probe = min(wl.T, 256)
-    tp = run(make_inputs(wl, seed=0, rows=probe))
-    rows = int(min(wl.T, max(probe, probe * budget_s / max(tp, 1e-3))))
-    rows = max(probe, rows // 64 * 64) if rows < wl.T else wl.T
-    log(f"cpu oracle: probe {probe} rows {tp:.2f}s -> sample {rows} rows")
-    inp = make_inputs(wl, seed=0, rows=rows)
-    total, passes = run(inp), 1
-    # a sample that is the whole workload and ends well inside the budget is
-    # repeated on the same inputs until the budget is spent; t is per pass
-    if rows == wl.T and total < budget_s / 2:
-        more = min(int(budget_s / total) - 1, 50)
-        total += run(inp, more)
-        passes += more
-    t = total / passes
+    out = {}
+    for prec, with_bwd, share in legs:
+        dt = np.float64 if prec == "f64" else np.float32
+        tp = timed(probe, with_bwd, dt)
+        leg_budget = budget_s * share
+        rows = int(min(wl.T, max(probe, probe * leg_budget / max(tp, 1e-3))))
+        rows = max(probe, rows // 64 * 64) if rows < wl.T else wl.T
+        total, passes = timed(rows, with_bwd, dt), 1
+        # a whole-workload sample that ends well inside its share is repeated on
+        # the same inputs until the share is spent; t is per pass
+        if rows == wl.T and total < leg_budget / 2:
+            more = min(int(leg_budget / total) - 1, 50)
+            total += timed(rows, with_bwd, dt, more)
+            passes += more
+        t = total / passes
+        sub = wl.replace(T=rows)
+        flops = sub.fwd_flops() + (sub.bwd_flops() if with_bwd else 0.0)
+        key = f"{prec}_{'fwd_bwd' if with_bwd else 'fwd'}"
+        out[key] = {"tflops": flops / t / 1e12, "tokens_per_s": rows / t, "s_per_pass": t, "rows": rows,
+                    "passes": passes, "fwd_gbs": sub.fwd_bytes() / t / 1e9 if not with_bwd else None}
+        log(f"cpu oracle {key}: {rows} rows, {passes} pass(es), {t:.3f} s per pass")
+    main = out["f64_fwd" if fwd_step else "f64_fwd_bwd"]
+    rows = main["rows"]
     what = (f"first {rows} of {wl.T} tokens" if rows < wl.T else
-            f"all {wl.T} tokens, {passes} pass{'es' if passes > 1 else ''}")
-    sub = wl.replace(T=rows)
+            f"all {wl.T} tokens, {main['passes']} pass{'es' if main['passes'] > 1 else ''}")
+    step = "forward" if fwd_step else "fwd+bwd"
+    sample = (f"{what}, seed 0, the float64 NumPy oracle's {step}, {main['s_per_pass']:.2f} s per pass; "
+              f"legs: float64 and float32, forward and fwd+bwd, each on its own row sample")
+    res = {"unit": "TFLOP/s", "value": main["tflops"], "cores": int(threads), "kind": "oracle", "sample": sample,
+           "tokens_per_s": main["tokens_per_s"], "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+           "legs": out}
     if wl.fwd_only and wl.hbm_metric:
-        return {"value": sub.fwd_bytes() / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"{what}, seed 0, float64 NumPy forward, {t:.2f} s per pass ({total:.1f} s)",
-                "tokens_per_s": rows / t}
-    flops = sub.fwd_flops() + (0 if (wl.seam or wl.fwd_only) else sub.bwd_flops())
-    step = "forward" if (wl.seam or wl.fwd_only) else "fwd+bwd"
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{what}, seed 0, float64 NumPy {step}, {t:.2f} s per pass ({total:.1f} s)",
-            "tokens_per_s": rows / t}
+        res["unit"], res["value"] = "GB/s", main["fwd_gbs"]
+    return res
 
 
 def main():
@@ -153,9 +196,9 @@ def main():
                     help="timed steps (default: about %.2f s of steps, at least 20)" % TIMED_S)
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default: about %.1f s of steps, at least 20)" % WARM_S)
-    ap.add_argument("--workload", default="qkv_identity")
+    ap.add_argument("--workload", default="qkv_silu_ckpt")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work on the host")
+    ap.add_argument("--cpu-budget", type=float, default=24.0, help="seconds of oracle work on the host")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy a 256 MiB buffer once (a plain copy kernel of known size, "
                          "used to scale the HBM byte counters of a profiling run)")
@@ -182,7 +225,8 @@ def main():
     x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
     B = [dev(b) for b in inp.B]
     dy = None if (wl.seam or wl.fwd_only) else [dev(t) for t in inp.dy]
-    del inp
+    if args.no_cpu_baseline:
+        del inp
     dims = rb.make_dims(wl.T, wl.d, wl.r, wl.g, wl.act, wl.dtype, wl.eps, wl.d_norm)
     dt = rb.TORCH_DTYPE[dims.dtype]
     gr, nu = wl.g * wl.r, wl.n_up
@@ -209,9 +253,14 @@ def main():
         dB = [torch.empty((wl.r, wl.d), dtype=torch.float32, device="cuda") for _ in range(nu)]
         rstd = torch.empty(wl.T, dtype=torch.float32, device="cuda")  # kept with h for the backward
 
-        def step():
-            rb.lr_block_fwd_rstd(dims, x, gamma, A, B, y, h, rstd, wsf)
-            rb.lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
+        if wl.residual:   # the sublayer out = x + block(x): residual add and dy -> dx fused
+            def step():
+                rb.lr_block_fwd_residual(dims, x, gamma, A, B, [x], y, h, rstd, wsf)
+                rb.lr_block_bwd_residual(dims, x, gamma, A, B, h, rstd, dy, dy[0], dx, dgamma, dA, dB, wsb)
+        else:
+            def step():
+                rb.lr_block_fwd_rstd(dims, x, gamma, A, B, y, h, rstd, wsf)
+                rb.lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
         flops = wl.fwd_flops() + wl.bwd_flops()
 
     if args.copy_calibration:
@@ -307,16 +356,18 @@ def main():
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
            "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "r": wl.r, "g": wl.g, "act": wl.act,
-                      "d_norm": wl.D, "step": "seam fwd" if wl.seam else ("fwd" if wl.fwd_only else "fwd+bwd"),
+                      "d_norm": wl.D, "residual": wl.residual,
+                      "step": "seam fwd" if wl.seam else ("fwd" if wl.fwd_only else "fwd+bwd"),
                       "parallelism": "none (1 GPU)"},
            "tflops": tflops,
            "tokens_per_s": wl.T / (ms_step * 1e-3),
            "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wl.dtype],
            "kernel_ms_warmup_step": per_kernel,
+           "checkpoint": None if (wl.seam or wl.fwd_only) else checkpoint_bytes(wl),
            "roofline": roof}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

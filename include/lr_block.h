@@ -131,6 +131,36 @@ lr_status lr_block_bwd_rstd(const lr_dims* dims, const void* x, const void* gamm
                             const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Residual variant.  The block is the body of a pre-norm transformer sublayer
+ * (the low-rank layers the pages train sit in LLaMA-2 models, technical summary
+ * §4), whose output adds the sublayer's input back.  The add is fused into the
+ * up-projection's epilogue, so y never makes a second pass through HBM:
+ *   y[i] = residual[i] + z_i . B[i]
+ *   residual: HOST array of n_up device pointers, residual[i] [T, d] (dtype);
+ *   residual[i] may equal y[i] (in-place accumulation into the residual
+ *   stream), otherwise it must not overlap any output.
+ * rstd_save as lr_block_fwd_rstd (may be NULL).  With a residual the
+ * small-rank shapes do not use the one-kernel forward: they run the
+ * down-projection and the up-projection kernels (same workspace size).
+ * LR_EINVAL when residual is NULL.  Other arguments and errors as lr_block_fwd. */
+lr_status lr_block_fwd_residual(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                                const void* const* B, const void* const* residual, void* const* y,
+                                void* h_save, float* rstd_save, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Backward of the residual variant: the residual path's gradient is added to
+ * the block's dx in the dx epilogue.
+ *   dx = (the block's dx) + dx_residual         dx_residual [T, d] (dtype)
+ * For out = x + block(x) (residual[0] = x, one up-projection) pass
+ * dx_residual = dy[0].  dx_residual may equal dx; it may be NULL only when T == 0
+ * (LR_EINVAL otherwise).  rstd_saved as lr_block_bwd_rstd (may be NULL).  The
+ * weight gradients do not depend on the residual.  Other arguments and errors
+ * as lr_block_bwd. */
+lr_status lr_block_bwd_residual(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                                const void* const* B, const void* h_saved, const float* rstd_saved,
+                                const void* const* dy, const void* dx_residual, void* dx, float* dgamma,
+                                float* dA, float* const* dB, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Shard seam of bottleneck-aware tensor parallelism (§2.1: the d x r factor runs
  * row-parallel over this call's slice of d; §2.2: Online-RMSNorm keeps the local
  * statistic and defers normalisation).  On one GPU the all-reduce of the partial

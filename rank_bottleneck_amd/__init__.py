@@ -42,7 +42,7 @@ class LrError(RuntimeError):
 
 _lib = None
 ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
-                "lr_down_partial", "lr_up_finish", "lr_block_workspace_size", "lr_status_str", "lr_trace_begin",
+                "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_down_partial", "lr_up_finish", "lr_block_workspace_size", "lr_status_str", "lr_trace_begin",
                 "lr_trace_count", "lr_trace_elapsed", "lr_trace_end")
 
 
@@ -63,10 +63,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lr_block_fwd_rstd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_block_bwd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_block_bwd_rstd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_fwd_residual.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_bwd_residual.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_down_partial.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_up_finish.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
-              "lr_down_partial", "lr_up_finish"):
+              "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_down_partial", "lr_up_finish"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lr_block_workspace_size.argtypes = [dims, ctypes.c_int]
     lib.lr_block_workspace_size.restype = sz
@@ -168,6 +170,21 @@ def lr_block_bwd_rstd(dims: LrDims, x, gamma, A, B: Sequence, h_saved, rstd_save
                                                           _stream(stream)))
 
 
+def lr_block_fwd_residual(dims: LrDims, x, gamma, A, B: Sequence, residual: Sequence, y: Sequence, h_save,
+                          rstd_save, ws, stream=None) -> None:
+    _check("lr_block_fwd_residual", load().lr_block_fwd_residual(
+        ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B), _ptr_array(residual), _ptr_array(y),
+        _ptr(h_save), _ptr(rstd_save), _ptr(ws), _ws_nbytes(ws), _stream(stream)))
+
+
+def lr_block_bwd_residual(dims: LrDims, x, gamma, A, B: Sequence, h_saved, rstd_saved, dy: Sequence, dx_residual,
+                          dx, dgamma, dA, dB: Sequence, ws, stream=None) -> None:
+    _check("lr_block_bwd_residual", load().lr_block_bwd_residual(
+        ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B), _ptr(h_saved), _ptr(rstd_saved),
+        _ptr_array(dy), _ptr(dx_residual), _ptr(dx), _ptr(dgamma), _ptr(dA), _ptr_array(dB), _ptr(ws),
+        _ws_nbytes(ws), _stream(stream)))
+
+
 def lr_down_partial(dims: LrDims, x, gamma, A, partial, sumsq, ws, stream=None) -> None:
     _check("lr_down_partial", load().lr_down_partial(ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A),
                                                       _ptr(partial), _ptr(sumsq), _ptr(ws), _ws_nbytes(ws),
@@ -205,23 +222,29 @@ def workspace(dims: LrDims, backward: bool, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def fwd(dims: LrDims, x, gamma, A, B: Sequence, save_h: bool = True, ws=None, stream=None, rstd=None):
+def fwd(dims: LrDims, x, gamma, A, B: Sequence, save_h: bool = True, ws=None, stream=None, rstd=None,
+        residual: Optional[Sequence] = None):
     """Allocating forward: returns (list of y_i, h or None).  rstd: an fp32 [T]
-    tensor that receives the rows' rstd, or None."""
+    tensor that receives the rows' rstd, or None.  residual: n_up [T, d]
+    tensors added to the y_i (lr_block_fwd_residual), or None."""
     dt = TORCH_DTYPE[dims.dtype]
     y = [torch.empty((dims.T, dims.d), dtype=dt, device=x.device) for _ in range(n_up(dims))]
     h = torch.empty((dims.T, dims.g * dims.r), dtype=dt, device=x.device) if save_h else None
     ws = workspace(dims, False, x.device) if ws is None else ws
-    if rstd is None:
+    if residual is not None:
+        lr_block_fwd_residual(dims, x, gamma, A, B, residual, y, h, rstd, ws, stream)
+    elif rstd is None:
         lr_block_fwd(dims, x, gamma, A, B, y, h, ws, stream)
     else:
         lr_block_fwd_rstd(dims, x, gamma, A, B, y, h, rstd, ws, stream)
     return y, h
 
 
-def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream=None, rstd=None):
+def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream=None, rstd=None,
+        dx_residual=None):
     """Allocating backward: returns dict(dx, dgamma, dA, dB).  rstd: the forward's
-    saved rstd, or None to recompute it from x."""
+    saved rstd, or None to recompute it from x.  dx_residual: a [T, d] tensor
+    added to dx (lr_block_bwd_residual), or None."""
     dt = TORCH_DTYPE[dims.dtype]
     dev = x.device
     dx = torch.empty((dims.T, dims.d), dtype=dt, device=dev)
@@ -229,7 +252,9 @@ def bwd(dims: LrDims, x, gamma, A, B: Sequence, h, dy: Sequence, ws=None, stream
     dA = torch.empty((dims.d, dims.g * dims.r), dtype=torch.float32, device=dev)
     dB = [torch.empty((dims.r, dims.d), dtype=torch.float32, device=dev) for _ in range(n_up(dims))]
     ws = workspace(dims, True, dev) if ws is None else ws
-    if rstd is None:
+    if dx_residual is not None:
+        lr_block_bwd_residual(dims, x, gamma, A, B, h, rstd, dy, dx_residual, dx, dgamma, dA, dB, ws, stream)
+    elif rstd is None:
         lr_block_bwd(dims, x, gamma, A, B, h, dy, dx, dgamma, dA, dB, ws, stream)
     else:
         lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, ws, stream)

@@ -121,11 +121,16 @@ struct TraceGuard {
 
 template <typename E>
 lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                   void* const* y, void* h_save, float* rstd_save, void* ws, hipStream_t s) {
+                   const void* const* residual, void* const* y, void* h_save, float* rstd_save, void* ws,
+                   hipStream_t s) {
   const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
   Carve cv{static_cast<char*>(ws)};
   void* Ap = cv.take<void>((size_t)D * gr * sizeof(E));
-  if (fused_fwd(d)) {
+  // With a residual the one-kernel small-rank forward is not used: those shapes
+  // run the down-projection and the up-projection (whose epilogue adds the
+  // residual), which fit in the same workspace.
+  const bool one_kernel = fused_fwd(d) && !residual;
+  if (one_kernel) {
     // small g*r: x . A', deferred rstd, sigma and the up-projections in one
     // kernel; z stays in LDS
     void* Bf = cv.take<void>((size_t)D * gr * sizeof(E));
@@ -138,7 +143,7 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
     return LR_OK;
   }
   void* z = cv.take<void>((size_t)T * gr * sizeof(E));
-  const int ns = small_splits(d);
+  const int ns = fused_fwd(d) ? 0 : small_splits(d);
   if (ns > 0) {
     // small g*r: split-K down-projection into fp32 partials, then the finish
     // kernel (sum, deferred rstd, sigma), then the up-projection
@@ -165,7 +170,11 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   const bool z_is_h = d->act == LR_ACT_IDENTITY && h_save;
   ua.z = z_is_h ? h_save : z;
   ua.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
-  for (int i = 0; i < n_up; ++i) { ua.B[i] = B[i]; ua.y[i] = y[i]; }
+  for (int i = 0; i < n_up; ++i) {
+    ua.B[i] = B[i];
+    ua.y[i] = y[i];
+    ua.res[i] = residual ? residual[i] : nullptr;
+  }
   ua.T = T; ua.d = D; ua.r = r;
   LR_LAUNCH("up", s, lr::launch_up<E>(ua, n_up, s));
   return LR_OK;
@@ -173,8 +182,8 @@ lr_status fwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
 
 template <typename E>
 lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
-                   const void* h, const float* rstd_saved, const void* const* dy, void* dx, float* dgamma, float* dA,
-                   float* const* dB, void* ws, hipStream_t s) {
+                   const void* h, const float* rstd_saved, const void* const* dy, const void* dx_residual, void* dx,
+                   float* dgamma, float* dA, float* const* dB, void* ws, hipStream_t s) {
   const int T = (int)d->T, D = (int)d->d, r = (int)d->r, g = (int)d->g, gr = g * r, n_up = n_up_of(d);
   const int nsp = n_up * lr::dz_nparts<E>(r);
   const int ngp = lr::wgrad_nparts<E>(gr);
@@ -227,7 +236,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
 
   lr::DxArgs xa{};
   xa.dh = dh; xa.A = A; xa.x = x; xa.gamma = gamma; xa.rstd = rstd; xa.spart = spart; xa.nspart = nsp; xa.spstride = sps;
-  xa.dx = dx; xa.T = T; xa.d = D; xa.r = r; xa.g = g; xa.invD = inv_width(d);
+  xa.dx = dx; xa.dres = dx_residual; xa.T = T; xa.d = D; xa.r = r; xa.g = g; xa.invD = inv_width(d);
   LR_LAUNCH("dx", s, lr::launch_dx<E>(xa, s));
   return LR_OK;
 }
@@ -288,6 +297,40 @@ lr_status check_ws(void* ws, size_t have, size_t need) {
   return LR_OK;
 }
 
+lr_status fwd_entry(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                    const void* const* residual, void* const* y, void* h_save, float* rstd_save, void* ws,
+                    size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save) || !opt(rstd_save)) return LR_EINVAL;
+  const int n_up = n_up_of(d);
+  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
+  if ((st = check_rows_ptrs(reinterpret_cast<const void* const*>(y), n_up, d->T)) != LR_OK) return st;
+  if (residual && (st = check_rows_ptrs(residual, n_up, d->T)) != LR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
+  return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, residual, y, h_save, rstd_save, ws, s)
+                             : fwd_impl<float>(d, x, gamma, A, B, residual, y, h_save, rstd_save, ws, s);
+}
+
+lr_status bwd_entry(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
+                    const void* h_saved, const float* rstd_saved, const void* const* dy, const void* dx_residual,
+                    void* dx, float* dgamma, float* dA, float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(h_saved, d->T) || !opt(rstd_saved) ||
+      !req_rows(dx, d->T) || !req(dgamma) || !req(dA) || !opt(dx_residual))
+    return LR_EINVAL;
+  const int n_up = n_up_of(d);
+  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
+  if ((st = check_rows_ptrs(dy, n_up, d->T)) != LR_OK) return st;
+  if ((st = check_ptrs(reinterpret_cast<const void* const*>(dB), n_up)) != LR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, bwd_ws(d))) != LR_OK) return st;
+  return d->dtype == LR_BF16
+             ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx_residual, dx, dgamma, dA, dB, ws, s)
+             : bwd_impl<float>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx_residual, dx, dgamma, dA, dB, ws, s);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -325,48 +368,44 @@ lr_status rmsnorm_online(const lr_dims* d, const void* x, const void* gamma, voi
   return LR_OK;
 }
 
+
 lr_status lr_block_fwd_rstd(const lr_dims* d, const void* x, const void* gamma, const void* A,
                             const void* const* B, void* const* y, void* h_save, float* rstd_save, void* ws,
                             size_t ws_bytes, hipStream_t s) {
-  lr_status st = check_dims(d);
-  if (st != LR_OK) return st;
-  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save) || !opt(rstd_save)) return LR_EINVAL;
-  const int n_up = n_up_of(d);
-  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
-  if ((st = check_rows_ptrs(reinterpret_cast<const void* const*>(y), n_up, d->T)) != LR_OK) return st;
-  if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
-  return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, y, h_save, rstd_save, ws, s)
-                             : fwd_impl<float>(d, x, gamma, A, B, y, h_save, rstd_save, ws, s);
+  return fwd_entry(d, x, gamma, A, B, nullptr, y, h_save, rstd_save, ws, ws_bytes, s);
 }
 
 lr_status lr_block_fwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
                        void* const* y, void* h_save, void* ws, size_t ws_bytes, hipStream_t s) {
-  return lr_block_fwd_rstd(d, x, gamma, A, B, y, h_save, nullptr, ws, ws_bytes, s);
+  return fwd_entry(d, x, gamma, A, B, nullptr, y, h_save, nullptr, ws, ws_bytes, s);
+}
+
+lr_status lr_block_fwd_residual(const lr_dims* d, const void* x, const void* gamma, const void* A,
+                                const void* const* B, const void* const* residual, void* const* y, void* h_save,
+                                float* rstd_save, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!residual) return LR_EINVAL;
+  return fwd_entry(d, x, gamma, A, B, residual, y, h_save, rstd_save, ws, ws_bytes, s);
 }
 
 lr_status lr_block_bwd_rstd(const lr_dims* d, const void* x, const void* gamma, const void* A,
                             const void* const* B, const void* h_saved, const float* rstd_saved,
                             const void* const* dy, void* dx, float* dgamma, float* dA, float* const* dB, void* ws,
                             size_t ws_bytes, hipStream_t s) {
-  lr_status st = check_dims(d);
-  if (st != LR_OK) return st;
-  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !req_rows(h_saved, d->T) || !opt(rstd_saved) ||
-      !req_rows(dx, d->T) || !req(dgamma) || !req(dA))
-    return LR_EINVAL;
-  const int n_up = n_up_of(d);
-  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
-  if ((st = check_rows_ptrs(dy, n_up, d->T)) != LR_OK) return st;
-  if ((st = check_ptrs(reinterpret_cast<const void* const*>(dB), n_up)) != LR_OK) return st;
-  if ((st = check_ws(ws, ws_bytes, bwd_ws(d))) != LR_OK) return st;
-  return d->dtype == LR_BF16 ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx, dgamma, dA, dB, ws, s)
-                             : bwd_impl<float>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx, dgamma, dA, dB, ws,
-                                               s);
+  return bwd_entry(d, x, gamma, A, B, h_saved, rstd_saved, dy, nullptr, dx, dgamma, dA, dB, ws, ws_bytes, s);
 }
 
 lr_status lr_block_bwd(const lr_dims* d, const void* x, const void* gamma, const void* A, const void* const* B,
                        const void* h_saved, const void* const* dy, void* dx, float* dgamma, float* dA,
                        float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
-  return lr_block_bwd_rstd(d, x, gamma, A, B, h_saved, nullptr, dy, dx, dgamma, dA, dB, ws, ws_bytes, s);
+  return bwd_entry(d, x, gamma, A, B, h_saved, nullptr, dy, nullptr, dx, dgamma, dA, dB, ws, ws_bytes, s);
+}
+
+lr_status lr_block_bwd_residual(const lr_dims* d, const void* x, const void* gamma, const void* A,
+                                const void* const* B, const void* h_saved, const float* rstd_saved,
+                                const void* const* dy, const void* dx_residual, void* dx, float* dgamma, float* dA,
+                                float* const* dB, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dx_residual && d && d->T > 0) return LR_EINVAL;
+  return bwd_entry(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx_residual, dx, dgamma, dA, dB, ws, ws_bytes, s);
 }
 
 lr_status lr_down_partial(const lr_dims* d, const void* x, const void* gamma, const void* A, float* partial,

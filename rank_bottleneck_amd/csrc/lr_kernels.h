@@ -53,6 +53,7 @@ struct UpArgs {
   int64_t ldz;
   const void* B[MAX_G];
   void* y[MAX_G];
+  const void* res[MAX_G];  // residual_i [T, d] added to y_i (all null: none); may equal y[i]
   int T, d, r;
 };
 
@@ -112,6 +113,7 @@ struct DxArgs {
   const float* spart;  // [T, spstride], the first nspart columns of each row used
   int nspart, spstride;
   void* dx;
+  const void* dres;    // [T, d] added to dx (the residual path's gradient), or null; may equal dx
   int T, d, r, g;
   float invD;
 };

@@ -358,8 +358,8 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
 }
 
 // ------------------------------------------------------------------ up projection
-// y_i = z_i . B_i ; one launch over (branch, tile)
-template <class C>
+// y_i = z_i . B_i (+ residual_i with RES); one launch over (branch, tile)
+template <class C, bool RES>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_up(UpArgs a) {
   using E = typename C::E;
   __shared__ uint4 lds[KernLds<C>::TOTAL];
@@ -375,18 +375,35 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   f32x16 acc[C::MB][C::NB];
   mainloop<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.r, lds, nullptr, acc);
   E* y = static_cast<E*>(a.y[br]);
+  const E* res = static_cast<const E*>(a.res[br]);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   char LR_LDS* reg = stage_region<C>(lds);
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
     stage_block<C>(acc, mb, reg);
     const int rbase = m0 + wm * C::WTM + mb * 32;
-    sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
-      const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
-      if (row >= a.T || col >= a.d) return;
-      const float4 v = lds_f4(rp + cl * 4);
-      store4(y + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
-    });
+    if constexpr (RES) {
+      // the block's residual rows are loaded first, all in flight together
+      sweep_block_pre<C, C::WTN, 1>(
+          reg,
+          [&](int rl, int cl, float4* in) {
+            const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+            in[0] = row < a.T && col < a.d ? load4(res + (int64_t)row * a.d + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+          },
+          [&](int rl, int cl, const char LR_LDS* rp, const float4* in) {
+            const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+            if (row >= a.T || col >= a.d) return;
+            const float4 v = lds_f4(rp + cl * 4);
+            store4(y + (int64_t)row * a.d + col, v.x + in[0].x, v.y + in[0].y, v.z + in[0].z, v.w + in[0].w);
+          });
+    } else {
+      sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+        const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+        if (row >= a.T || col >= a.d) return;
+        const float4 v = lds_f4(rp + cl * 4);
+        store4(y + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
+      });
+    }
   }
 }
 
@@ -906,10 +923,11 @@ struct SprimeRows {
 };
 
 // ------------------------------------------------------------------ backward: dx
-// acc = dh' . A^T over K = g*r.  Row-sweep epilogue: dx = gamma*acc - x*rstd*S'/D,
-// with S' summed from the dz partials.  x rows of block mb+1 are loaded while
-// block mb is computed; block 0, gamma and the row statistic at the last k step.
-template <class C>
+// acc = dh' . A^T over K = g*r.  Row-sweep epilogue: dx = gamma*acc - x*rstd*S'/D
+// (+ dres with RES), with S' summed from the dz partials.  x (and dres) rows of
+// block mb+1 are loaded while block mb is computed; block 0, gamma and the row
+// statistic at the last k step.
+template <class C, bool RES>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dx(DxArgs a) {
   using E = typename C::E;
   using R = Raw4<E>;
@@ -928,15 +946,19 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   const int col = n0 + wn * C::WTN + sw.cl;
   const bool cok = col < a.d;
   const E* __restrict__ x = static_cast<const E*>(a.x);
-  E* __restrict__ dx = static_cast<E*>(a.dx);
+  const E* dres = static_cast<const E*>(a.dres);
+  E* dx = static_cast<E*>(a.dx);
 
-  typename R::T xin0[SW::IT], xin1[SW::IT];
-  auto load_block = [&](int mb, typename R::T (&buf)[SW::IT]) {
+  // x rows, then (RES) the dres rows: buf[it] and buf[SW::IT + it]
+  constexpr int NBUF = RES ? 2 * SW::IT : SW::IT;
+  typename R::T xin0[NBUF], xin1[NBUF];
+  auto load_block = [&](int mb, typename R::T (&buf)[NBUF]) {
     const int rb = m0 + wm * C::WTM + mb * 32;
 #pragma unroll
     for (int it = 0; it < SW::IT; ++it) {
       const int row = rb + sw.rl(it);
       buf[it] = row < a.T && cok ? R::load(x + (int64_t)row * a.d + col) : R::zero();
+      if constexpr (RES) buf[SW::IT + it] = row < a.T && cok ? R::load(dres + (int64_t)row * a.d + col) : R::zero();
     }
   };
   typename R::T graw = R::zero();
@@ -962,7 +984,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   const float4 g4 = R::f4(graw);
   char LR_LDS* reg = stage_region<C>(lds);
   // block mb computes from `cur` while block mb+1 loads into `nxt`
-  auto block = [&](int mb, const typename R::T (&cur)[SW::IT], typename R::T (&nxt)[SW::IT]) {
+  auto block = [&](int mb, const typename R::T (&cur)[NBUF], typename R::T (&nxt)[NBUF]) {
     if (PF && mb + 1 < C::MB) load_block(mb + 1, nxt);
     stage_block<C>(acc, mb, reg);
     const int rb = m0 + wm * C::WTM + mb * 32;
@@ -973,8 +995,13 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
       const float4 v = lds_f4(reg + rl * RowStage<C>::PITCH + sw.cl * 4);
       const float4 x4 = R::f4(cur[it]);
       const float sr = srow[row - m0];
-      store4(dx + (int64_t)row * a.d + col, g4.x * v.x - x4.x * sr, g4.y * v.y - x4.y * sr,
-             g4.z * v.z - x4.z * sr, g4.w * v.w - x4.w * sr);
+      float4 o = make_float4(g4.x * v.x - x4.x * sr, g4.y * v.y - x4.y * sr, g4.z * v.z - x4.z * sr,
+                             g4.w * v.w - x4.w * sr);
+      if constexpr (RES) {
+        const float4 r4 = R::f4(cur[SW::IT + it]);
+        o.x += r4.x; o.y += r4.y; o.z += r4.z; o.w += r4.w;
+      }
+      store4(dx + (int64_t)row * a.d + col, o.x, o.y, o.z, o.w);
     }
   };
   if constexpr (PF) {
@@ -1144,7 +1171,10 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
 template <class C>
 hipError_t launch_up_cfg(const UpArgs& a, int n_up, hipStream_t s) {
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
-  hipLaunchKernelGGL((k_up<C>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  if (a.res[0])
+    hipLaunchKernelGGL((k_up<C, true>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_up<C, false>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1345,7 +1375,10 @@ hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
   using C = typename Cfgs<E>::Dx;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
-  hipLaunchKernelGGL((k_dx<C>), dim3(tiles), dim3(C::THREADS), 0, s, a);
+  if (a.dres)
+    hipLaunchKernelGGL((k_dx<C, true>), dim3(tiles), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_dx<C, false>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

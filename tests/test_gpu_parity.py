@@ -242,16 +242,28 @@ def test_shard_seam_small(act, g, dtype):
         sss.append(ss)
     P = torch.stack(parts).sum(0).contiguous()   # stands in for the all-reduce
     SS = torch.stack(sss).sum(0).contiguous()
+    # the finish step on its own: both sides take the oracle's summed partials
+    # (rounded once to the fp32 the entry point takes)
+    rps = [oracle.down_partial(inp.x.v[:, slice(s * dl, (s + 1) * dl)], inp.gamma.v[s * dl:(s + 1) * dl],
+                               inp.A.v[s * dl:(s + 1) * dl, :]) for s in range(tp)]
+    P_or = np.float32(sum(p for p, _ in rps))
+    SS_or = np.float32(sum(q for _, q in rps))
     for s in range(tp):
         c = slice(s * dl, (s + 1) * dl)
         dims = rb.make_dims(T, dl, r, g, act, dtype, wl.eps, d_norm=dl * tp)
         Bs = [dev(b.store[:, c].copy()) for b in inp.B]
-        y, h = rb.up_finish(dims, P, SS, Bs)
+        y, h = rb.up_finish(dims, dev(P_or), dev(SS_or), Bs)
         torch.cuda.synchronize()
-        ref = oracle.up_finish(host(P), host(SS), [b.v[:, c] for b in inp.B], r, g, act, wl.eps, dl * tp)
+        ref = oracle.up_finish(P_or.astype(np.float64), SS_or.astype(np.float64), [b.v[:, c] for b in inp.B], r, g,
+                               act, wl.eps, dl * tp)
         assert_close(host(h), ref["h"], dtype, "h")
         for i, yi in enumerate(y):
             assert_close(host(yi), ref["y"][i], dtype, "y (seam)")
+        # the whole seam on the GPU (its partials summed in place of the
+        # all-reduce) against the unsharded block
+        y2, _ = rb.up_finish(dims, P, SS, Bs)
+        torch.cuda.synchronize()
+        for i, yi in enumerate(y2):
             assert_close(host(yi), full["y"][i][:, c], dtype, "y (vs unsharded)")
 
 
@@ -333,7 +345,7 @@ FULL_FWD = ["qkv_identity", "swiglu_mlp", "qkv_silu_ckpt", "small_r64", "small_r
             "small_swiglu_r64", "small_swiglu_r128", "vanilla_tp_shard"]
 
 
-def _sample_rows(T, n=192, seed=0):
+def _sample_rows(T, n=1024, seed=0):
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([rng.choice(T, n - 8, replace=False), np.arange(T - 8, T)]))
     return rows
@@ -401,3 +413,140 @@ def test_full_size_backward(name):
     assert_close(host(g["dA"]), ref["dA"], wl.dtype, "dA")
     for i in range(len(B)):
         assert_close(host(g["dB"][i]), ref["dB"][i], wl.dtype, f"dB{i}")
+
+
+# ------------------------------------------------------------------ grouped branches up to MAX_G
+@pytest.mark.parametrize("wl", [
+    # g = 8 at r = 64: eight concatenated down-projections and eight batched up-projections
+    Workload("bf16_g8_r64", 700, 512, 64, 8, "silu", "bf16"),
+    # g = 5 at r = 1024: 5 x 8 = 40 S' row partials, more than the 32 the dx
+    # kernel loads ahead of its epilogue, so its tail loop runs
+    Workload("bf16_g5_r1024", 600, 256, 1024, 5, "silu", "bf16"),
+    Workload("f32_g8_r64", 130, 256, 64, 8, "identity", "f32"),
+], ids=lambda w: w.name)
+def test_many_branches_whole_gradients(wl):
+    _say("many branches", wl)
+    inp = make_inputs(wl, seed=9)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    for keep_rstd in (False, True):
+        rstd = torch.full((wl.T,), float("nan"), dtype=torch.float32, device="cuda") if keep_rstd else None
+        y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd)
+        g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy], rstd=rstd)
+        torch.cuda.synchronize()
+        ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps)
+        assert_close(host(h), ref["h"], wl.dtype, "h")
+        for i, yi in enumerate(y):
+            assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+        rb_ = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                               wl.r, wl.g, wl.act, wl.eps)
+        for k in ("dx", "dgamma", "dA"):
+            assert_close(host(g[k]), rb_[k], wl.dtype, k)
+        for i in range(len(B)):
+            assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
+
+
+# ------------------------------------------------------------------ residual variant
+RESIDUAL = [
+    # the GEMM path: SwiGLU sublayer out = x + block(x), r = 1024
+    Workload("res_swiglu_r1024", 700, 1024, 1024, 2, "swiglu", "bf16"),
+    # per-branch residuals with three up-projections
+    Workload("res_identity_g3", 555, 512, 320, 3, "identity", "bf16"),
+    # small rank: shapes the one-kernel forward takes without a residual
+    Workload("res_swiglu_r64", 1000, 512, 64, 2, "swiglu", "bf16"),
+    Workload("res_silu_r256", 333, 448, 256, 1, "silu", "bf16"),
+    Workload("res_f32", 300, 320, 128, 1, "silu", "f32"),
+]
+
+
+@pytest.mark.parametrize("wl", RESIDUAL, ids=lambda w: w.name)
+def test_residual_forward_backward(wl):
+    """lr_block_fwd_residual / lr_block_bwd_residual against the oracle's
+    residual variant: the first branch's residual is x (the sublayer
+    out = x + block(x), whose dx gains dy_0), the others seeded draws."""
+    _say("residual", wl)
+    inp = make_inputs(wl, seed=12)
+    rng = np.random.default_rng(13)
+    extra = [workloads_tensor(rng.standard_normal((wl.T, wl.d)), wl.dtype) for _ in range(wl.n_up - 1)]
+    res_h = [inp.x] + extra
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    res = [x] + [dev(t) for t in extra]
+    rstd = torch.empty(wl.T, dtype=torch.float32, device="cuda")
+    y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd, residual=res)
+    dy = [dev(t) for t in inp.dy]
+    g = rb.bwd(dims, x, gamma, A, B, h, dy, rstd=rstd, dx_residual=dy[0])
+    torch.cuda.synchronize()
+    Bv = [b.v for b in inp.B]
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, Bv, wl.r, wl.g, wl.act, wl.eps, wl.D,
+                           residual=[t.v for t in res_h])
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    for i, yi in enumerate(y):
+        assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+    rbw = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, Bv, [t.v for t in inp.dy], wl.r, wl.g, wl.act, wl.eps,
+                           wl.D, dx_residual=inp.dy[0].v)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), rbw[k], wl.dtype, k)
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), rbw["dB"][i], wl.dtype, f"dB{i}")
+
+
+@pytest.mark.parametrize("wl", [RESIDUAL[0], RESIDUAL[2]], ids=lambda w: w.name)
+def test_residual_in_place(wl):
+    """The residual accumulated in place (y_i is the residual buffer) and the
+    residual gradient accumulated into dx in place: equal to the out-of-place
+    calls, bitwise."""
+    _say("residual in place", wl)
+    inp = make_inputs(wl, seed=14)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    res = [x.clone() for _ in range(wl.n_up)]
+    y_ref, h = rb.fwd(dims, x, gamma, A, B, residual=res)
+    ws = rb.workspace(dims, False)
+    rb.lr_block_fwd_residual(dims, x, gamma, A, B, res, res, None, None, ws)   # y_i written over residual_i
+    dy = [dev(t) for t in inp.dy]
+    g_ref = rb.bwd(dims, x, gamma, A, B, h, dy, dx_residual=dy[0])
+    dx = dy[0].clone()
+    dgamma = torch.empty(wl.d, dtype=torch.float32, device="cuda")
+    dA = torch.empty((wl.d, wl.g * wl.r), dtype=torch.float32, device="cuda")
+    dB = [torch.empty((wl.r, wl.d), dtype=torch.float32, device="cuda") for _ in range(wl.n_up)]
+    rb.lr_block_bwd_residual(dims, x, gamma, A, B, h, None, dy, dx, dx, dgamma, dA, dB, rb.workspace(dims, True))
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(res, y_ref))
+    assert torch.equal(dx, g_ref["dx"]) and torch.equal(dA, g_ref["dA"]) and torch.equal(dgamma, g_ref["dgamma"])
+
+
+def workloads_tensor(values64, dtype):
+    from workloads import Tensor
+    return Tensor(values64, dtype)
+
+
+def test_full_size_residual_sublayer():
+    """The SwiGLU sublayer out = x + block(x) at its full shape: sampled forward
+    rows, every gradient whole (dx including dy through the residual)."""
+    wl = WORKLOADS["swiglu_mlp_res"]
+    _say("full residual", wl)
+    inp = make_inputs(wl, seed=0)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    rstd = torch.empty(wl.T, dtype=torch.float32, device="cuda")
+    y, h = rb.fwd(dims, x, gamma, A, B, rstd=rstd, residual=[x])
+    dy = [dev(t) for t in inp.dy]
+    g = rb.bwd(dims, x, gamma, A, B, h, dy, rstd=rstd, dx_residual=dy[0])
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl.T)
+    ri = torch.as_tensor(rows, device="cuda")
+    Bv = [b.v for b in inp.B]
+    ref = oracle.block_fwd(inp.x.v[rows], inp.gamma.v, inp.A.v, Bv, wl.r, wl.g, wl.act, wl.eps, wl.D,
+                           residual=[inp.x.v[rows]])
+    assert_close(host(y[0][ri]), ref["y"][0], wl.dtype, "y0 rows")
+    del y
+    rbw = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, Bv, [t.v for t in inp.dy], wl.r, wl.g, wl.act, wl.eps,
+                           wl.D, dx_residual=inp.dy[0].v)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), rbw[k], wl.dtype, k)
+    assert_close(host(g["dB"][0]), rbw["dB"][0], wl.dtype, "dB0")

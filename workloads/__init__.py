@@ -45,6 +45,7 @@ class Workload:
     seam: bool = False    # run through the shard seam (partial + finish) instead of the fused block
     fwd_only: bool = False  # benchmarked as a forward pass
     hbm_metric: bool = False  # reported as forward HBM GB/s (memory-bound sweep) instead of TFLOP/s
+    residual: bool = False  # the sublayer out = x + block(x): residual_0 = x, and dx gains dy_0
     note: str = ""
 
     @property
@@ -88,6 +89,11 @@ WORKLOADS: Dict[str, Workload] = {
     "qkv_silu_ckpt": Workload("qkv_silu_ckpt", T=16384, d=4096, r=1024, g=3, act="silu", dtype="bf16",
                               note="backward from the saved [T, 3r] pre-activation"),
 }
+# the SwiGLU bottleneck as a pre-norm sublayer: out = x + block(x), the residual
+# add fused into the up-projection's epilogue and dy added into dx
+WORKLOADS["swiglu_mlp_res"] = Workload("swiglu_mlp_res", T=16384, d=4096, r=1024, g=2, act="swiglu", dtype="bf16",
+                                       residual=True,
+                                       note="swiglu_mlp as the sublayer out = x + block(x) (residual fused)")
 # memory-bound small-rank sweep (forward)
 for _r in (64, 128, 256):
     WORKLOADS[f"small_r{_r}"] = Workload(f"small_r{_r}", T=16384, d=4096, r=_r, g=1, act="silu",
