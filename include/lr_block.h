@@ -28,9 +28,10 @@
  *     (LR_BF16: bfloat16 storage, fp32 accumulation; LR_F32: fp32).  sumsq,
  *     rstd, the shard partial and all weight gradients are fp32.
  *   - The caller owns every buffer.  The library allocates no device memory,
- *     keeps no pointer after a call returns and holds no mutable global state.
- *     Scratch space is the caller's workspace `ws` of at least
- *     lr_block_workspace_size() bytes (256-byte aligned).
+ *     keeps no pointer after a call returns and holds no mutable global state,
+ *     except lr_block_fwd_noalloc's per-GPU device scratch (below).  Scratch
+ *     space is the caller's workspace `ws` of at least lr_block_workspace_size()
+ *     bytes (256-byte aligned).
  *   - All work is enqueued on `stream`; nothing synchronises.  Buffers must stay
  *     alive until the stream has passed the call.
  *   - Outputs must not alias inputs.  Gradients are overwritten, not accumulated.
@@ -160,6 +161,30 @@ lr_status lr_block_bwd_residual(const lr_dims* dims, const void* x, const void* 
                                 const void* const* B, const void* h_saved, const float* rstd_saved,
                                 const void* const* dy, const void* dx_residual, void* dx, float* dgamma,
                                 float* dA, float* const* dB, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Device scratch of lr_block_fwd_noalloc, per GPU: 128 MiB. */
+#define LR_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* lr_block_fwd_rstd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a file-scope device
+ * array of LR_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds
+ * until the process ends; the call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *   - Arguments, outputs and errors as lr_block_fwd_rstd (rstd_save may be NULL).
+ *   - LR_EWORKSPACE when these dims need more than LR_NOALLOC_SCRATCH_BYTES
+ *     (lr_block_workspace_size(dims, 0) > LR_NOALLOC_SCRATCH_BYTES); checked on
+ *     the host, nothing launched.
+ *   - `stream` must belong to the current device (LR_EINVAL otherwise).  The
+ *     first call on a device looks the array's address up once (LR_EHIP if that
+ *     fails).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     contents (the forward writes every scratch byte it reads, so nothing needs
+ *     clearing): calls that overlap on one GPU (two streams, or two host
+ *     threads) race and must be serialised by the caller. */
+lr_status lr_block_fwd_noalloc(const lr_dims* dims, const void* x, const void* gamma, const void* A,
+                               const void* const* B, void* const* y, void* h_save, float* rstd_save,
+                               hipStream_t stream);
 
 /* Shard seam of bottleneck-aware tensor parallelism (§2.1: the d x r factor runs
  * row-parallel over this call's slice of d; §2.2: Online-RMSNorm keeps the local

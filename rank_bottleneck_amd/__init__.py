@@ -42,7 +42,7 @@ class LrError(RuntimeError):
 
 _lib = None
 ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
-                "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_down_partial", "lr_up_finish", "lr_block_workspace_size", "lr_status_str", "lr_trace_begin",
+                "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_block_fwd_noalloc", "lr_down_partial", "lr_up_finish", "lr_block_workspace_size", "lr_status_str", "lr_trace_begin",
                 "lr_trace_count", "lr_trace_elapsed", "lr_trace_end")
 
 
@@ -65,10 +65,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lr_block_bwd_rstd.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_block_fwd_residual.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_block_bwd_residual.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lr_block_fwd_noalloc.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lr_down_partial.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_up_finish.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
-              "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_down_partial", "lr_up_finish"):
+              "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_block_fwd_noalloc", "lr_down_partial",
+              "lr_up_finish"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lr_block_workspace_size.argtypes = [dims, ctypes.c_int]
     lib.lr_block_workspace_size.restype = sz
@@ -183,6 +185,18 @@ def lr_block_bwd_residual(dims: LrDims, x, gamma, A, B: Sequence, h_saved, rstd_
         ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B), _ptr(h_saved), _ptr(rstd_saved),
         _ptr_array(dy), _ptr(dx_residual), _ptr(dx), _ptr(dgamma), _ptr(dA), _ptr_array(dB), _ptr(ws),
         _ws_nbytes(ws), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # LR_NOALLOC_SCRATCH_BYTES
+
+
+def lr_block_fwd_noalloc(dims: LrDims, x, gamma, A, B: Sequence, y: Sequence, h_save, rstd_save,
+                         stream=None) -> None:
+    """The forward with the library's per-GPU device scratch as its workspace
+    (no allocation by the library; the outputs are the caller's)."""
+    _check("lr_block_fwd_noalloc", load().lr_block_fwd_noalloc(
+        ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A), _ptr_array(B), _ptr_array(y), _ptr(h_save),
+        _ptr(rstd_save), _stream(stream)))
 
 
 def lr_down_partial(dims: LrDims, x, gamma, A, partial, sumsq, ws, stream=None) -> None:

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "lr_block.h"
@@ -331,6 +333,36 @@ lr_status bwd_entry(const lr_dims* d, const void* x, const void* gamma, const vo
 }
 
 
+
+// Scratch of the allocation-free forward (lr_block_fwd_noalloc): a file-scope
+// device array, one copy per GPU, held until the process ends.  Host code uses
+// only the device address hipGetSymbolAddress returns for the current device,
+// never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = (size_t)LR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the scratch array's address on device `dev` (which is current), looked up once
+lr_status scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return LR_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return LR_EHIP;
+      g_scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return LR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -385,6 +417,29 @@ lr_status lr_block_fwd_residual(const lr_dims* d, const void* x, const void* gam
                                 float* rstd_save, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!residual) return LR_EINVAL;
   return fwd_entry(d, x, gamma, A, B, residual, y, h_save, rstd_save, ws, ws_bytes, s);
+}
+
+lr_status lr_block_fwd_noalloc(const lr_dims* d, const void* x, const void* gamma, const void* A,
+                               const void* const* B, void* const* y, void* h_save, float* rstd_save,
+                               hipStream_t s) {
+  lr_status st = check_dims(d);
+  if (st != LR_OK) return st;
+  if (!req_rows(x, d->T) || !req(gamma) || !req(A) || !opt(h_save) || !opt(rstd_save)) return LR_EINVAL;
+  const int n_up = n_up_of(d);
+  if ((st = check_ptrs(B, n_up)) != LR_OK) return st;
+  if ((st = check_rows_ptrs(reinterpret_cast<const void* const*>(y), n_up, d->T)) != LR_OK) return st;
+  const size_t need = fwd_ws(d);
+  if (need > kScratchBytes) return LR_EWORKSPACE;
+  // the stream must belong to the current device, whose copy of the array the
+  // kernels get
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LR_EHIP;
+  if (hipStreamGetDevice(s, &sdev) != hipSuccess) return LR_EHIP;
+  if (sdev != dev) return LR_EINVAL;
+  void* ws = nullptr;
+  if ((st = scratch_on(dev, &ws)) != LR_OK) return st;
+  return d->dtype == LR_BF16 ? fwd_impl<bf16>(d, x, gamma, A, B, nullptr, y, h_save, rstd_save, ws, s)
+                             : fwd_impl<float>(d, x, gamma, A, B, nullptr, y, h_save, rstd_save, ws, s);
 }
 
 lr_status lr_block_bwd_rstd(const lr_dims* d, const void* x, const void* gamma, const void* A,

@@ -142,3 +142,23 @@ def test_rmsnorm_arguments():
     dims = rb.make_dims(8, 16, 64, 1)
     assert lib.rmsnorm_online(ctypes.byref(dims), None, FAKE, None, None, None, None) == rb.LR_EINVAL
     assert lib.rmsnorm_online(ctypes.byref(dims), FAKE, None, FAKE, None, None, None) == rb.LR_EINVAL
+
+
+def test_noalloc_rejects_on_the_host():
+    """lr_block_fwd_noalloc's checks that run before any HIP call: bad dims and
+    pointers, and dims whose workspace exceeds the static scratch."""
+    lib = rb.load()
+    arr = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    big = rb.make_dims(65536, 4096, 1024, 3, "silu", "bf16")          # 25 MiB + 384 MiB
+    assert rb.lr_block_workspace_size(big, False) > rb.NOALLOC_SCRATCH_BYTES
+    assert lib.lr_block_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, arr, arr, None, None, None) \
+        == rb.LR_EWORKSPACE
+    c4 = rb.make_dims(16384, 4096, 1024, 3, "silu", "bf16")           # the largest forward here fits
+    assert rb.lr_block_workspace_size(c4, False) <= rb.NOALLOC_SCRATCH_BYTES
+    bad = rb.make_dims(64, 100, 64, 1)
+    assert lib.lr_block_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, arr, arr, None, None, None) \
+        == rb.LR_EUNSUPPORTED
+    ok = rb.make_dims(64, 128, 64, 1)
+    assert lib.lr_block_fwd_noalloc(ctypes.byref(ok), None, FAKE, FAKE, arr, arr, None, None, None) == rb.LR_EINVAL
+    assert lib.lr_block_fwd_noalloc(ctypes.byref(ok), FAKE, FAKE, FAKE, arr, arr, None, FAKE + 4, None) \
+        == rb.LR_EINVAL
