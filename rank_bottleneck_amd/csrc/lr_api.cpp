@@ -198,7 +198,10 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   float* gpart = cv.take<float>((size_t)D * ngp * 4);
   const lr::WgradPlan wp = lr::wgrad_plan<E>(T, D, r, g, n_up);
   const int ns = wp.nsplit;
+  // the split-tile plan reduces only dB tiles; dA's tiles run whole and leave
+  // dgamma partials, as an unsplit pass does
   const bool reduced = wp.streamk || ns > 1;
+  const bool gamma_parts = !reduced || wp.split_tiles > 0;
   const int64_t pstride = (int64_t)n_up * r * D + (int64_t)D * gr;
   float* wpart = cv.take<float>((size_t)wp.part_floats * 4);
 
@@ -224,16 +227,16 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
   wa.nsplit = ns; wa.wpart = wpart; wa.part_stride = pstride; wa.part_offA = (int64_t)n_up * r * D;
   wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
-  wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles;
+  wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles; wa.split_tiles = wp.split_tiles;
   {
     const int BK = lr::gemm_bk<E>();   // split lengths are whole k steps
     const int ksteps = (T + BK - 1) / BK;
     wa.ksplit = ((ksteps + ns - 1) / ns) * BK;
   }
   LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
-  if (reduced)  // the reduction also forms dgamma
+  if (reduced)  // the reduction (all splits and stream-K: it also forms dgamma)
     LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
-  else          // one pass: the kernel left per-tile dgamma partials
+  if (gamma_parts)  // dA's tiles ran whole: they left per-tile dgamma partials
     LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, false), ngp, s));
 
   lr::DxArgs xa{};

@@ -93,12 +93,19 @@ struct WgradArgs {
   // BM x BN fp32 slot at wpart[(position*maxseg + ordinal) * BM*BN].  Position p
   // holds tile (p % S) * (tiles / S) + p / S (S = 1: tile p).
   int streamk, sk_G, sk_Q, sk_R, sk_KS, sk_maxseg, sk_S, sk_tiles;
+  // split_tiles S > 0 (nsplit == 2): only the first S tiles (all dB tiles) run
+  // as two token halves, writing BM x BN fp32 slots wpart[(half * S + tile) *
+  // BM*BN] that k_wgrad_reduce_tiles adds; the other tiles run whole and write
+  // dB / dA directly.  Work-group ids: per XCD, its share of the whole tiles
+  // first, then its share of the halves.
+  int split_tiles;
 };
 
 // How the token-reduced weight gradients are split.
 struct WgradPlan {
   int streamk;        // 1: stream-K over (tile, k step); 0: nsplit equal token splits
   int nsplit;         // token splits when !streamk (1 = one pass, no reduction)
+  int split_tiles;    // > 0: only this many (dB) tiles split in two (see WgradArgs)
   int G, Q, R, KS, maxseg, tiles;
   int S;              // stream-K tile interleave (see WgradArgs)
   int64_t part_floats;  // fp32 partial floats the plan needs in the workspace

@@ -606,8 +606,27 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   const int tmA = (a.d + C::BM - 1) / C::BM, tnA = (gr + C::BN - 1) / C::BN;
   const int per_split = a.n_up * tmB * tnB + tmA * tnA;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = logical / per_split;
-  int w = logical % per_split;
+  int split, w;
+  bool slot_out = false;   // a split tile's half: writes its fp32 slot
+  if (a.split_tiles > 0) {
+    // per XCD (logical ranges of P ids): the first U/8 ids take whole tiles
+    // S, S+1, ..., the rest the halves of tiles 0..S-1 (the long work first)
+    const int S = a.split_tiles, U = per_split - S, P = (U + 2 * S) / kNumXcd;
+    const int x = logical / P, i = logical % P, uw = U / kNumXcd;
+    if (i < uw) {
+      split = 0;
+      w = S + x * uw + i;
+    } else {
+      const int item = x * (P - uw) + (i - uw);   // 0 .. 2S-1
+      split = item / S;
+      w = item % S;
+      slot_out = true;
+    }
+  } else {
+    split = logical / per_split;
+    w = logical % per_split;
+  }
+  const int tile = w;
   const int job = w < a.n_up * tmB * tnB ? w / (tmB * tnB) : a.n_up;
   w = job < a.n_up ? w % (tmB * tnB) : w - a.n_up * tmB * tnB;
   const bool isA = job == a.n_up;
@@ -616,8 +635,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   int tm, tn;
   grouped_tile<kGroupM>(w, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int kbeg = split * a.ksplit;
-  const int klen = min(a.ksplit, a.T - kbeg);
+  const bool whole = a.split_tiles > 0 && !slot_out;
+  const int kbeg = whole ? 0 : split * a.ksplit;
+  const int klen = whole ? a.T : min(a.ksplit, a.T - kbeg);
   Opnd oa, ob;
   if (isA) {
     oa = Opnd{a.x, a.d, a.d, a.T};   // x^T: (m = j, k = t) at x[t*d + j]
@@ -629,13 +649,19 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   f32x16 acc[C::MB][C::NB];
   mainloop<C, true, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, kbeg, klen > 0 ? klen : 0, lds, nullptr, acc);
 
+  // element (row, col) of the output goes to out[(row - r0) * ldo + col - c0]
   float* out;
-  if (a.nsplit > 1) {
+  int64_t ldo = N;
+  int r0 = 0, c0 = 0;
+  if (slot_out) {
+    out = a.wpart + ((int64_t)split * a.split_tiles + tile) * (C::BM * C::BN);
+    ldo = C::BN; r0 = m0; c0 = n0;
+  } else if (a.nsplit > 1 && a.split_tiles == 0) {
     out = a.wpart + (int64_t)split * a.part_stride + (isA ? a.part_offA : (int64_t)job * a.r * a.d);
   } else {
     out = isA ? a.dA : a.dB[job];
   }
-  const bool finalA = isA && a.nsplit == 1;
+  const bool finalA = isA && (a.nsplit == 1 || a.split_tiles > 0);
   const E* Aw = static_cast<const E*>(a.A);
   const E* gamma = static_cast<const E*>(a.gamma);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
@@ -663,7 +689,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
             const float4 v = lds_f4(rp + cl * 4);
             const float gj = finalA ? in[1].x : 1.0f;
             if (finalA) s = in[0].x * v.x + in[0].y * v.y + in[0].z * v.z + in[0].w * v.w;
-            store4(out + (int64_t)row * N + col, gj * v.x, gj * v.y, gj * v.z, gj * v.w);
+            store4(out + (int64_t)(row - r0) * ldo + (col - c0), gj * v.x, gj * v.y, gj * v.z, gj * v.w);
           }
           if (finalA) {
             s = row_sum<LPR>(s);
@@ -744,6 +770,27 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
   }
   const int row = (int)((int64_t)blockIdx.x - nbb);
   wred_row_a<E>(a, row, [&](int c) { return sum4(nB + (int64_t)row * gr + c); });
+}
+
+// Sum of the two halves of each split tile (k_wgrad with split_tiles > 0): one
+// thread per 4 consecutive slot values, the halves added in order, written to
+// the tile's place in dB (split tiles are dB tiles).
+template <class C>
+__global__ __launch_bounds__(256) void k_wgrad_reduce_tiles(WgradArgs a) {
+  constexpr int TS = C::BM * C::BN;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)a.split_tiles * TS) return;
+  const int tile = (int)(i / TS), loc = (int)(i % TS);
+  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+  const int job = tile / (tmB * tnB);
+  int tm, tn;
+  grouped_tile<kGroupM>(tile % (tmB * tnB), tmB, tnB, tm, tn);
+  const int row = tm * C::BM + loc / C::BN, col = tn * C::BN + loc % C::BN;
+  if (row >= a.r || col >= a.d) return;
+  const float4 p0 = *reinterpret_cast<const float4*>(a.wpart + i);
+  const float4 p1 = *reinterpret_cast<const float4*>(a.wpart + (int64_t)a.split_tiles * TS + i);
+  *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.d + col) =
+      make_float4(p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w);
 }
 
 // Stream-K weight gradients.  Tiles are numbered job-major (dB_0 .. dB_{n_up-1},
@@ -1329,6 +1376,21 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
     p.part_floats = (int64_t)p.tiles * p.maxseg * C::BM * C::BN;
     return p;
   }
+  // Between one and two rounds of whole tiles: split just enough (dB) tiles in
+  // two that the work-groups fill exactly two rounds, the whole tiles first
+  // (one tile-time) and then the halves (half a tile-time), instead of
+  // splitting every tile and reducing all of dA and dB.
+  {
+    const int S = 2 * kNumCu - p.tiles, U = p.tiles - S;
+    const int tilesB = n_up * cdiv(r, C::BM) * cdiv(d, C::BN);
+    if (Cfgs<E>::HAS_SKINNY && p.tiles > kNumCu && S > 0 && S <= tilesB && U % kNumXcd == 0 &&
+        (2 * S) % kNumXcd == 0 && p.KS >= 32) {
+      p.nsplit = 2;
+      p.split_tiles = S;
+      p.part_floats = (int64_t)2 * S * C::BM * C::BN;
+      return p;
+    }
+  }
   // token splits: aim for at least two waves of work-groups on 256 CUs, with
   // >= 16 k steps per split
   int sp = 1;
@@ -1344,7 +1406,8 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   const int gr = a.g * a.r;
   const int tilesB = cdiv(a.r, C::BM) * cdiv(a.d, C::BN);
   const int tilesA = cdiv(a.d, C::BM) * cdiv(gr, C::BN);
-  const int total = (a.n_up * tilesB + tilesA) * a.nsplit;
+  const int total = a.split_tiles > 0 ? a.n_up * tilesB + tilesA + a.split_tiles
+                                     : (a.n_up * tilesB + tilesA) * a.nsplit;
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (a.streamk) {
       hipLaunchKernelGGL((k_wgrad_sk<C>), dim3(a.sk_G), dim3(C::THREADS), 0, s, a);
@@ -1366,6 +1429,12 @@ hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
     }
   }
   if (a.nsplit == 1) return hipSuccess;
+  if (a.split_tiles > 0) {
+    using C = typename Cfgs<E>::Wgrad;
+    const int64_t n4 = (int64_t)a.split_tiles * C::BM * C::BN / 4;
+    hipLaunchKernelGGL((k_wgrad_reduce_tiles<C>), dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -550,3 +550,25 @@ def test_full_size_residual_sublayer():
     for k in ("dx", "dgamma", "dA"):
         assert_close(host(g[k]), rbw[k], wl.dtype, k)
     assert_close(host(g["dB"][0]), rbw["dB"][0], wl.dtype, "dB0")
+
+
+@pytest.mark.parametrize("wl", [
+    # 384 weight-gradient tiles: 128 dB tiles run as two token halves, 256 whole
+    Workload("bf16_wgrad_split_tiles", 2048, 4096, 1024, 3, "silu", "bf16"),
+    # ragged: partial rank tiles (r = 960), T not a multiple of the k step
+    Workload("bf16_wgrad_split_tiles_ragged", 2050, 4096, 960, 3, "identity", "bf16"),
+], ids=lambda w: w.name)
+def test_backward_split_tiles(wl):
+    """Weight gradients that split only some (dB) tiles over two token halves:
+    every gradient compared whole."""
+    _say("split tiles bwd", wl)
+    inp = make_inputs(wl, seed=15)
+    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy])
+    torch.cuda.synchronize()
+    ref = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), ref[k], wl.dtype, k)
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), ref["dB"][i], wl.dtype, f"dB{i}")
