@@ -56,6 +56,21 @@ def one_kernel_forward(wl) -> bool:
     return (wl.r == 64 and wl.g <= 4) or (wl.r == 128 and wl.g <= 2) or (wl.r == 256 and wl.g == 1)
 
 
+def wgrad_split_tiles(wl) -> int:
+    """Tiles the library's weight-gradient plan splits over two token halves
+    when the 256 x 256 tiles fill between one and two rounds of the 256 CUs (the
+    rest run whole); 0 when that plan does not apply."""
+    if wl.dtype != "bf16":
+        return 0
+    cd = lambda a, b: -(-a // b)
+    gr = wl.g * wl.r
+    tiles_b = wl.n_up * cd(wl.r, 256) * cd(wl.d, 256)
+    tiles = tiles_b + cd(wl.d, 256) * cd(gr, 256)
+    S = 512 - tiles
+    ok = tiles > 256 and 0 < S <= tiles_b and (tiles - S) % 8 == 0 and (2 * S) % 8 == 0 and cd(wl.T, 64) >= 32
+    return S if ok else 0
+
+
 def kernel_work(wl, name: str):
     """Algorithmic (flops, HBM bytes) of one launch of kernel `name`: every
     operand read once and every result written once; GEMM flops only."""
@@ -78,7 +93,12 @@ def kernel_work(wl, name: str):
         return (2.0 * T * r * d * nu + 2.0 * T * d * gr,
                 e * (T * (zcols or gr) + nu * T * d + T * d + T * gr + d * gr) + 4 * (d * gr + nu * r * d))
     if name == "wgrad_reduce":   # the split-K sum: only its fp32 results count
+        split = wgrad_split_tiles(wl)
+        if split:   # only the split (dB) tiles are summed
+            return 0.0, 4 * split * 256 * 256
         return 0.0, 4 * (d * gr + nu * r * d)
+    if name == "sum_parts":   # dgamma from the whole dA tiles' row partials
+        return 0.0, 4 * d * (-(-gr // 256) * 2 + 1)
     if name == "dx":   # the residual variant also reads the residual path's gradient
         return 2.0 * T * gr * d, e * (T * gr + d * gr + (3 if wl.residual else 2) * T * d) + 4 * T
     if name == "fold_gamma":   # the one-kernel small-rank path also reorders B

@@ -373,36 +373,79 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   Opnd oa{static_cast<const E*>(a.z) + (int64_t)br * a.r, a.ldz, a.T, a.r};
   Opnd ob{a.B[br], a.d, a.d, a.r};
   f32x16 acc[C::MB][C::NB];
-  mainloop<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.r, lds, nullptr, acc);
   E* y = static_cast<E*>(a.y[br]);
-  const E* res = static_cast<const E*>(a.res[br]);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   char LR_LDS* reg = stage_region<C>(lds);
+  // residual rows of 32-row block 0 are loaded during the last k step, those of
+  // block mb+1 while block mb is computed, where a block's sweep is at most 8
+  // iterations (the buffers fit the registers); otherwise each block's residual
+  // rows are loaded, all at once, when it is due
+  constexpr bool RES_PF = RES && Sweep<C, C::WTN>::IT <= 8;
+  if constexpr (RES_PF) {
+    using R = Raw4<E>;
+    using SW = Sweep<C, C::WTN>;
+    const E* res = static_cast<const E*>(a.res[br]);
+    const SW sw;
+    const int col = n0 + wn * C::WTN + sw.cl;
+    const bool cok = col < a.d;
+    typedef typename R::T Buf[SW::IT];
+    Buf r0, r1;
+    auto load_block = [&](int mb, Buf& buf) {
+      const int rb = m0 + wm * C::WTM + mb * 32;
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) {
-    stage_block<C>(acc, mb, reg);
-    const int rbase = m0 + wm * C::WTM + mb * 32;
-    if constexpr (RES) {
-      // the block's residual rows are loaded first, all in flight together
-      sweep_block_pre<C, C::WTN, 1>(
-          reg,
-          [&](int rl, int cl, float4* in) {
-            const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
-            in[0] = row < a.T && col < a.d ? load4(res + (int64_t)row * a.d + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-          },
-          [&](int rl, int cl, const char LR_LDS* rp, const float4* in) {
-            const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
-            if (row >= a.T || col >= a.d) return;
-            const float4 v = lds_f4(rp + cl * 4);
-            store4(y + (int64_t)row * a.d + col, v.x + in[0].x, v.y + in[0].y, v.z + in[0].z, v.w + in[0].w);
-          });
-    } else {
-      sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
-        const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
-        if (row >= a.T || col >= a.d) return;
-        const float4 v = lds_f4(rp + cl * 4);
-        store4(y + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
-      });
+      for (int it = 0; it < SW::IT; ++it) {
+        const int row = rb + sw.rl(it);
+        buf[it] = row < a.T && cok ? R::load(res + (int64_t)row * a.d + col) : R::zero();
+      }
+    };
+    mainloop<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.r, lds, nullptr, acc,
+                                    [&]() { load_block(0, r0); });
+    auto block = [&](int mb, const Buf& cur, Buf& nxt) {
+      if (mb + 1 < C::MB) load_block(mb + 1, nxt);
+      stage_block<C>(acc, mb, reg);
+      const int rb = m0 + wm * C::WTM + mb * 32;
+#pragma unroll
+      for (int it = 0; it < SW::IT; ++it) {
+        const int rl = sw.rl(it), row = rb + rl;
+        if (row >= a.T || !cok) continue;
+        const float4 v = lds_f4(reg + rl * RowStage<C>::PITCH + sw.cl * 4);
+        const float4 r4 = R::f4(cur[it]);
+        store4(y + (int64_t)row * a.d + col, v.x + r4.x, v.y + r4.y, v.z + r4.z, v.w + r4.w);
+      }
+    };
+#pragma unroll
+    for (int mb = 0; mb < C::MB; mb += 2) {
+      block(mb, r0, r1);
+      if (mb + 1 < C::MB) block(mb + 1, r1, r0);
+    }
+  } else {
+    const E* res = static_cast<const E*>(a.res[br]);
+    mainloop<C, false, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, a.r, lds, nullptr, acc);
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      stage_block<C>(acc, mb, reg);
+      const int rbase = m0 + wm * C::WTM + mb * 32;
+      if constexpr (RES) {
+        sweep_block_pre<C, C::WTN, 1>(
+            reg,
+            [&](int rl, int cl, float4* in) {
+              const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+              in[0] = row < a.T && col < a.d ? load4(res + (int64_t)row * a.d + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+            },
+            [&](int rl, int cl, const char LR_LDS* rp, const float4* in) {
+              const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+              if (row >= a.T || col >= a.d) return;
+              const float4 v = lds_f4(rp + cl * 4);
+              store4(y + (int64_t)row * a.d + col, v.x + in[0].x, v.y + in[0].y, v.z + in[0].z, v.w + in[0].w);
+            });
+      } else {
+        sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
+          const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
+          if (row >= a.T || col >= a.d) return;
+          const float4 v = lds_f4(rp + cl * 4);
+          store4(y + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
+        });
+      }
     }
   }
 }

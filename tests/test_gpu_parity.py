@@ -572,3 +572,22 @@ def test_backward_split_tiles(wl):
         assert_close(host(g[k]), ref[k], wl.dtype, k)
     for i in range(len(B)):
         assert_close(host(g["dB"][i]), ref["dB"][i], wl.dtype, f"dB{i}")
+
+
+@pytest.mark.parametrize("wl", [
+    # 891 up-projection tiles (3.5 rounds), ragged T, a partial last column tile
+    # (d = 2112), K = 320 (five k steps)
+    Workload("bf16_up_many_tiles_ragged", 8269, 2112, 320, 3, "silu", "bf16"),
+    # SwiGLU's single up-projection, 1024 tiles
+    Workload("bf16_up_many_tiles_swiglu", 4096, 4096, 512, 2, "swiglu", "bf16"),
+], ids=lambda w: w.name)
+def test_forward_up_many_tiles(wl):
+    """Up-projections over several rounds of tiles with ragged edges: h and
+    every y_i compared whole."""
+    _say("up many tiles", wl)
+    inp = make_inputs(wl, seed=16, with_dy=False)
+    _, _, y, h = _run_fwd(wl, inp)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    for i, yi in enumerate(y):
+        assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
