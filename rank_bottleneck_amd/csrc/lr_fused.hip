@@ -32,8 +32,7 @@
 // up-projection needs no LDS ring and no wait on other waves' loads.
 //
 // LDS (bytes from 0):
-//   phase 1: a ring of SX x tiles and its sink, then a ring of SA A'^T tiles and
-//     its sink;
+//   phase 1: a ring of SX x tiles, then a ring of SA A'^T tiles;
 //   phases 2-3 (after the ring is drained): z as [BM][64] tiles (K contiguous,
 //     swizzled as an MFMA A tile), the partial row sums of squares, then the
 //     fp32 staging of h (phase 2) or two bf16 y tiles (phase 3).
@@ -47,27 +46,30 @@ namespace lr {
 template <int GR, int K3, int NBR>
 struct FusedGeo {
   static constexpr int BM = 64;
-  static constexpr int BK1 = GR > 128 ? 32 : 64;
+  static constexpr int BK1 = 64;
   // phase-1 rings: x tiles (from HBM, the MMA waves' DMA) SX stages deep, A'^T
   // tiles (L2-resident, the store waves' DMA) SA deep; each role waits only for
-  // its own loads, so the x stream keeps 7-15 stages in flight however large
-  // the A'^T tiles are
-  static constexpr int SX = GR == 64 ? 12 : (GR == 128 ? 8 : 16);
-  static constexpr int SA = 4;
+  // its own loads, so the x stream keeps 7-11 stages in flight however large
+  // the A'^T tiles are.  Every width takes 64-deep stages: the fixed cost of a
+  // stage (wait, barrier, DMA issue) is paid once per 64 k values, which for
+  // g*r = 256 measured 10% faster than 32-deep stages in a deeper ring.
+  static constexpr int SX = GR == 64 ? 12 : 8;
+  static constexpr int SA = GR > 128 ? 3 : 4;
   // phase 1 tile [BM, GR], k split inside the work-group, so that each wave has
   // 4-8 independent accumulators and every LDS fragment is read by one wave (or
   // one wave pair):
-  //   g*r <= 128 (BK = 64, four 16-deep sub-steps per stage): MMA wave w the
-  //     whole tile over sub-step w; NSP = 4 partials, added in phase 2;
-  //   wider (BK = 32, two sub-steps): MMA wave w sub-step w/2 and column half
-  //     w%2, all BM rows; the sub-step-1 waves add their partial into the
-  //     sub-step-0 waves' staging in place (four partials would not fit in LDS).
-  // NSS = partial row sums of squares (one per sub-step).
+  // Each stage holds four 16-deep k sub-steps.
+  //   g*r <= 128: MMA wave w the whole tile over sub-step w; NSP = 4 partials,
+  //     added in phase 2;
+  //   wider: MMA wave w sub-steps w/2 and w/2 + 2 and column half w%2, all BM
+  //     rows; the waves of sub-steps 1 and 3 add their partial into the others'
+  //     staging in place (four partials would not fit in LDS).
+  // NSS = partial row sums of squares (one per wave's set of sub-steps).
   using C1 = PipeCfg<BM, GR, BK1, 2, 2, 2>;  // tile and fragment geometry
   static constexpr bool KSPLIT = GR <= 128;
   static constexpr int NSP = KSPLIT ? 4 : 1, NSS = KSPLIT ? 4 : 2;
   static constexpr int MB1 = 2, NB1 = KSPLIT ? GR / 32 : GR / 64;
-  static_assert(C1::KS == (KSPLIT ? 4 : 2), "one k sub-step per MMA wave (pair)");
+  static_assert(C1::KS == 4, "four k sub-steps per stage");
   // phase 3 tile [BM, BN3] per column tile: each MMA wave all BM rows of NB3
   // 32-column blocks; the B fragments of PF column tiles ahead in flight
   // (register buffers NBUF = PF + 1), 48-64 KB per CU.  NB3 = 2 for g*r = 64
@@ -82,8 +84,8 @@ struct FusedGeo {
   static constexpr int KT = K3 / 64;  // 64-deep k blocks of one branch's z
 
   static constexpr int XB = C1::A_BYTES, AB = C1::B_BYTES;  // one x / A'^T stage
-  static constexpr int X_SINK = SX * XB, A_RING = X_SINK + XB, A_SINK = A_RING + SA * AB;
-  static constexpr int P1 = A_SINK + AB;
+  static constexpr int A_RING = SX * XB;
+  static constexpr int P1 = A_RING + SA * AB;
   static constexpr int ZT = BM * 128;                  // one [BM][64] bf16 z tile
   static constexpr int ZB = NBR * KT * ZT;
   static constexpr int ROWSS = ZB;                     // NSS x BM partial sums of squares
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool mma = wave < 4;
   const int w = wave & 3;                 // index within the role
-  const int wm = w >> 1, wn = w & 1;      // wide phase 1: k sub-step wm, column half wn
+  const int wm = w >> 1, wn = w & 1;      // wide phase 1: k sub-steps wm, wm + 2, column half wn
   const int u = w * 64 + lane;            // store-role thread index 0..255
   const int m0 = blockIdx.x * G::BM;
   const int d = a.d;
@@ -151,15 +153,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dat.init(oa, MapId{}, 0, w, lane);
     dat.init_range(oa, 0, 0);
   }
-  // stages past the end read an empty range into the ring's sink, which keeps
-  // each role's load count per k step the same
+  // stages past the end read an empty range, which keeps each role's load count
+  // per k step the same; they land in the slot of stage st - S, consumed before
+  // the barrier that precedes the issue, and no later stage maps there
   auto issue_x = [&](int st) {
     const bool live = st < nk1;
-    dxt.issue(dxt.rsrc(st, live), lds0 + (live ? (st % G::SX) * G::XB : G::X_SINK), w);
+    dxt.issue(dxt.rsrc(st, live), lds0 + (st % G::SX) * G::XB, w);
   };
   auto issue_a = [&](int st) {
     const bool live = st < nk1;
-    dat.issue(dat.rsrc(st, live), lds0 + (live ? G::A_RING + (st % G::SA) * G::AB : G::A_SINK), w);
+    dat.issue(dat.rsrc(st, live), lds0 + G::A_RING + (st % G::SA) * G::AB, w);
   };
   if (mma) {
 #pragma unroll
@@ -180,22 +183,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       issue_x(kt + G::SX - 1);
       const char LR_LDS* ta = ldsp + (kt % G::SX) * G::XB;
       const char LR_LDS* tb = ldsp + G::A_RING + (kt % G::SA) * G::AB;
-      // sub-step s1 of the stage, all BM rows, columns col0 .. col0 + 32*NB1
-      const int s1 = G::KSPLIT ? w : wm, col0 = G::KSPLIT ? 0 : wn * (GR / 2);
-      uint4 fa[MB1], fb[NB1];
+      // sub-step(s) s1 of the stage, all BM rows, columns col0 .. col0 + 32*NB1
+      const int col0 = G::KSPLIT ? 0 : wn * (GR / 2);
 #pragma unroll
-      for (int mb = 0; mb < MB1; ++mb) fa[mb] = frag<C1, G::BM, false>(ta, mb * 32, s1, lane);
+      for (int sp = 0; sp < (G::KSPLIT ? 1 : 2); ++sp) {
+        const int s1 = G::KSPLIT ? w : wm + 2 * sp;
+        uint4 fa[MB1], fb[NB1];
 #pragma unroll
-      for (int nb = 0; nb < NB1; ++nb) fb[nb] = frag<C1, GR, false>(tb, col0 + nb * 32, s1, lane);
+        for (int mb = 0; mb < MB1; ++mb) fa[mb] = frag<C1, G::BM, false>(ta, mb * 32, s1, lane);
 #pragma unroll
-      for (int mb = 0; mb < MB1; ++mb) {
-        ss[mb] = frag_sumsq(fa[mb], ss[mb]);
+        for (int nb = 0; nb < NB1; ++nb) fb[nb] = frag<C1, GR, false>(tb, col0 + nb * 32, s1, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB1; ++nb) mfma_chunk(acc1[mb][nb], fb[nb], fa[mb], (bf16*)nullptr);
+        for (int mb = 0; mb < MB1; ++mb) {
+          ss[mb] = frag_sumsq(fa[mb], ss[mb]);
+#pragma unroll
+          for (int nb = 0; nb < NB1; ++nb) mfma_chunk(acc1[mb][nb], fb[nb], fa[mb], (bf16*)nullptr);
+        }
       }
     }
   }
-  wait_vmcnt<0>();  // the sink loads of dead stages (both roles)
+  wait_vmcnt<0>();  // the empty loads of dead stages (both roles)
   lgkm_wait0();
   block_barrier();  // the rings are dead from here on
 
@@ -228,13 +235,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mb = 0; mb < MB1; ++mb) {
       ss[mb] += __shfl_xor(ss[mb], 32);
-      // sub-step s1's partial (KSPLIT: every wave; else the column-half-0 waves)
+      // the partial of this wave's sub-step(s) (KSPLIT: every wave; else the column-half-0 waves)
       if ((G::KSPLIT || wn == 0) && lane < 32) ssp[(G::KSPLIT ? w : wm) * G::BM + mb * 32 + lane] = ss[mb];
     }
   }
   if constexpr (!G::KSPLIT) {
     lgkm_wait0();
-    block_barrier();  // the sub-step-0 partial is staged
+    block_barrier();  // the wm = 0 waves' partial is staged
     if (mma && wm == 1) stage_acc1(0, wn * (GR / 2), true);
   }
   lgkm_wait0();
