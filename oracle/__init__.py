@@ -8,8 +8,11 @@ written from the BOOST pages:
 
   "BOOST: BOttleneck-Optimized Scalable Training Framework for Low-Rank Large
   Language Models" -- technical summary (gist.science, §1 Problem statement,
-  §2.1 Bottleneck-aware tensor parallelism, §2.2 System-level optimisations)
-  and the arXiv abstract (2512.12131).
+  §2.1 Bottleneck-aware tensor parallelism, §2.2 System-level optimisations,
+  §4 results) and the arXiv abstract (2512.12131).
+
+``block`` is the bottleneck block itself; ``mlp`` the per-projection low-rank
+SwiGLU MLP (the other reading of the SwiGLU wiring).
 
 Where the pages leave a step open (the block formula, the nonlinearity, the
 RMSNorm formula, the checkpoint contents), the oracle takes the plain readings
@@ -22,6 +25,7 @@ unpinned".
 """
 from .block import (act_forward, act_backward, rms_stats, rmsnorm, block_fwd, block_bwd,
                     down_partial, up_finish, branch_slices, working_precision)
+from .mlp import mlp_fwd, mlp_bwd
 
 __all__ = ["act_forward", "act_backward", "rms_stats", "rmsnorm", "block_fwd", "block_bwd",
-           "down_partial", "up_finish", "branch_slices", "working_precision"]
+           "down_partial", "up_finish", "branch_slices", "working_precision", "mlp_fwd", "mlp_bwd"]
