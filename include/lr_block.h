@@ -211,6 +211,56 @@ lr_status lr_up_finish(const lr_dims* dims, const float* partial, const float* s
  * Returns 0 for dims that the calls would reject. */
 size_t lr_block_workspace_size(const lr_dims* dims, int backward);
 
+/* Per-projection low-rank SwiGLU MLP: the other reading of how the block's
+ * SwiGLU is wired.  The MLP sublayer of the LLaMA-2 models the pages pre-train
+ * (technical summary §4) keeps SwiGLU at its full width f, and each of its
+ * three linear maps is a low-rank layer of rank r with nothing between its two
+ * factors (§1, §2.1).  The two input-side down factors read the same normalised
+ * input and are concatenated, their up factors run as a batch (§2.2, linear
+ * layer grouping); the checkpoint is the two narrow tensors h_in and h_out
+ * (§2.2, low-rank activation checkpointing), from which the backward
+ * recomputes gate, up and s.
+ *   rstd_t = (sum_j x_tj^2 / d + eps)^(-1/2)
+ *   h_in   = diag(rstd) . x . diag(gamma) . A_in         A_in = [A_g | A_u], [d, 2r]
+ *   gate   = h_in[:, :r] . B_g,  up = h_in[:, r:] . B_u   B_g, B_u [r, f]
+ *   s      = SiLU(gate) * up                               [T, f]
+ *   h_out  = s . A_o                                       A_o [f, r]
+ *   out    = h_out . B_o  (+ residual)                     B_o [r, d]
+ * Element types as for the block (dims->dtype; weight gradients fp32).
+ * Supported: T >= 0; d, f and r positive multiples of 64. */
+typedef struct {
+  int64_t T, d, f, r;   /* tokens, model width, MLP width, rank of every factorised linear */
+  float eps;
+  lr_dtype dtype;
+} lr_mlp_dims;
+
+/* Workspace bytes of lr_mlp_fwd (backward == 0) or lr_mlp_bwd (backward != 0);
+ * 0 for dims the calls would reject.  The forward holds gate and s, the
+ * backward gate, up and s ([T, f] each). */
+size_t lr_mlp_workspace_size(const lr_mlp_dims* dims, int backward);
+
+/* Forward.  x [T, d], gamma [d], A_in [d, 2r], B_g and B_u [r, f], A_o [f, r],
+ * B_o [r, d]; out [T, d].  residual [T, d] or NULL (none), may equal out.
+ * h_in_save [T, 2r], h_out_save [T, r] (the checkpoint) and rstd_save [T] (fp32)
+ * may each be NULL (inference).  Errors as lr_block_fwd. */
+lr_status lr_mlp_fwd(const lr_mlp_dims* dims, const void* x, const void* gamma, const void* A_in,
+                     const void* B_g, const void* B_u, const void* A_o, const void* B_o,
+                     const void* residual, void* out, void* h_in_save, void* h_out_save, float* rstd_save,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward for the upstream gradient dout [T, d].  h_in_saved and h_out_saved
+ * are the forward's checkpoint; rstd_saved [T] or NULL (recomputed from x).
+ * dx [T, d] (dtype) = the MLP's input gradient (+ dx_residual [T, d] when
+ * non-NULL; for out = x + mlp(x) pass dout, and dx_residual may equal dx).
+ * Weight gradients (fp32, overwritten): dgamma [d], dA_in [d, 2r], dB_g and
+ * dB_u [r, f], dA_o [f, r], dB_o [r, d].  Errors as lr_block_bwd. */
+lr_status lr_mlp_bwd(const lr_mlp_dims* dims, const void* x, const void* gamma, const void* A_in,
+                     const void* B_g, const void* B_u, const void* A_o, const void* B_o,
+                     const void* h_in_saved, const void* h_out_saved, const float* rstd_saved,
+                     const void* dout, const void* dx_residual, void* dx, float* dgamma, float* dA_in,
+                     float* dB_g, float* dB_u, float* dA_o, float* dB_o, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
 /* Kernel timing for benchmarks (not part of the block's arithmetic).
  * Between lr_trace_begin and lr_trace_end, every kernel that an entry point
  * launches from the CALLING THREAD whose name matches `kernel` (NULL: all) is

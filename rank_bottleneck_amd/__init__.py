@@ -7,8 +7,9 @@ raise.
 
 The functions carry the C entry points' names (rmsnorm_online, lr_block_fwd,
 lr_block_bwd, lr_down_partial, lr_up_finish, lr_block_workspace_size,
-lr_status_str) and take torch tensors; ``fwd``/``bwd``/``down_partial``/
-``up_finish`` additionally allocate the outputs and the workspace.
+lr_mlp_fwd, lr_mlp_bwd, lr_status_str, ...) and take torch tensors;
+``fwd``/``bwd``/``down_partial``/``up_finish``/``mlp_fwd``/``mlp_bwd``
+additionally allocate the outputs and the workspace.
 """
 from __future__ import annotations
 
@@ -34,6 +35,11 @@ class LrDims(ctypes.Structure):
                 ("act", ctypes.c_int32)]
 
 
+class LrMlpDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64), ("r", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
 class LrError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {lr_status_str(status)} ({status})")
@@ -42,8 +48,9 @@ class LrError(RuntimeError):
 
 _lib = None
 ENTRY_POINTS = ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
-                "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_block_fwd_noalloc", "lr_down_partial", "lr_up_finish", "lr_block_workspace_size", "lr_status_str", "lr_trace_begin",
-                "lr_trace_count", "lr_trace_elapsed", "lr_trace_end")
+                "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_block_fwd_noalloc", "lr_down_partial",
+                "lr_up_finish", "lr_block_workspace_size", "lr_mlp_fwd", "lr_mlp_bwd", "lr_mlp_workspace_size",
+                "lr_status_str", "lr_trace_begin", "lr_trace_count", "lr_trace_elapsed", "lr_trace_end")
 
 
 def load(path: Optional[str] = None) -> ctypes.CDLL:
@@ -68,9 +75,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lr_block_fwd_noalloc.argtypes = [dims, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lr_down_partial.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.lr_up_finish.argtypes = [dims, vp, vp, vp, vp, vp, vp, sz, vp]
+    mdims = ctypes.POINTER(LrMlpDims)
+    lib.lr_mlp_fwd.argtypes = [mdims] + [vp] * 13 + [sz, vp]
+    lib.lr_mlp_bwd.argtypes = [mdims] + [vp] * 20 + [sz, vp]
+    lib.lr_mlp_workspace_size.argtypes = [mdims, ctypes.c_int]
+    lib.lr_mlp_workspace_size.restype = sz
     for f in ("rmsnorm_online", "lr_block_fwd", "lr_block_fwd_rstd", "lr_block_bwd", "lr_block_bwd_rstd",
               "lr_block_fwd_residual", "lr_block_bwd_residual", "lr_block_fwd_noalloc", "lr_down_partial",
-              "lr_up_finish"):
+              "lr_up_finish", "lr_mlp_fwd", "lr_mlp_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lr_block_workspace_size.argtypes = [dims, ctypes.c_int]
     lib.lr_block_workspace_size.restype = sz
@@ -211,6 +223,31 @@ def lr_up_finish(dims: LrDims, partial, sumsq, B: Sequence, y: Sequence, h_save,
                                                 _stream(stream)))
 
 
+def make_mlp_dims(T: int, d: int, f: int, r: int, dtype: str = "bf16", eps: float = 1e-6) -> LrMlpDims:
+    return LrMlpDims(T, d, f, r, eps, DTYPES[dtype])
+
+
+def lr_mlp_workspace_size(dims: LrMlpDims, backward: bool) -> int:
+    return int(load().lr_mlp_workspace_size(ctypes.byref(dims), 1 if backward else 0))
+
+
+def lr_mlp_fwd(dims: LrMlpDims, x, gamma, A_in, B_g, B_u, A_o, B_o, residual, out, h_in_save, h_out_save,
+               rstd_save, ws, stream=None) -> None:
+    _check("lr_mlp_fwd", load().lr_mlp_fwd(
+        ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A_in), _ptr(B_g), _ptr(B_u), _ptr(A_o), _ptr(B_o),
+        _ptr(residual), _ptr(out), _ptr(h_in_save), _ptr(h_out_save), _ptr(rstd_save), _ptr(ws), _ws_nbytes(ws),
+        _stream(stream)))
+
+
+def lr_mlp_bwd(dims: LrMlpDims, x, gamma, A_in, B_g, B_u, A_o, B_o, h_in_saved, h_out_saved, rstd_saved, dout,
+               dx_residual, dx, dgamma, dA_in, dB_g, dB_u, dA_o, dB_o, ws, stream=None) -> None:
+    _check("lr_mlp_bwd", load().lr_mlp_bwd(
+        ctypes.byref(dims), _ptr(x), _ptr(gamma), _ptr(A_in), _ptr(B_g), _ptr(B_u), _ptr(A_o), _ptr(B_o),
+        _ptr(h_in_saved), _ptr(h_out_saved), _ptr(rstd_saved), _ptr(dout), _ptr(dx_residual), _ptr(dx),
+        _ptr(dgamma), _ptr(dA_in), _ptr(dB_g), _ptr(dB_u), _ptr(dA_o), _ptr(dB_o), _ptr(ws), _ws_nbytes(ws),
+        _stream(stream)))
+
+
 def lr_trace_begin(kernel: Optional[str] = None, max_launches: int = 1024) -> None:
     _check("lr_trace_begin", load().lr_trace_begin(None if kernel is None else kernel.encode(), max_launches))
 
@@ -292,3 +329,38 @@ def up_finish(dims: LrDims, partial, sumsq, B: Sequence, save_h: bool = True, ws
     ws = workspace(dims, False, dev) if ws is None else ws
     lr_up_finish(dims, partial, sumsq, B, y, h, ws, stream)
     return y, h
+
+
+def mlp_workspace(dims: LrMlpDims, backward: bool, device="cuda") -> torch.Tensor:
+    n = lr_mlp_workspace_size(dims, backward)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mlp_fwd(dims: LrMlpDims, x, gamma, A_in, B_g, B_u, A_o, B_o, residual=None, save: bool = True, rstd=None,
+            ws=None, stream=None):
+    """Allocating MLP forward: returns (out, h_in or None, h_out or None).  rstd:
+    an fp32 [T] tensor that receives the rows' rstd, or None."""
+    dt = TORCH_DTYPE[dims.dtype]
+    dev = x.device
+    out = torch.empty((dims.T, dims.d), dtype=dt, device=dev)
+    h_in = torch.empty((dims.T, 2 * dims.r), dtype=dt, device=dev) if save else None
+    h_out = torch.empty((dims.T, dims.r), dtype=dt, device=dev) if save else None
+    ws = mlp_workspace(dims, False, dev) if ws is None else ws
+    lr_mlp_fwd(dims, x, gamma, A_in, B_g, B_u, A_o, B_o, residual, out, h_in, h_out, rstd, ws, stream)
+    return out, h_in, h_out
+
+
+def mlp_bwd(dims: LrMlpDims, x, gamma, A_in, B_g, B_u, A_o, B_o, h_in, h_out, dout, rstd=None, dx_residual=None,
+            ws=None, stream=None):
+    """Allocating MLP backward: returns dict(dx, dgamma, dA_in, dB_g, dB_u, dA_o, dB_o)."""
+    dt = TORCH_DTYPE[dims.dtype]
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dx": torch.empty((dims.T, dims.d), dtype=dt, device=dev), "dgamma": torch.empty(dims.d, **f32),
+         "dA_in": torch.empty((dims.d, 2 * dims.r), **f32), "dB_g": torch.empty((dims.r, dims.f), **f32),
+         "dB_u": torch.empty((dims.r, dims.f), **f32), "dA_o": torch.empty((dims.f, dims.r), **f32),
+         "dB_o": torch.empty((dims.r, dims.d), **f32)}
+    ws = mlp_workspace(dims, True, dev) if ws is None else ws
+    lr_mlp_bwd(dims, x, gamma, A_in, B_g, B_u, A_o, B_o, h_in, h_out, rstd, dout, dx_residual, g["dx"], g["dgamma"],
+               g["dA_in"], g["dB_g"], g["dB_u"], g["dA_o"], g["dB_o"], ws, stream)
+    return g

@@ -77,7 +77,7 @@ size_t bwd_ws_t(const lr_dims* d) {
   const size_t es = sizeof(E), gr = (size_t)(d->g * d->r), T = (size_t)d->T;
   const int nsp = n_up_of(d) * lr::dz_nparts<E>((int)d->r);
   const int ngp = lr::wgrad_nparts<E>((int)gr);
-  const lr::WgradPlan wp = lr::wgrad_plan<E>((int)d->T, (int)d->d, (int)d->r, (int)d->g, n_up_of(d));
+  const lr::WgradPlan wp = lr::wgrad_plan<E>((int)d->T, (int)d->d, (int)d->r, (int)d->g, n_up_of(d), (int)d->d);
   const size_t part = (size_t)wp.part_floats * 4;
   return align_up(T * 4) + align_up(T * gr * es) * 2 + align_up(T * lr::spart_stride(nsp) * 4) +
          align_up((size_t)d->d * ngp * 4) +
@@ -196,7 +196,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   const int sps = lr::spart_stride(nsp);
   float* spart = cv.take<float>((size_t)T * sps * 4);
   float* gpart = cv.take<float>((size_t)D * ngp * 4);
-  const lr::WgradPlan wp = lr::wgrad_plan<E>(T, D, r, g, n_up);
+  const lr::WgradPlan wp = lr::wgrad_plan<E>(T, D, r, g, n_up, D);
   const int ns = wp.nsplit;
   // the split-tile plan reduces only dB tiles; dA's tiles run whole and leave
   // dgamma partials, as an unsplit pass does
@@ -224,7 +224,7 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   wa.ldz = d->act == LR_ACT_SWIGLU ? r : gr;
   for (int i = 0; i < n_up; ++i) { wa.dy[i] = dy[i]; wa.dB[i] = dB[i]; }
   wa.x = x; wa.dh = dh; wa.A = A; wa.gamma = gamma; wa.dA = dA; wa.dgamma = dgamma; wa.gpart = gpart; wa.ngpart = ngp;
-  wa.T = T; wa.d = D; wa.r = r; wa.g = g; wa.n_up = n_up;
+  wa.T = T; wa.d = D; wa.dn = D; wa.r = r; wa.g = g; wa.n_up = n_up;
   wa.nsplit = ns; wa.wpart = wpart; wa.part_stride = pstride; wa.part_offA = (int64_t)n_up * r * D;
   wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
   wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles; wa.split_tiles = wp.split_tiles;
@@ -333,6 +333,184 @@ lr_status bwd_entry(const lr_dims* d, const void* x, const void* gamma, const vo
   return d->dtype == LR_BF16
              ? bwd_impl<bf16>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx_residual, dx, dgamma, dA, dB, ws, s)
              : bwd_impl<float>(d, x, gamma, A, B, h_saved, rstd_saved, dy, dx_residual, dx, dgamma, dA, dB, ws, s);
+}
+
+
+// ---------------------------------------------------------------- per-projection low-rank SwiGLU MLP
+// Input layers: the block with identity between its factors, g = 2 and
+// up-projections of width f; SwiGLU at width f in the second up-projection's
+// epilogue; output layer: a down factor without normalisation over width f and
+// an up factor back to d.  The backward recomputes gate, up and s from h_in.
+lr_status check_mlp(const lr_mlp_dims* m) {
+  if (!m) return LR_EINVAL;
+  if (m->dtype != LR_F32 && m->dtype != LR_BF16) return LR_EINVAL;
+  if (m->T < 0 || m->d <= 0 || m->f <= 0 || m->r <= 0) return LR_EINVAL;
+  if (!(m->eps >= 0.f) || !isfinite(m->eps)) return LR_EINVAL;
+  if (m->d % 64 || m->f % 64 || m->r % 64) return LR_EUNSUPPORTED;
+  if (m->T > (1ll << 30) || m->d > (1 << 20) || m->f > (1 << 20) || m->r > (1 << 19)) return LR_EUNSUPPORTED;
+  return LR_OK;
+}
+
+// A'_in, h_in, h_out, gate, s
+size_t mlp_fwd_ws(const lr_mlp_dims* m) {
+  const size_t es = esize(m->dtype), T = (size_t)m->T, d = (size_t)m->d, f = (size_t)m->f, r = (size_t)m->r;
+  return align_up(d * 2 * r * es) + align_up(T * 2 * r * es) + align_up(T * r * es) + 2 * align_up(T * f * es);
+}
+
+template <typename E>
+lr::WgradPlan mlp_plan_in(const lr_mlp_dims* m) {
+  return lr::wgrad_plan<E>((int)m->T, (int)m->d, (int)m->r, 2, 2, (int)m->f);
+}
+template <typename E>
+lr::WgradPlan mlp_plan_out(const lr_mlp_dims* m) {
+  return lr::wgrad_plan<E>((int)m->T, (int)m->f, (int)m->r, 1, 1, (int)m->d);
+}
+
+// rstd, gate, up, s, dh_out, dh_in, S' partials, dgamma partials, weight-gradient partials
+template <typename E>
+size_t mlp_bwd_ws_t(const lr_mlp_dims* m) {
+  const size_t es = sizeof(E), T = (size_t)m->T, d = (size_t)m->d, f = (size_t)m->f, r = (size_t)m->r;
+  const int nsp = 2 * lr::dz_nparts<E>((int)r);
+  const int ngp = lr::wgrad_nparts<E>(2 * (int)r);
+  const int64_t pf1 = mlp_plan_in<E>(m).part_floats, pf2 = mlp_plan_out<E>(m).part_floats;
+  return align_up(T * 4) + 3 * align_up(T * f * es) + align_up(T * r * es) + align_up(T * 2 * r * es) +
+         align_up(T * lr::spart_stride(nsp) * 4) + align_up(d * ngp * 4) +
+         align_up((size_t)(pf1 > pf2 ? pf1 : pf2) * 4);
+}
+size_t mlp_bwd_ws(const lr_mlp_dims* m) { return m->dtype == LR_BF16 ? mlp_bwd_ws_t<bf16>(m) : mlp_bwd_ws_t<float>(m); }
+
+template <typename E>
+lr_status mlp_fwd_impl(const lr_mlp_dims* m, const void* x, const void* gamma, const void* A_in, const void* B_g,
+                       const void* B_u, const void* A_o, const void* B_o, const void* residual, void* out,
+                       void* h_in_save, void* h_out_save, float* rstd_save, void* ws, hipStream_t s) {
+  const int T = (int)m->T, D = (int)m->d, F = (int)m->f, r = (int)m->r;
+  Carve cv{static_cast<char*>(ws)};
+  void* Ap = cv.take<void>((size_t)D * 2 * r * sizeof(E));
+  void* h_in = cv.take<void>((size_t)T * 2 * r * sizeof(E));
+  void* h_out = cv.take<void>((size_t)T * r * sizeof(E));
+  void* gate = cv.take<void>((size_t)T * F * sizeof(E));
+  void* sw = cv.take<void>((size_t)T * F * sizeof(E));
+  if (h_in_save) h_in = h_in_save;
+  if (h_out_save) h_out = h_out_save;
+  // input layers' down factors: [A_g | A_u] with gamma folded in, rstd applied late
+  LR_LAUNCH("fold_gamma", s, lr::launch_fold_gamma<E>(A_in, gamma, Ap, D, 2 * r, s));
+  lr::DownArgs da{};
+  da.x = x; da.Ap = Ap; da.T = T; da.d = D; da.r = r; da.g = 2; da.act = lr::ACT_IDENTITY; da.mode = lr::DOWN_BLOCK;
+  da.invD = 1.0f / (float)D; da.eps = m->eps; da.h = h_in; da.z = h_in; da.rstd = rstd_save;
+  LR_LAUNCH("down", s, lr::launch_down<E>(da, s));
+  // their up factors: gate, then up with s = SiLU(gate) * up formed in the epilogue
+  lr::UpArgs ug{};
+  ug.z = h_in; ug.ldz = 2 * r; ug.B[0] = B_g; ug.y[0] = gate; ug.T = T; ug.d = F; ug.r = r;
+  LR_LAUNCH("up", s, lr::launch_up<E>(ug, 1, s));
+  lr::UpArgs uu{};
+  uu.z = static_cast<const E*>(h_in) + r; uu.ldz = 2 * r; uu.B[0] = B_u; uu.y[0] = sw; uu.res[0] = gate; uu.swiglu = 1;
+  uu.T = T; uu.d = F; uu.r = r;
+  LR_LAUNCH("up", s, lr::launch_up<E>(uu, 1, s));
+  // output layer: down factor over width f (no normalisation), up factor to d
+  lr::DownArgs dd{};
+  dd.x = sw; dd.Ap = A_o; dd.T = T; dd.d = F; dd.r = r; dd.g = 1; dd.act = lr::ACT_IDENTITY; dd.mode = lr::DOWN_PLAIN;
+  dd.invD = 1.0f / (float)F; dd.eps = m->eps; dd.h = h_out; dd.z = h_out;
+  LR_LAUNCH("down", s, lr::launch_down<E>(dd, s));
+  lr::UpArgs uo{};
+  uo.z = h_out; uo.ldz = r; uo.B[0] = B_o; uo.y[0] = out; uo.res[0] = residual; uo.T = T; uo.d = D; uo.r = r;
+  LR_LAUNCH("up", s, lr::launch_up<E>(uo, 1, s));
+  return LR_OK;
+}
+
+// weight gradients of one layer group: the launch, then the reduction and the
+// dgamma sum where the plan needs them
+template <typename E>
+lr_status mlp_wgrad(lr::WgradArgs wa, const lr::WgradPlan& wp, int gr, float* gpart, int ngp, hipStream_t s) {
+  const int ns = wp.nsplit;
+  const bool reduced = wp.streamk || ns > 1;
+  const bool gamma_parts = wa.gamma && (!reduced || wp.split_tiles > 0);
+  wa.nsplit = ns;
+  wa.part_stride = (int64_t)wa.n_up * wa.r * wa.dn + (int64_t)wa.d * gr;
+  wa.part_offA = (int64_t)wa.n_up * wa.r * wa.dn;
+  wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
+  wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles; wa.split_tiles = wp.split_tiles;
+  {
+    const int BK = lr::gemm_bk<E>();
+    const int ksteps = (wa.T + BK - 1) / BK;
+    wa.ksplit = ((ksteps + ns - 1) / ns) * BK;
+  }
+  LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
+  if (reduced) LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
+  if (gamma_parts)
+    LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, wa.dgamma, wa.d, lr::wgrad_nparts_used<E>(gr, false), ngp, s));
+  return LR_OK;
+}
+
+template <typename E>
+lr_status mlp_bwd_impl(const lr_mlp_dims* m, const void* x, const void* gamma, const void* A_in, const void* B_g,
+                       const void* B_u, const void* A_o, const void* B_o, const void* h_in, const void* h_out,
+                       const float* rstd_saved, const void* dout, const void* dx_residual, void* dx, float* dgamma,
+                       float* dA_in, float* dB_g, float* dB_u, float* dA_o, float* dB_o, void* ws, hipStream_t s) {
+  const int T = (int)m->T, D = (int)m->d, F = (int)m->f, r = (int)m->r;
+  const int nsp = 2 * lr::dz_nparts<E>(r), sps = lr::spart_stride(nsp);
+  const int ngp = lr::wgrad_nparts<E>(2 * r);
+  const lr::WgradPlan p_in = mlp_plan_in<E>(m), p_out = mlp_plan_out<E>(m);
+  Carve cv{static_cast<char*>(ws)};
+  float* rstd_ws = cv.take<float>((size_t)T * 4);
+  void* gate = cv.take<void>((size_t)T * F * sizeof(E));
+  void* up = cv.take<void>((size_t)T * F * sizeof(E));
+  void* sw = cv.take<void>((size_t)T * F * sizeof(E));
+  void* dh_out = cv.take<void>((size_t)T * r * sizeof(E));
+  void* dh_in = cv.take<void>((size_t)T * 2 * r * sizeof(E));
+  float* spart = cv.take<float>((size_t)T * sps * 4);
+  float* gpart = cv.take<float>((size_t)D * ngp * 4);
+  float* wpart = cv.take<float>((size_t)(p_in.part_floats > p_out.part_floats ? p_in.part_floats : p_out.part_floats) * 4);
+
+  const float* rstd = rstd_saved;
+  if (!rstd) {
+    LR_LAUNCH("rms_stats", s,
+              lr::launch_rms_stats<E>(x, nullptr, nullptr, nullptr, rstd_ws, T, D, 1.0f / (float)D, m->eps, s));
+    rstd = rstd_ws;
+  }
+  // gate, up and s recomputed from the checkpoint h_in
+  lr::UpArgs ug{};
+  ug.z = h_in; ug.ldz = 2 * r; ug.B[0] = B_g; ug.y[0] = gate; ug.T = T; ug.d = F; ug.r = r;
+  LR_LAUNCH("up", s, lr::launch_up<E>(ug, 1, s));
+  lr::UpArgs uu{};
+  uu.z = static_cast<const E*>(h_in) + r; uu.ldz = 2 * r; uu.B[0] = B_u; uu.y[0] = sw; uu.y2[0] = up;
+  uu.res[0] = gate; uu.swiglu = 1; uu.T = T; uu.d = F; uu.r = r;
+  LR_LAUNCH("up", s, lr::launch_up<E>(uu, 1, s));
+
+  // output layer: dh_out = dout . B_o^T; dB_o = h_out^T . dout and dA_o = s^T . dh_out
+  lr::DzArgs zo{};
+  zo.dy[0] = dout; zo.B[0] = B_o; zo.h = h_out; zo.rstd = nullptr; zo.dh = dh_out; zo.z = nullptr;
+  zo.spart = nullptr; zo.spstride = 0; zo.T = T; zo.d = D; zo.r = r; zo.g = 1; zo.act = lr::ACT_IDENTITY;
+  LR_LAUNCH("dz", s, lr::launch_dz<E>(zo, 1, s));
+  lr::WgradArgs wo{};
+  wo.z = h_out; wo.ldz = r; wo.dy[0] = dout; wo.dB[0] = dB_o; wo.x = sw; wo.dh = dh_out; wo.A = nullptr;
+  wo.gamma = nullptr; wo.dA = dA_o; wo.dgamma = nullptr; wo.gpart = nullptr; wo.ngpart = 0; wo.wpart = wpart;
+  wo.T = T; wo.d = F; wo.dn = D; wo.r = r; wo.g = 1; wo.n_up = 1;
+  lr_status st = mlp_wgrad<E>(wo, p_out, r, nullptr, 0, s);
+  if (st != LR_OK) return st;
+  // ds = dh_out . A_o^T with the SwiGLU backward in the epilogue: dgate over
+  // gate, dup over up (s is no longer needed)
+  lr::DxArgs xo{};
+  xo.dh = dh_out; xo.A = A_o; xo.x = gate; xo.dres = up; xo.dx = gate; xo.dx2 = up; xo.swiglu = 1;
+  xo.T = T; xo.d = F; xo.r = r; xo.g = 1; xo.invD = 1.0f / (float)F;
+  LR_LAUNCH("dx", s, lr::launch_dx<E>(xo, s));
+
+  // input layers: the block's backward for dy = (dgate, dup)
+  lr::DzArgs zi{};
+  zi.dy[0] = gate; zi.dy[1] = up; zi.B[0] = B_g; zi.B[1] = B_u; zi.h = h_in; zi.rstd = rstd; zi.dh = dh_in;
+  zi.z = nullptr; zi.spart = spart; zi.spstride = sps; zi.T = T; zi.d = F; zi.r = r; zi.g = 2;
+  zi.act = lr::ACT_IDENTITY;
+  LR_LAUNCH("dz", s, lr::launch_dz<E>(zi, 2, s));
+  lr::WgradArgs wi{};
+  wi.z = h_in; wi.ldz = 2 * r; wi.dy[0] = gate; wi.dy[1] = up; wi.dB[0] = dB_g; wi.dB[1] = dB_u; wi.x = x;
+  wi.dh = dh_in; wi.A = A_in; wi.gamma = gamma; wi.dA = dA_in; wi.dgamma = dgamma; wi.gpart = gpart;
+  wi.ngpart = ngp; wi.wpart = wpart; wi.T = T; wi.d = D; wi.dn = F; wi.r = r; wi.g = 2; wi.n_up = 2;
+  if ((st = mlp_wgrad<E>(wi, p_in, 2 * r, gpart, ngp, s)) != LR_OK) return st;
+  lr::DxArgs xi{};
+  xi.dh = dh_in; xi.A = A_in; xi.x = x; xi.gamma = gamma; xi.rstd = rstd; xi.spart = spart; xi.nspart = nsp;
+  xi.spstride = sps; xi.dx = dx; xi.dres = dx_residual; xi.T = T; xi.d = D; xi.r = r; xi.g = 2;
+  xi.invD = 1.0f / (float)D;
+  LR_LAUNCH("dx", s, lr::launch_dx<E>(xi, s));
+  return LR_OK;
 }
 
 
@@ -488,6 +666,46 @@ lr_status lr_up_finish(const lr_dims* d, const float* partial, const float* sums
   if ((st = check_ws(ws, ws_bytes, fwd_ws(d))) != LR_OK) return st;
   return d->dtype == LR_BF16 ? finish_impl<bf16>(d, partial, sumsq, B, y, h_save, ws, s)
                              : finish_impl<float>(d, partial, sumsq, B, y, h_save, ws, s);
+}
+
+size_t lr_mlp_workspace_size(const lr_mlp_dims* m, int backward) {
+  if (check_mlp(m) != LR_OK) return 0;
+  return backward ? mlp_bwd_ws(m) : mlp_fwd_ws(m);
+}
+
+lr_status lr_mlp_fwd(const lr_mlp_dims* m, const void* x, const void* gamma, const void* A_in, const void* B_g,
+                     const void* B_u, const void* A_o, const void* B_o, const void* residual, void* out,
+                     void* h_in_save, void* h_out_save, float* rstd_save, void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_mlp(m);
+  if (st != LR_OK) return st;
+  if (!req_rows(x, m->T) || !req(gamma) || !req(A_in) || !req(B_g) || !req(B_u) || !req(A_o) || !req(B_o) ||
+      !opt(residual) || !req_rows(out, m->T) || !opt(h_in_save) || !opt(h_out_save) || !opt(rstd_save))
+    return LR_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, mlp_fwd_ws(m))) != LR_OK) return st;
+  return m->dtype == LR_BF16 ? mlp_fwd_impl<bf16>(m, x, gamma, A_in, B_g, B_u, A_o, B_o, residual, out, h_in_save,
+                                                  h_out_save, rstd_save, ws, s)
+                             : mlp_fwd_impl<float>(m, x, gamma, A_in, B_g, B_u, A_o, B_o, residual, out,
+                                                   h_in_save, h_out_save, rstd_save, ws, s);
+}
+
+lr_status lr_mlp_bwd(const lr_mlp_dims* m, const void* x, const void* gamma, const void* A_in, const void* B_g,
+                     const void* B_u, const void* A_o, const void* B_o, const void* h_in_saved,
+                     const void* h_out_saved, const float* rstd_saved, const void* dout, const void* dx_residual,
+                     void* dx, float* dgamma, float* dA_in, float* dB_g, float* dB_u, float* dA_o, float* dB_o,
+                     void* ws, size_t ws_bytes, hipStream_t s) {
+  lr_status st = check_mlp(m);
+  if (st != LR_OK) return st;
+  if (!req_rows(x, m->T) || !req(gamma) || !req(A_in) || !req(B_g) || !req(B_u) || !req(A_o) || !req(B_o) ||
+      !req_rows(h_in_saved, m->T) || !req_rows(h_out_saved, m->T) || !opt(rstd_saved) || !req_rows(dout, m->T) ||
+      !opt(dx_residual) || !req_rows(dx, m->T) || !req(dgamma) || !req(dA_in) || !req(dB_g) || !req(dB_u) ||
+      !req(dA_o) || !req(dB_o))
+    return LR_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, mlp_bwd_ws(m))) != LR_OK) return st;
+  return m->dtype == LR_BF16
+             ? mlp_bwd_impl<bf16>(m, x, gamma, A_in, B_g, B_u, A_o, B_o, h_in_saved, h_out_saved, rstd_saved, dout,
+                                  dx_residual, dx, dgamma, dA_in, dB_g, dB_u, dA_o, dB_o, ws, s)
+             : mlp_bwd_impl<float>(m, x, gamma, A_in, B_g, B_u, A_o, B_o, h_in_saved, h_out_saved, rstd_saved, dout,
+                                   dx_residual, dx, dgamma, dA_in, dB_g, dB_u, dA_o, dB_o, ws, s);
 }
 
 lr_status lr_trace_begin(const char* kernel, int max_launches) {

@@ -9,7 +9,14 @@ namespace lr {
 typedef __bf16 bf16;
 
 enum { ACT_IDENTITY = 0, ACT_SILU = 1, ACT_SWIGLU = 2 };
-enum { DOWN_BLOCK = 0, DOWN_PARTIAL = 1 };
+// DOWN_PLAIN: h = x . A with no normalisation (a low-rank layer's down factor
+// on an input that is not normalised)
+enum { DOWN_BLOCK = 0, DOWN_PARTIAL = 1, DOWN_PLAIN = 2 };
+// up-projection epilogues: y = acc; y = res + acc; y = SiLU(res) * acc
+enum { UP_PLAIN = 0, UP_RES = 1, UP_SWIGLU = 2 };
+// dx epilogues: the RMSNorm backward; the same plus dres; the SwiGLU backward
+// (x = gate, dres = up, dx = dgate, dx2 = dup) with no normalisation
+enum { DX_NORM = 0, DX_NORM_RES = 1, DX_SWIGLU = 2 };
 constexpr int MAX_G = 8;
 
 struct DownArgs {
@@ -54,17 +61,21 @@ struct UpArgs {
   const void* B[MAX_G];
   void* y[MAX_G];
   const void* res[MAX_G];  // residual_i [T, d] added to y_i (all null: none); may equal y[i]
-  int T, d, r;
+  // swiglu != 0: res[i] holds the gate and y_i = SiLU(res_i) * acc; y2[i], when
+  // non-null, receives acc as well
+  int swiglu;
+  void* y2[MAX_G];
+  int T, d, r;        // d: the output width (columns of B_i and y_i)
 };
 
 struct DzArgs {
   const void* dy[MAX_G];
   const void* B[MAX_G];
   const void* h;      // saved pre-activation [T, g*r]
-  const float* rstd;  // [T]
+  const float* rstd;  // [T], or null: no normalisation (the factor is 1)
   void* dh;           // [T, g*r]   rstd * dh
   void* z;            // sigma(h): [T, g*r] (SiLU) or [T, r] (SwiGLU); unused for identity
-  float* spart;       // [T, spstride]: partials of S' (columns past the partial count unused)
+  float* spart;       // [T, spstride]: partials of S' (columns past the partial count unused), or null
   int spstride;
   int T, d, r, g, act;
   int tile0;          // first tile of this launch (launch_dz sets it)
@@ -78,16 +89,17 @@ struct WgradArgs {
   const void* x;
   const void* dh;
   const void* A;
-  const void* gamma;
+  const void* gamma;  // null: no normalisation, dA = M and no dgamma (A unused)
   float* dA;
   float* dgamma;      // [d]: written by the reductions (launch_wgrad_reduce)
   float* gpart;       // [d, ngpart]: dgamma partials of an unsplit launch_wgrad
   int ngpart;
-  int T, d, r, g, n_up;
+  int T, d, r, g, n_up;     // d: width of x (rows of dA)
+  int dn;                   // width of dy_i (columns of dB_i)
   int nsplit, ksplit;       // token splits and tokens per split (a multiple of the k step)
   float* wpart;             // nsplit x part_stride fp32 partial tiles (nsplit > 1), or the stream-K slots
-  int64_t part_stride;      // n_up*r*d + d*g*r
-  int64_t part_offA;        // n_up*r*d
+  int64_t part_stride;      // n_up*r*dn + d*g*r
+  int64_t part_offA;        // n_up*r*dn
   // stream-K (streamk != 0): G work-groups split tiles*KS k steps evenly, the first R
   // taking Q+1 and the rest Q; each (sequence position, covering work-group) writes a
   // BM x BN fp32 slot at wpart[(position*maxseg + ordinal) * BM*BN].  Position p
@@ -121,6 +133,11 @@ struct DxArgs {
   int nspart, spstride;
   void* dx;
   const void* dres;    // [T, d] added to dx (the residual path's gradient), or null; may equal dx
+  // swiglu != 0: the SwiGLU backward instead of the RMSNorm one: x holds the
+  // gate and dres the up values, dx receives dgate and dx2 dup (both may equal
+  // their input); gamma, rstd and the S' partials are unused
+  int swiglu;
+  void* dx2;
   int T, d, r, g;
   float invD;
 };
@@ -168,6 +185,7 @@ inline int spart_stride(int nparts) { return (nparts + 3) & ~3; }
 template <typename E> int wgrad_nparts(int gr);
 template <typename E> int gemm_bk();
 template <typename E> int wgrad_nparts_used(int gr, bool reduced);
-template <typename E> WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up);
+// dn: width of dy_i and dB_i (d for the block)
+template <typename E> WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up, int dn);
 
 }  // namespace lr

@@ -246,7 +246,7 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, uint4* lds, int bid
     if (a.mode == DOWN_PARTIAL) {
       if (tn == 0 && m0 + i < a.T) a.sumsq[m0 + i] = ssv;
     } else {
-      const float rs = __builtin_amdgcn_rsqf(ssv * a.invD + a.eps);
+      const float rs = a.mode == DOWN_PLAIN ? 1.0f : __builtin_amdgcn_rsqf(ssv * a.invD + a.eps);
       rowss[i] = rs;
       if (a.rstd && tn == 0 && m0 + i < a.T) a.rstd[m0 + i] = rs;
     }
@@ -359,9 +359,20 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
 
 // ------------------------------------------------------------------ up projection
 // y_i = z_i . B_i (+ residual_i with RES); one launch over (branch, tile)
-template <class C, bool RES>
+// the up-projection's output from the accumulator v and the epilogue input r
+template <int EPI>
+__device__ __forceinline__ float4 up_out(const float4& v, const float4& r) {
+  if constexpr (EPI == UP_SWIGLU)
+    return make_float4(r.x * sigmoidf_(r.x) * v.x, r.y * sigmoidf_(r.y) * v.y, r.z * sigmoidf_(r.z) * v.z,
+                       r.w * sigmoidf_(r.w) * v.w);
+  else
+    return make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
+}
+
+template <class C, int EPI>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_up(UpArgs a) {
   using E = typename C::E;
+  constexpr bool RES = EPI != UP_PLAIN;
   __shared__ uint4 lds[KernLds<C>::TOTAL];
   const int tiles_n = (a.d + C::BN - 1) / C::BN;
   const int tiles_m = (a.T + C::BM - 1) / C::BM;
@@ -374,9 +385,10 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   Opnd ob{a.B[br], a.d, a.d, a.r};
   f32x16 acc[C::MB][C::NB];
   E* y = static_cast<E*>(a.y[br]);
+  E* y2 = EPI == UP_SWIGLU ? static_cast<E*>(a.y2[br]) : nullptr;
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   char LR_LDS* reg = stage_region<C>(lds);
-  // residual rows of 32-row block 0 are loaded during the last k step, those of
+  // residual (or gate) rows of 32-row block 0 are loaded during the last k step, those of
   // block mb+1 while block mb is computed, where a block's sweep is at most 8
   // iterations (the buffers fit the registers); otherwise each block's residual
   // rows are loaded, all at once, when it is due
@@ -409,8 +421,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
         const int rl = sw.rl(it), row = rb + rl;
         if (row >= a.T || !cok) continue;
         const float4 v = lds_f4(reg + rl * RowStage<C>::PITCH + sw.cl * 4);
-        const float4 r4 = R::f4(cur[it]);
-        store4(y + (int64_t)row * a.d + col, v.x + r4.x, v.y + r4.y, v.z + r4.z, v.w + r4.w);
+        const float4 o = up_out<EPI>(v, R::f4(cur[it]));
+        store4(y + (int64_t)row * a.d + col, o.x, o.y, o.z, o.w);
+        if (EPI == UP_SWIGLU && y2) store4(y2 + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
       }
     };
 #pragma unroll
@@ -436,7 +449,9 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
               const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
               if (row >= a.T || col >= a.d) return;
               const float4 v = lds_f4(rp + cl * 4);
-              store4(y + (int64_t)row * a.d + col, v.x + in[0].x, v.y + in[0].y, v.z + in[0].z, v.w + in[0].w);
+              const float4 o = up_out<EPI>(v, in[0]);
+              store4(y + (int64_t)row * a.d + col, o.x, o.y, o.z, o.w);
+              if (EPI == UP_SWIGLU && y2) store4(y2 + (int64_t)row * a.d + col, v.x, v.y, v.z, v.w);
             });
       } else {
         sweep_block<C, C::WTN>(reg, [&](int rl, int cl, const char LR_LDS* rp) {
@@ -528,7 +543,7 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, in
   };
   RowVals<C> rsv;
   auto pre = [&]() {   // the row values first: they are needed first
-    rsv.load([&](int i) { return m0 + i < a.T ? a.rstd[m0 + i] : 0.f; });
+    rsv.load([&](int i) { return m0 + i < a.T ? (a.rstd ? a.rstd[m0 + i] : 1.0f) : 0.f; });
     load_block(0, g0, u0);
   };
 
@@ -600,7 +615,7 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, uint4* lds, int bid, in
         }
       }
       srow = row_sum<SW::LPR>(srow);
-      if (row < a.T && row_sum_lane<SW::LPR>()) a.spart[(int64_t)row * a.spstride + part] = srow;
+      if (a.spart && row < a.T && row_sum_lane<SW::LPR>()) a.spart[(int64_t)row * a.spstride + part] = srow;
     }
   };
   if constexpr (PF) {
@@ -645,7 +660,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   using E = typename C::E;
   __shared__ uint4 lds[KernLds<C>::TOTAL];
   const int gr = a.g * a.r;
-  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.dn + C::BN - 1) / C::BN;
   const int tmA = (a.d + C::BM - 1) / C::BM, tnA = (gr + C::BN - 1) / C::BN;
   const int per_split = a.n_up * tmB * tnB + tmA * tnA;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -673,7 +688,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   const int job = w < a.n_up * tmB * tnB ? w / (tmB * tnB) : a.n_up;
   w = job < a.n_up ? w % (tmB * tnB) : w - a.n_up * tmB * tnB;
   const bool isA = job == a.n_up;
-  const int M = isA ? a.d : a.r, N = isA ? gr : a.d;
+  const int M = isA ? a.d : a.r, N = isA ? gr : a.dn;
   const int tiles_m = isA ? tmA : tmB, tiles_n = isA ? tnA : tnB;
   int tm, tn;
   grouped_tile<kGroupM>(w, tiles_m, tiles_n, tm, tn);
@@ -687,7 +702,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
     ob = Opnd{a.dh, gr, gr, a.T};    // dh': (n = c, k = t) at dh[t*gr + c]
   } else {
     oa = Opnd{static_cast<const E*>(a.z) + (int64_t)job * a.r, a.ldz, a.r, a.T};
-    ob = Opnd{a.dy[job], a.d, a.d, a.T};
+    ob = Opnd{a.dy[job], a.dn, a.dn, a.T};
   }
   f32x16 acc[C::MB][C::NB];
   mainloop<C, true, true, false>(oa, ob, MapId{}, MapId{}, m0, n0, kbeg, klen > 0 ? klen : 0, lds, nullptr, acc);
@@ -700,11 +715,13 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
     out = a.wpart + ((int64_t)split * a.split_tiles + tile) * (C::BM * C::BN);
     ldo = C::BN; r0 = m0; c0 = n0;
   } else if (a.nsplit > 1 && a.split_tiles == 0) {
-    out = a.wpart + (int64_t)split * a.part_stride + (isA ? a.part_offA : (int64_t)job * a.r * a.d);
+    out = a.wpart + (int64_t)split * a.part_stride + (isA ? a.part_offA : (int64_t)job * a.r * a.dn);
   } else {
     out = isA ? a.dA : a.dB[job];
   }
   const bool finalA = isA && (a.nsplit == 1 || a.split_tiles > 0);
+  // dA = diag(gamma) M and the dgamma partials (without gamma: dA = M)
+  const bool dgam = finalA && a.gamma != nullptr;
   const E* Aw = static_cast<const E*>(a.A);
   const E* gamma = static_cast<const E*>(a.gamma);
   const int wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
@@ -720,7 +737,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
         [&](int rl, int cl, float4* in) {
           const int row = rbase + rl, col = n0 + wn * C::WTN + cl;
           in[0] = in[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (finalA && row < M && col < N) {
+          if (dgam && row < M && col < N) {
             in[0] = load4(Aw + (int64_t)row * gr + col);
             in[1].x = to_f32(gamma[row]);
           }
@@ -730,11 +747,11 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
           float s = 0.f;
           if (row < M && col < N) {
             const float4 v = lds_f4(rp + cl * 4);
-            const float gj = finalA ? in[1].x : 1.0f;
-            if (finalA) s = in[0].x * v.x + in[0].y * v.y + in[0].z * v.z + in[0].w * v.w;
+            const float gj = dgam ? in[1].x : 1.0f;
+            if (dgam) s = in[0].x * v.x + in[0].y * v.y + in[0].z * v.z + in[0].w * v.w;
             store4(out + (int64_t)(row - r0) * ldo + (col - c0), gj * v.x, gj * v.y, gj * v.z, gj * v.w);
           }
-          if (finalA) {
+          if (dgam) {
             s = row_sum<LPR>(s);
             if (row < M && row_sum_lane<LPR>()) a.gpart[(int64_t)row * a.ngpart + tn * C::WN + wn] = s;
           }
@@ -747,7 +764,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
 // dgamma_j = sum_c A_jc M_jc (the row's partial sums added over the work-group
 // in a fixed order) and writes it, so no separate pass sums partials per row.
 __device__ __forceinline__ int64_t wred_blocks_b(const WgradArgs& a) {
-  return ((int64_t)a.n_up * a.r * a.d / 4 + 255) / 256;
+  return ((int64_t)a.n_up * a.r * a.dn / 4 + 255) / 256;
 }
 __device__ __forceinline__ float wred_block_sum(float s) {
   __shared__ float red[4];
@@ -763,17 +780,22 @@ template <typename E, class F>
 __device__ __forceinline__ void wred_row_a(const WgradArgs& a, int row, F&& sum4) {
   const int gr = a.g * a.r;
   const E* Aw = static_cast<const E*>(a.A);
-  const float gj = to_f32(static_cast<const E*>(a.gamma)[row]);
+  const bool dgam = a.gamma != nullptr;   // without gamma: dA = M, no dgamma
+  const float gj = dgam ? to_f32(static_cast<const E*>(a.gamma)[row]) : 1.0f;
   float s = 0.f;
   for (int c = threadIdx.x * 4; c < gr; c += 256 * 4) {
     const float4 acc = sum4(c);
-    const float4 a4 = load4(Aw + (int64_t)row * gr + c);
-    s += a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
+    if (dgam) {
+      const float4 a4 = load4(Aw + (int64_t)row * gr + c);
+      s += a4.x * acc.x + a4.y * acc.y + a4.z * acc.z + a4.w * acc.w;
+    }
     *reinterpret_cast<float4*>(a.dA + (int64_t)row * gr + c) =
         make_float4(gj * acc.x, gj * acc.y, gj * acc.z, gj * acc.w);
   }
-  s = wred_block_sum(s);
-  if (threadIdx.x == 0) a.dgamma[row] = s;
+  if (dgam) {
+    s = wred_block_sum(s);
+    if (threadIdx.x == 0) a.dgamma[row] = s;
+  }
 }
 
 // Sum the split partials in split order.  Partial element i: [0, nB) the dB
@@ -782,7 +804,7 @@ __device__ __forceinline__ void wred_row_a(const WgradArgs& a, int row, F&& sum4
 template <typename E>
 __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
   const int gr = a.g * a.r;
-  const int64_t nB = (int64_t)a.n_up * a.r * a.d;
+  const int64_t nB = (int64_t)a.n_up * a.r * a.dn;
   // the 4 outputs from element i, the split partials added in split order (up
   // to U loads in flight)
   auto sum4 = [&](int64_t i) {
@@ -806,8 +828,8 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
   if ((int64_t)blockIdx.x < nbb) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= nB) return;
-    const int job = (int)(i / ((int64_t)a.r * a.d));
-    const int64_t k = i % ((int64_t)a.r * a.d);
+    const int job = (int)(i / ((int64_t)a.r * a.dn));
+    const int64_t k = i % ((int64_t)a.r * a.dn);
     *reinterpret_cast<float4*>(a.dB[job] + k) = sum4(i);
     return;
   }
@@ -824,15 +846,15 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce_tiles(WgradArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (int64_t)a.split_tiles * TS) return;
   const int tile = (int)(i / TS), loc = (int)(i % TS);
-  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.dn + C::BN - 1) / C::BN;
   const int job = tile / (tmB * tnB);
   int tm, tn;
   grouped_tile<kGroupM>(tile % (tmB * tnB), tmB, tnB, tm, tn);
   const int row = tm * C::BM + loc / C::BN, col = tn * C::BN + loc % C::BN;
-  if (row >= a.r || col >= a.d) return;
+  if (row >= a.r || col >= a.dn) return;
   const float4 p0 = *reinterpret_cast<const float4*>(a.wpart + i);
   const float4 p1 = *reinterpret_cast<const float4*>(a.wpart + (int64_t)a.split_tiles * TS + i);
-  *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.d + col) =
+  *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.dn + col) =
       make_float4(p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w);
 }
 
@@ -865,14 +887,14 @@ struct SkTile {
 template <class C>
 __device__ __forceinline__ SkTile sk_tile(const WgradArgs& a, int t) {
   const int gr = a.g * a.r;
-  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+  const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.dn + C::BN - 1) / C::BN;
   const int tnA = (gr + C::BN - 1) / C::BN;
   SkTile s;
   const int nB = a.n_up * tmB * tnB;
   if (t < nB) {
     s.job = t / (tmB * tnB);
     const int w = t % (tmB * tnB);
-    s.tm = w / tnB; s.tn = w % tnB; s.M = a.r; s.N = a.d;
+    s.tm = w / tnB; s.tn = w % tnB; s.M = a.r; s.N = a.dn;
   } else {
     const int w = t - nB;
     s.job = a.n_up; s.tm = w / tnA; s.tn = w % tnA; s.M = a.d; s.N = gr;
@@ -908,7 +930,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
       ob = Opnd{a.dh, gr, gr, a.T};    // dh': (n = c, k = t) at dh[t*gr + c]
     } else {
       oa = Opnd{static_cast<const E*>(a.z) + (int64_t)st.job * a.r, a.ldz, a.r, a.T};
-      ob = Opnd{a.dy[st.job], a.d, a.d, a.T};
+      ob = Opnd{a.dy[st.job], a.dn, a.dn, a.T};
     }
     __syncthreads();   // the previous segment's epilogue is done with LDS
     f32x16 acc[C::MB][C::NB];
@@ -937,10 +959,10 @@ template <class C>
 __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
   using E = typename C::E;
   const int gr = a.g * a.r;
-  const int64_t nB = (int64_t)a.n_up * a.r * a.d;
+  const int64_t nB = (int64_t)a.n_up * a.r * a.dn;
   // the 4 outputs at (job, row, col): the slots of the covering work-groups
   auto sum4 = [&](int job, int row, int col) {
-    const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.d + C::BN - 1) / C::BN;
+    const int tmB = (a.r + C::BM - 1) / C::BM, tnB = (a.dn + C::BN - 1) / C::BN;
     const int tnA = (gr + C::BN - 1) / C::BN;
     const int tm = row / C::BM, tn = col / C::BN;
     const int t = sk_pos_of(job < a.n_up ? job * tmB * tnB + tm * tnB + tn : a.n_up * tmB * tnB + tm * tnA + tn,
@@ -960,10 +982,10 @@ __global__ __launch_bounds__(256) void k_wgrad_sk_reduce(WgradArgs a) {
   if ((int64_t)blockIdx.x < nbb) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= nB) return;
-    const int job = (int)(i / ((int64_t)a.r * a.d));
-    const int64_t k = i % ((int64_t)a.r * a.d);
-    const int row = (int)(k / a.d), col = (int)(k % a.d);
-    *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.d + col) = sum4(job, row, col);
+    const int job = (int)(i / ((int64_t)a.r * a.dn));
+    const int64_t k = i % ((int64_t)a.r * a.dn);
+    const int row = (int)(k / a.dn), col = (int)(k % a.dn);
+    *reinterpret_cast<float4*>(a.dB[job] + (int64_t)row * a.dn + col) = sum4(job, row, col);
     return;
   }
   const int row = (int)((int64_t)blockIdx.x - nbb);
@@ -1014,12 +1036,16 @@ struct SprimeRows {
 
 // ------------------------------------------------------------------ backward: dx
 // acc = dh' . A^T over K = g*r.  Row-sweep epilogue: dx = gamma*acc - x*rstd*S'/D
-// (+ dres with RES), with S' summed from the dz partials.  x (and dres) rows of
-// block mb+1 are loaded while block mb is computed; block 0, gamma and the row
-// statistic at the last k step.
-template <class C, bool RES>
+// (+ dres with DX_NORM_RES), with S' summed from the dz partials.  x (and dres)
+// rows of block mb+1 are loaded while block mb is computed; block 0, gamma and
+// the row statistic at the last k step.
+// DX_SWIGLU: acc is the gradient ds of s = SiLU(gate) * up; the epilogue reads
+// gate (in x's place) and up (in dres's) and writes dgate = ds * up * SiLU'(gate)
+// to dx and dup = ds * SiLU(gate) to dx2.
+template <class C, int MODE>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void k_dx(DxArgs a) {
   using E = typename C::E;
+  constexpr bool RES = MODE != DX_NORM;   // a second row input (dres, or up)
   using R = Raw4<E>;
   using SW = Sweep<C, C::WTN>;
   constexpr bool PF = C::NWAVES <= 4;  // prefetch of the next row block's x (see dz)
@@ -1038,6 +1064,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   const E* __restrict__ x = static_cast<const E*>(a.x);
   const E* dres = static_cast<const E*>(a.dres);
   E* dx = static_cast<E*>(a.dx);
+  E* dx2 = static_cast<E*>(a.dx2);
 
   // x rows, then (RES) the dres rows: buf[it] and buf[SW::IT + it]
   constexpr int NBUF = RES ? 2 * SW::IT : SW::IT;
@@ -1054,8 +1081,10 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
   typename R::T graw = R::zero();
   SprimeRows<C> srv;
   auto pre = [&]() {   // the row values first: they are needed first
-    srv.load(a, m0);
-    graw = cok ? R::load(static_cast<const E*>(a.gamma) + col) : R::zero();
+    if constexpr (MODE != DX_SWIGLU) {
+      srv.load(a, m0);
+      graw = cok ? R::load(static_cast<const E*>(a.gamma) + col) : R::zero();
+    }
     load_block(0, xin0);
   };
 
@@ -1068,7 +1097,7 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
     mainloop<C, false, false, false>(oa, ob, MapId{}, MapId{}, m0, n0, 0, gr, lds, nullptr, acc);
     pre();
   }
-  srv.publish(a, m0, srow);
+  if constexpr (MODE != DX_SWIGLU) srv.publish(a, m0, srow);
   __syncthreads();
 
   const float4 g4 = R::f4(graw);
@@ -1084,6 +1113,20 @@ __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::W
       if (row >= a.T || !cok) continue;
       const float4 v = lds_f4(reg + rl * RowStage<C>::PITCH + sw.cl * 4);
       const float4 x4 = R::f4(cur[it]);
+      if constexpr (MODE == DX_SWIGLU) {
+        const float4 u4 = R::f4(cur[SW::IT + it]);
+        const float ds[4] = {v.x, v.y, v.z, v.w}, gv[4] = {x4.x, x4.y, x4.z, x4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+        float dg[4], du[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = sigmoidf_(gv[e]);
+          dg[e] = ds[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+          du[e] = ds[e] * gv[e] * sg;
+        }
+        store4(dx + (int64_t)row * a.d + col, dg[0], dg[1], dg[2], dg[3]);
+        store4(dx2 + (int64_t)row * a.d + col, du[0], du[1], du[2], du[3]);
+        continue;
+      }
       const float sr = srow[row - m0];
       float4 o = make_float4(g4.x * v.x - x4.x * sr, g4.y * v.y - x4.y * sr, g4.z * v.z - x4.z * sr,
                              g4.w * v.w - x4.w * sr);
@@ -1261,10 +1304,12 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
 template <class C>
 hipError_t launch_up_cfg(const UpArgs& a, int n_up, hipStream_t s) {
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
-  if (a.res[0])
-    hipLaunchKernelGGL((k_up<C, true>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  if (a.res[0] && a.swiglu)
+    hipLaunchKernelGGL((k_up<C, UP_SWIGLU>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+  else if (a.res[0])
+    hipLaunchKernelGGL((k_up<C, UP_RES>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_up<C, false>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_up<C, UP_PLAIN>), dim3(tiles * n_up), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1386,12 +1431,12 @@ hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s) {
 }
 
 template <typename E>
-WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
+WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up, int dn) {
   using C = typename Cfgs<E>::Wgrad;
   const int gr = g * r;
   WgradPlan p{};
   p.S = 1;
-  p.tiles = n_up * cdiv(r, C::BM) * cdiv(d, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
+  p.tiles = n_up * cdiv(r, C::BM) * cdiv(dn, C::BN) + cdiv(d, C::BM) * cdiv(gr, C::BN);
   p.KS = cdiv(T, C::BK);
   const int64_t total = (int64_t)p.tiles * p.KS;
   p.nsplit = 1;
@@ -1425,7 +1470,7 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
   // splitting every tile and reducing all of dA and dB.
   {
     const int S = 2 * kNumCu - p.tiles, U = p.tiles - S;
-    const int tilesB = n_up * cdiv(r, C::BM) * cdiv(d, C::BN);
+    const int tilesB = n_up * cdiv(r, C::BM) * cdiv(dn, C::BN);
     if (Cfgs<E>::HAS_SKINNY && p.tiles > kNumCu && S > 0 && S <= tilesB && U % kNumXcd == 0 &&
         (2 * S) % kNumXcd == 0 && p.KS >= 32) {
       p.nsplit = 2;
@@ -1439,7 +1484,7 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up) {
   int sp = 1;
   while (p.tiles * sp < 2 * kNumCu && p.KS / (2 * sp) >= 16 && sp < 16) sp *= 2;
   p.nsplit = sp;
-  p.part_floats = sp > 1 ? (int64_t)sp * ((int64_t)n_up * r * d + (int64_t)d * gr) : 0;
+  p.part_floats = sp > 1 ? (int64_t)sp * ((int64_t)n_up * r * dn + (int64_t)d * gr) : 0;
   return p;
 }
 
@@ -1447,7 +1492,7 @@ template <typename E>
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   using C = typename Cfgs<E>::Wgrad;
   const int gr = a.g * a.r;
-  const int tilesB = cdiv(a.r, C::BM) * cdiv(a.d, C::BN);
+  const int tilesB = cdiv(a.r, C::BM) * cdiv(a.dn, C::BN);
   const int tilesA = cdiv(a.d, C::BM) * cdiv(gr, C::BN);
   const int total = a.split_tiles > 0 ? a.n_up * tilesB + tilesA + a.split_tiles
                                      : (a.n_up * tilesB + tilesA) * a.nsplit;
@@ -1464,7 +1509,7 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
 template <typename E>
 hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
   // dB work-groups (one thread per 4 outputs), then one work-group per dA row
-  const int64_t blocks = cdiv((int64_t)a.n_up * a.r * a.d / 4, 256) + a.d;
+  const int64_t blocks = cdiv((int64_t)a.n_up * a.r * a.dn / 4, 256) + a.d;
   if constexpr (Cfgs<E>::HAS_SKINNY) {
     if (a.streamk) {
       hipLaunchKernelGGL((k_wgrad_sk_reduce<typename Cfgs<E>::Wgrad>), dim3(blocks), dim3(256), 0, s, a);
@@ -1487,10 +1532,12 @@ hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
   using C = typename Cfgs<E>::Dx;
   if (a.T == 0) return hipSuccess;
   const int tiles = cdiv(a.T, C::BM) * cdiv(a.d, C::BN);
-  if (a.dres)
-    hipLaunchKernelGGL((k_dx<C, true>), dim3(tiles), dim3(C::THREADS), 0, s, a);
+  if (a.swiglu)
+    hipLaunchKernelGGL((k_dx<C, DX_SWIGLU>), dim3(tiles), dim3(C::THREADS), 0, s, a);
+  else if (a.dres)
+    hipLaunchKernelGGL((k_dx<C, DX_NORM_RES>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_dx<C, false>), dim3(tiles), dim3(C::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_dx<C, DX_NORM>), dim3(tiles), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1530,7 +1577,7 @@ template int dz_nparts<bf16>(int);
 template int dz_nparts<float>(int);
 template int wgrad_nparts<bf16>(int);
 template int wgrad_nparts<float>(int);
-template WgradPlan wgrad_plan<bf16>(int, int, int, int, int);
-template WgradPlan wgrad_plan<float>(int, int, int, int, int);
+template WgradPlan wgrad_plan<bf16>(int, int, int, int, int, int);
+template WgradPlan wgrad_plan<float>(int, int, int, int, int, int);
 
 }  // namespace lr

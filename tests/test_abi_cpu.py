@@ -162,3 +162,53 @@ def test_noalloc_rejects_on_the_host():
     assert lib.lr_block_fwd_noalloc(ctypes.byref(ok), None, FAKE, FAKE, arr, arr, None, None, None) == rb.LR_EINVAL
     assert lib.lr_block_fwd_noalloc(ctypes.byref(ok), FAKE, FAKE, FAKE, arr, arr, None, FAKE + 4, None) \
         == rb.LR_EINVAL
+
+
+def declared_signatures():
+    """{name: number of parameters} of every function the header declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(([^)]*)\)\s*;", src, flags=re.M):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argtypes_match_the_header():
+    """Every entry point's ctypes argument list has as many entries as the C
+    declaration has parameters (a short list would pass later arguments, the
+    stream among them, with ctypes' default int conversion)."""
+    lib = rb.load()
+    sig = declared_signatures()
+    assert sorted(sig) == sorted(rb.ENTRY_POINTS)
+    for name, n in sig.items():
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
+def test_mlp_host_checks():
+    lib = rb.load()
+    m = rb.make_mlp_dims(16384, 4096, 11008, 1024)
+    f, b = rb.lr_mlp_workspace_size(m, False), rb.lr_mlp_workspace_size(m, True)
+    # forward: folded A_in, h_in, h_out, gate and s; backward: gate, up, s and more
+    assert f >= 4096 * 2048 * 2 + 16384 * 3072 * 2 + 2 * 16384 * 11008 * 2
+    assert b >= 3 * 16384 * 11008 * 2
+    assert rb.lr_mlp_workspace_size(rb.make_mlp_dims(64, 128, 100, 64), False) == 0    # f % 64
+    ok = rb.make_mlp_dims(64, 128, 192, 64)
+    need = rb.lr_mlp_workspace_size(ok, False)
+    p = [FAKE] * 7
+    assert lib.lr_mlp_fwd(ctypes.byref(ok), *p, None, FAKE, None, None, None, FAKE, need - 1, None) \
+        == rb.LR_EWORKSPACE
+    assert lib.lr_mlp_fwd(ctypes.byref(ok), *p, None, None, None, None, None, FAKE, need, None) \
+        == rb.LR_EINVAL                                                                  # out missing
+    assert lib.lr_mlp_fwd(ctypes.byref(ok), *p, FAKE + 2, FAKE, None, None, None, FAKE, need, None) \
+        == rb.LR_EINVAL                                                                  # misaligned residual
+    bad = rb.make_mlp_dims(64, 128, 192, 96)
+    assert lib.lr_mlp_fwd(ctypes.byref(bad), *p, None, FAKE, None, None, None, FAKE, 1 << 40, None) \
+        == rb.LR_EUNSUPPORTED
+    need_b = rb.lr_mlp_workspace_size(ok, True)
+    g = [FAKE] * 7
+    assert lib.lr_mlp_bwd(ctypes.byref(ok), *p, FAKE, FAKE, None, FAKE, None, *g, FAKE, need_b - 1, None) \
+        == rb.LR_EWORKSPACE
+    assert lib.lr_mlp_bwd(ctypes.byref(ok), *p, None, FAKE, None, FAKE, None, *g, FAKE, need_b, None) \
+        == rb.LR_EINVAL                                                                  # h_in_saved missing

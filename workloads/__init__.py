@@ -171,3 +171,83 @@ def make_inputs(wl: Workload, seed: int = 0, with_dy: bool = True, rows: Optiona
     dt = wl.dtype
     return Inputs(wl, seed, Tensor(x, dt), Tensor(gamma, dt), Tensor(A, dt),
                   [Tensor(b, dt) for b in B], None if dy is None else [Tensor(t, dt) for t in dy])
+
+
+# ----------------------------------------------------------------------------- per-projection MLP
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    """The per-projection low-rank SwiGLU MLP: model width d, MLP width f, every
+    factorised linear of rank r."""
+    name: str
+    T: int
+    d: int
+    f: int
+    r: int
+    dtype: str
+    eps: float = 1e-6
+    residual: bool = False   # out = x + mlp(x): residual = x, and dx gains dout
+    note: str = ""
+
+    def fwd_flops(self) -> float:
+        """GEMMs of a forward: x . A_in, the two up factors to f, s . A_o, h_out . B_o."""
+        return 2.0 * self.T * self.r * (3 * self.d + 3 * self.f)
+
+    def bwd_flops(self) -> float:
+        """GEMMs of a backward, without the recomputation of gate and up (two
+        more up factors, 4 T r f)."""
+        return 2.0 * self.T * self.r * (6 * self.d + 6 * self.f)
+
+    def recompute_flops(self) -> float:
+        return 4.0 * self.T * self.r * self.f
+
+    def replace(self, **kw) -> "MlpWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+MLP_WORKLOADS: Dict[str, MlpWorkload] = {
+    "lowrank_mlp": MlpWorkload("lowrank_mlp", T=16384, d=4096, f=11008, r=1024, dtype="bf16", residual=True,
+                               note="LLaMA-2-7B-width MLP sublayer out = x + mlp(x), each of gate, up and down "
+                                    "a rank-1024 factor pair, SwiGLU at width 11008"),
+}
+
+
+@dataclasses.dataclass
+class MlpInputs:
+    wl: MlpWorkload
+    seed: int
+    x: Tensor
+    gamma: Tensor
+    A_in: Tensor
+    B_g: Tensor
+    B_u: Tensor
+    A_o: Tensor
+    B_o: Tensor
+    dout: Optional[Tensor]
+
+
+def make_mlp_inputs(wl: MlpWorkload, seed: int = 0, with_dout: bool = True, rows: Optional[int] = None) -> MlpInputs:
+    """Draw one MLP workload's inputs (fixed order, one PCG64 stream per seed):
+        x     ~ N(0, 1)          [T, d]
+        gamma = 1 + N(0, 0.1)    [d]
+        A_in  ~ N(0, 1/d)        [d, 2r]   ([A_g | A_u])
+        B_g   ~ N(0, 1/r)        [r, f]
+        B_u   ~ N(0, 1/r)        [r, f]
+        A_o   ~ N(0, 1/f)        [f, r]
+        B_o   ~ N(0, 1/r)        [r, d]
+        dout  ~ N(0, 1)          [T, d]
+    rounded to the storage dtype as for the block.  ``rows`` keeps the first
+    rows of x and dout after drawing the full arrays."""
+    rng = np.random.default_rng(seed)
+    T, d, f, r = wl.T, wl.d, wl.f, wl.r
+    keep = T if rows is None else min(rows, T)
+    x = rng.standard_normal((T, d))[:keep]
+    gamma = 1.0 + rng.standard_normal(d) * math.sqrt(0.1)
+    A_in = rng.standard_normal((d, 2 * r)) / math.sqrt(d)
+    B_g = rng.standard_normal((r, f)) / math.sqrt(r)
+    B_u = rng.standard_normal((r, f)) / math.sqrt(r)
+    A_o = rng.standard_normal((f, r)) / math.sqrt(f)
+    B_o = rng.standard_normal((r, d)) / math.sqrt(r)
+    dout = rng.standard_normal((T, d))[:keep] if with_dout else None
+    dt = wl.dtype
+    return MlpInputs(wl, seed, Tensor(x, dt), Tensor(gamma, dt), Tensor(A_in, dt), Tensor(B_g, dt), Tensor(B_u, dt),
+                     Tensor(A_o, dt), Tensor(B_o, dt), None if dout is None else Tensor(dout, dt))
