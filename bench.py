@@ -3,7 +3,8 @@
 
 One step = one forward (with the rank-r checkpoint) + one backward of the block
 over one batch of synthetic, seeded input already resident in HBM, through the
-C ABI (the shard workload "btp_shard" times its two seam calls instead).  Prints
+C ABI (the shard workload "btp_shard" times its two seam calls instead; the
+workload "lowrank_mlp" times the per-projection low-rank SwiGLU MLP).  Prints
 ONE JSON line: block fwd+bwd TFLOP/s (algorithmic GEMM FLOPs, elementwise work
 not counted), tokens/s, % of the bf16 MFMA peak, the roofline of the dominant
 kernel (timed with HIP events on its launch stream over the timed region) and
@@ -26,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "low-rank block fwd+bwd TFLOP/s (bf16) and % MFMA peak; tokens/s per block"
 METRIC_FWD = "low-rank block forward HBM GB/s (small-rank, memory-bound sweep)"
+METRIC_MLP = "per-projection low-rank SwiGLU MLP fwd+bwd TFLOP/s (bf16) and % MFMA peak; tokens/s"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (published)
 PEAK_GBS = 8000.0                                # MI355X HBM3E (published)
 WARM_S = 0.5     # default untimed warm-up, seconds of steps
@@ -110,6 +112,40 @@ def kernel_work(wl, name: str):
     return 0.0, 0.0
 
 
+def mlp_kernel_work(wl, name: str):
+    """Algorithmic (flops, HBM bytes) of all launches of kernel `name` in one
+    step of the per-projection MLP (forward, then a backward that recomputes
+    gate, up and s): each launch's operands read once and results written once;
+    GEMM flops as executed, the recomputation included."""
+    T, d, f, r = wl.T, wl.d, wl.f, wl.r
+    e = 2 if wl.dtype == "bf16" else 4
+    res = 1 if wl.residual else 0
+    if name == "up":   # gate, up (+s), out; then gate and up (+s) again in the backward
+        fl = 2.0 * T * r * (4 * f + d)
+        gate = e * (T * r + r * f + T * f)
+        upf = e * (T * r + r * f + 2 * T * f)
+        return fl, gate + upf + e * (T * r + r * d + (1 + res) * T * d) + gate + upf + e * T * f
+    if name == "down":   # x . A_in (normalised), s . A_o (plain)
+        return 2.0 * T * r * (2 * d + f), e * (T * d + 2 * d * r + 2 * T * r + T * f + f * r + T * r) + 4 * T
+    if name == "dz":     # dout . B_o^T; (dgate, dup) . (B_g, B_u)^T with the S' partials
+        return (2.0 * T * r * (d + 2 * f),
+                e * (T * d + r * d + 2 * T * r + 2 * T * f + 2 * r * f + 2 * T * 2 * r) + 4 * T)
+    if name == "wgrad":  # dB_o, dA_o; dB_g, dB_u, dA_in
+        return (2.0 * T * r * (d + f) + 2.0 * T * r * (2 * f + 2 * d),
+                e * (T * r + T * d + T * f + T * r) + 4 * (r * d + f * r)
+                + e * (2 * T * r + 2 * T * f + T * d + 2 * T * r + 2 * d * r) + 4 * (2 * r * f + 2 * d * r))
+    if name == "dx":     # ds with the SwiGLU backward (gate, up in; dgate, dup out); dx with RMSNorm
+        return (2.0 * T * r * (f + 2 * d),
+                e * (T * r + f * r + 4 * T * f) + e * (2 * T * r + 2 * d * r + (2 + res) * T * d) + 4 * T)
+    if name == "fold_gamma":
+        return 0.0, e * (2 * d * 2 * r + d)
+    if name == "wgrad_reduce":
+        return 0.0, 4 * (r * d + f * r)
+    if name == "sum_parts":
+        return 0.0, 4 * d * 17
+    return 0.0, 0.0
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -146,10 +182,18 @@ def cpu_baseline(wl, inp, budget_s: float = 24.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    fwd_step = wl.seam or wl.fwd_only
+    is_mlp = hasattr(wl, "f")
+    fwd_step = not is_mlp and (wl.seam or wl.fwd_only)
 
     def oracle_pass(rows, with_bwd):
         x = inp.x.v[:rows]
+        if is_mlp:
+            w = [t.v for t in (inp.gamma, inp.A_in, inp.B_g, inp.B_u, inp.A_o, inp.B_o)]
+            oracle.mlp_fwd(x, *w, wl.r, wl.eps, residual=x if wl.residual else None)
+            if with_bwd:
+                dout = inp.dout.v[:rows]
+                oracle.mlp_bwd(x, *w, dout, wl.r, wl.eps, dx_residual=dout if wl.residual else None)
+            return
         args = (x, inp.gamma.v, inp.A.v, [b.v for b in inp.B])
         if wl.seam:
             p, ss = oracle.down_partial(*args[:3])
@@ -192,7 +236,8 @@ def cpu_baseline(wl, inp, budget_s: float = 24.0):
         flops = sub.fwd_flops() + (sub.bwd_flops() if with_bwd else 0.0)
         key = f"{prec}_{'fwd_bwd' if with_bwd else 'fwd'}"
         out[key] = {"tflops": flops / t / 1e12, "tokens_per_s": rows / t, "s_per_pass": t, "rows": rows,
-                    "passes": passes, "fwd_gbs": sub.fwd_bytes() / t / 1e9 if not with_bwd else None}
+                    "passes": passes,
+                    "fwd_gbs": sub.fwd_bytes() / t / 1e9 if not (with_bwd or is_mlp) else None}
         log(f"cpu oracle {key}: {rows} rows, {passes} pass(es), {t:.3f} s per pass")
     main = out["f64_fwd" if fwd_step else "f64_fwd_bwd"]
     rows = main["rows"]
@@ -204,7 +249,7 @@ def cpu_baseline(wl, inp, budget_s: float = 24.0):
     res = {"unit": "TFLOP/s", "value": main["tflops"], "cores": int(threads), "kind": "oracle", "sample": sample,
            "tokens_per_s": main["tokens_per_s"], "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
            "legs": out}
-    if wl.fwd_only and wl.hbm_metric:
+    if not is_mlp and wl.fwd_only and wl.hbm_metric:
         res["unit"], res["value"] = "GB/s", main["fwd_gbs"]
     return res
 
@@ -230,17 +275,19 @@ def main():
 
     import torch
     import rank_bottleneck_amd as rb
-    from workloads import WORKLOADS, make_inputs
-
-    wl = WORKLOADS[args.workload]
-    log("workload", wl)
-    torch.cuda.set_device(0)
-    inp = make_inputs(wl, seed=0, with_dy=not (wl.seam or wl.fwd_only))
+    from workloads import MLP_WORKLOADS, WORKLOADS, make_inputs, make_mlp_inputs
 
     def dev(t):
         if t.dtype == "bf16":
             return torch.from_numpy(t.store.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(t.store).cuda()
+
+    torch.cuda.set_device(0)
+    if args.workload in MLP_WORKLOADS:
+        return main_mlp(args, MLP_WORKLOADS[args.workload], rb, torch, dev, make_mlp_inputs)
+    wl = WORKLOADS[args.workload]
+    log("workload", wl)
+    inp = make_inputs(wl, seed=0, with_dy=not (wl.seam or wl.fwd_only))
 
     x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
     B = [dev(b) for b in inp.B]
@@ -283,6 +330,97 @@ def main():
                 rb.lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
         flops = wl.fwd_flops() + wl.bwd_flops()
 
+    ms_step, per_kernel, dominant, dom_ms = measure(args, step, rb, torch)
+    roof = roofline(wl, dominant, dom_ms, kernel_work(wl, dominant), wl.dtype)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    metric, value, unit = METRIC, tflops, "TFLOP/s"
+    if wl.fwd_only and wl.hbm_metric:
+        metric, value, unit = METRIC_FWD, wl.fwd_bytes() / (ms_step * 1e-3) / 1e9, "GB/s"
+    elif wl.fwd_only:
+        metric = "low-rank block forward TFLOP/s (bf16)"
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+           "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "r": wl.r, "g": wl.g, "act": wl.act,
+                      "d_norm": wl.D, "residual": wl.residual,
+                      "step": "seam fwd" if wl.seam else ("fwd" if wl.fwd_only else "fwd+bwd"),
+                      "parallelism": "none (1 GPU)"},
+           "tflops": tflops,
+           "tokens_per_s": wl.T / (ms_step * 1e-3),
+           "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wl.dtype],
+           "kernel_ms_warmup_step": per_kernel,
+           "checkpoint": None if (wl.seam or wl.fwd_only) else checkpoint_bytes(wl),
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def main_mlp(args, wl, rb, torch, dev, make_mlp_inputs):
+    """The per-projection low-rank SwiGLU MLP: one step = lr_mlp_fwd (keeping
+    h_in, h_out and rstd) + lr_mlp_bwd, as the sublayer out = x + mlp(x) when
+    the workload has the residual."""
+    log("workload", wl)
+    inp = make_mlp_inputs(wl, seed=0)
+    x = dev(inp.x)
+    w = [dev(t) for t in (inp.gamma, inp.A_in, inp.B_g, inp.B_u, inp.A_o, inp.B_o)]
+    dout = dev(inp.dout)
+    if args.no_cpu_baseline:
+        del inp
+    dims = rb.make_mlp_dims(wl.T, wl.d, wl.f, wl.r, wl.dtype, wl.eps)
+    dt = rb.TORCH_DTYPE[dims.dtype]
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out_t = torch.empty((wl.T, wl.d), dtype=dt, device="cuda")
+    h_in = torch.empty((wl.T, 2 * wl.r), dtype=dt, device="cuda")
+    h_out = torch.empty((wl.T, wl.r), dtype=dt, device="cuda")
+    rstd = torch.empty(wl.T, **f32)
+    dx = torch.empty((wl.T, wl.d), dtype=dt, device="cuda")
+    grads = [torch.empty(wl.d, **f32), torch.empty((wl.d, 2 * wl.r), **f32), torch.empty((wl.r, wl.f), **f32),
+             torch.empty((wl.r, wl.f), **f32), torch.empty((wl.f, wl.r), **f32), torch.empty((wl.r, wl.d), **f32)]
+    wsf, wsb = rb.mlp_workspace(dims, False), rb.mlp_workspace(dims, True)
+    res = x if wl.residual else None
+    dres = dout if wl.residual else None
+
+    def step():
+        rb.lr_mlp_fwd(dims, x, *w, res, out_t, h_in, h_out, rstd, wsf)
+        rb.lr_mlp_bwd(dims, x, *w, h_in, h_out, rstd, dout, dres, dx, *grads, wsb)
+
+    ms_step, per_kernel, dominant, dom_ms = measure(args, step, rb, torch)
+    roof = roofline(wl, dominant, dom_ms, mlp_kernel_work(wl, dominant), wl.dtype)
+    flops = wl.fwd_flops() + wl.bwd_flops()
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    e = 2 if wl.dtype == "bf16" else 4
+    out = {"metric": METRIC_MLP, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+           "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "f": wl.f, "r": wl.r, "residual": wl.residual,
+                      "step": "fwd+bwd", "parallelism": "none (1 GPU)"},
+           "tflops": tflops,
+           "tflops_with_recompute": (flops + wl.recompute_flops()) / (ms_step * 1e-3) / 1e12,
+           "tokens_per_s": wl.T / (ms_step * 1e-3),
+           "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wl.dtype],
+           "kernel_ms_warmup_step": per_kernel,
+           "checkpoint": {"kept_bytes": e * wl.T * 3 * wl.r + 4 * wl.T,
+                          "wide_bytes": e * wl.T * 3 * wl.f,
+                          "ratio": (e * wl.T * 3 * wl.f) / (e * wl.T * 3 * wl.r + 4 * wl.T)},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def measure(args, step, rb, torch):
+    """Warm-up, a traced warm-up step (per-kernel times, the dominant kernel),
+    then the timed region.  Returns (ms per step, per-kernel ms of the traced
+    step, the dominant kernel's name, its ms per timed step for the traced
+    steps)."""
     if args.copy_calibration:
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -316,23 +454,25 @@ def main():
     args.warmup = done + max(args.warmup - done - 1, 0) + 1
     rb.lr_trace_begin(None, 64)
     step()
-    per_kernel = {}
+    per_kernel, per_count = {}, {}
     for i in range(rb.lr_trace_count()):
         name, ms = rb.lr_trace_elapsed(i)
         per_kernel[name] = per_kernel.get(name, 0.0) + ms
+        per_count[name] = per_count.get(name, 0) + 1
     rb.lr_trace_end()
     torch.cuda.synchronize()
     dominant = max(per_kernel, key=per_kernel.get)
     log("warm-up kernel ms:", {k: round(v, 4) for k, v in per_kernel.items()}, "dominant:", dominant)
 
-    # timed region: K steps; the dominant kernel's first TRACED launches are
-    # bracketed by HIP events on its stream.  Each event pair leaves the GPU idle
-    # for a few microseconds, so bracketing every launch would inflate the step
-    # time that the headline value comes from.
+    # timed region: K steps; the dominant kernel's launches of the first TRACED
+    # steps are bracketed by HIP events on its stream.  Each event pair leaves
+    # the GPU idle for a few microseconds, so bracketing every launch would
+    # inflate the step time that the headline value comes from.
     traced = max(1, min(args.steps, 5))
+    per_step = per_count[dominant]
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    rb.lr_trace_begin(dominant, traced)
+    rb.lr_trace_begin(dominant, traced * per_step)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
@@ -345,19 +485,26 @@ def main():
     rb.lr_trace_end()
     ms_step = t0.elapsed_time(t1) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)")
+    # the dominant kernel's time per step (the sum of its launches in a step)
+    dom_step = float(np.sum(dom_ms)) / (len(dom_ms) / per_step) if dom_ms else float("nan")
+    return ms_step, per_kernel, dominant, (dom_step, per_step)
 
-    tflops = flops / (ms_step * 1e-3) / 1e12
-    dom_avg = float(np.mean(dom_ms)) if dom_ms else float("nan")
-    kf, kb = kernel_work(wl, dominant)
-    ridge = PEAK_TFLOPS[wl.dtype] * 1e12 / (PEAK_GBS * 1e9)
+
+def roofline(wl, dominant, dom, work, dtype):
+    """Roofline of the dominant kernel: its algorithmic flops (or bytes) per step
+    over its time per step (for a kernel launched once per step, per launch)."""
+    dom_avg, per_step = dom
+    kf, kb = work
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_GBS * 1e9)
     if kf > 0 and kf / max(kb, 1) > ridge:
-        roof = {"bound": "mfma", "achieved": kf / (dom_avg * 1e-3) / 1e12, "peak": PEAK_TFLOPS[wl.dtype],
+        roof = {"bound": "mfma", "achieved": kf / (dom_avg * 1e-3) / 1e12, "peak": PEAK_TFLOPS[dtype],
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": kb / (dom_avg * 1e-3) / 1e9, "peak": PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dominant
     roof["kernel_ms"] = dom_avg
+    roof["launches_per_step"] = per_step
     roof["algorithmic_flops"] = kf
     roof["algorithmic_bytes"] = kb
     roof["traffic"] = None
@@ -366,31 +513,7 @@ def main():
         rec = json.load(open(tpath)).get(f"{wl.name}/{dominant}")
         if rec and rec.get("source_hash") == source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
-
-    metric, value, unit = METRIC, tflops, "TFLOP/s"
-    if wl.fwd_only and wl.hbm_metric:
-        metric, value, unit = METRIC_FWD, wl.fwd_bytes() / (ms_step * 1e-3) / 1e9, "GB/s"
-    elif wl.fwd_only:
-        metric = "low-rank block forward TFLOP/s (bf16)"
-    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-           "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "r": wl.r, "g": wl.g, "act": wl.act,
-                      "d_norm": wl.D, "residual": wl.residual,
-                      "step": "seam fwd" if wl.seam else ("fwd" if wl.fwd_only else "fwd+bwd"),
-                      "parallelism": "none (1 GPU)"},
-           "tflops": tflops,
-           "tokens_per_s": wl.T / (ms_step * 1e-3),
-           "pct_mfma_peak": 100.0 * tflops / PEAK_TFLOPS[wl.dtype],
-           "kernel_ms_warmup_step": per_kernel,
-           "checkpoint": None if (wl.seam or wl.fwd_only) else checkpoint_bytes(wl),
-           "roofline": roof}
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a row sample")
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    return roof
 
 
 if __name__ == "__main__":
