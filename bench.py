@@ -58,19 +58,22 @@ def one_kernel_forward(wl) -> bool:
     return (wl.r == 64 and wl.g <= 4) or (wl.r == 128 and wl.g <= 2) or (wl.r == 256 and wl.g == 1)
 
 
-def wgrad_split_tiles(wl) -> int:
+def split_tiles(T, d, r, g, n_up, dn, dtype="bf16") -> int:
     """Tiles the library's weight-gradient plan splits over two token halves
     when the 256 x 256 tiles fill between one and two rounds of the 256 CUs (the
-    rest run whole); 0 when that plan does not apply."""
-    if wl.dtype != "bf16":
+    rest run whole); 0 when that plan does not apply.  dn: the dB width."""
+    if dtype != "bf16":
         return 0
     cd = lambda a, b: -(-a // b)
-    gr = wl.g * wl.r
-    tiles_b = wl.n_up * cd(wl.r, 256) * cd(wl.d, 256)
-    tiles = tiles_b + cd(wl.d, 256) * cd(gr, 256)
+    tiles_b = n_up * cd(r, 256) * cd(dn, 256)
+    tiles = tiles_b + cd(d, 256) * cd(g * r, 256)
     S = 512 - tiles
-    ok = tiles > 256 and 0 < S <= tiles_b and (tiles - S) % 8 == 0 and (2 * S) % 8 == 0 and cd(wl.T, 64) >= 32
+    ok = tiles > 256 and 0 < S <= tiles_b and (tiles - S) % 8 == 0 and (2 * S) % 8 == 0 and cd(T, 64) >= 32
     return S if ok else 0
+
+
+def wgrad_split_tiles(wl) -> int:
+    return split_tiles(wl.T, wl.d, wl.r, wl.g, wl.n_up, wl.d, wl.dtype)
 
 
 def kernel_work(wl, name: str):
@@ -96,8 +99,8 @@ def kernel_work(wl, name: str):
                 e * (T * (zcols or gr) + nu * T * d + T * d + T * gr + d * gr) + 4 * (d * gr + nu * r * d))
     if name == "wgrad_reduce":   # the split-K sum: only its fp32 results count
         split = wgrad_split_tiles(wl)
-        if split:   # only the split (dB) tiles are summed
-            return 0.0, 4 * split * 256 * 256
+        if split:   # only the split (dB) tiles are summed; dgamma from the dA tiles' row partials
+            return 0.0, 4 * split * 256 * 256 + 4 * d * (-(-gr // 256) * 2 + 1)
         return 0.0, 4 * (d * gr + nu * r * d)
     if name == "sum_parts":   # dgamma from the whole dA tiles' row partials
         return 0.0, 4 * d * (-(-gr // 256) * 2 + 1)
@@ -139,10 +142,12 @@ def mlp_kernel_work(wl, name: str):
                 e * (T * r + f * r + 4 * T * f) + e * (2 * T * r + 2 * d * r + (2 + res) * T * d) + 4 * T)
     if name == "fold_gamma":
         return 0.0, e * (2 * d * 2 * r + d)
-    if name == "wgrad_reduce":
-        return 0.0, 4 * (r * d + f * r)
-    if name == "sum_parts":
-        return 0.0, 4 * d * 17
+    if name == "wgrad_reduce":   # output layer's sums (no split tiles there), input layer's split tiles and dgamma
+        s_out = split_tiles(T, f, r, 1, 1, d, wl.dtype)
+        s_in = split_tiles(T, d, r, 2, 2, f, wl.dtype)
+        out_b = 4 * s_out * 256 * 256 if s_out else 4 * (r * d + f * r)
+        in_b = 4 * s_in * 256 * 256 + 4 * d * (-(-2 * r // 256) * 2 + 1) if s_in else 4 * (2 * r * f + d * 2 * r)
+        return 0.0, out_b + in_b
     return 0.0, 0.0
 
 

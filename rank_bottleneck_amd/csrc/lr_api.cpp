@@ -201,7 +201,9 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   // the split-tile plan reduces only dB tiles; dA's tiles run whole and leave
   // dgamma partials, as an unsplit pass does
   const bool reduced = wp.streamk || ns > 1;
-  const bool gamma_parts = !reduced || wp.split_tiles > 0;
+  // dgamma from the whole dA tiles' row partials: its own launch after an
+  // unsplit pass, inside the reduction with split tiles
+  const bool gamma_parts = !reduced;
   const int64_t pstride = (int64_t)n_up * r * D + (int64_t)D * gr;
   float* wpart = cv.take<float>((size_t)wp.part_floats * 4);
 
@@ -228,13 +230,14 @@ lr_status bwd_impl(const lr_dims* d, const void* x, const void* gamma, const voi
   wa.nsplit = ns; wa.wpart = wpart; wa.part_stride = pstride; wa.part_offA = (int64_t)n_up * r * D;
   wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
   wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles; wa.split_tiles = wp.split_tiles;
+  wa.gparts_used = lr::wgrad_nparts_used<E>(gr, false);
   {
     const int BK = lr::gemm_bk<E>();   // split lengths are whole k steps
     const int ksteps = (T + BK - 1) / BK;
     wa.ksplit = ((ksteps + ns - 1) / ns) * BK;
   }
   LR_LAUNCH("wgrad", s, lr::launch_wgrad<E>(wa, s));
-  if (reduced)  // the reduction (all splits and stream-K: it also forms dgamma)
+  if (reduced)  // the reduction (it also forms dgamma)
     LR_LAUNCH("wgrad_reduce", s, lr::launch_wgrad_reduce<E>(wa, s));
   if (gamma_parts)  // dA's tiles ran whole: they left per-tile dgamma partials
     LR_LAUNCH("sum_parts", s, lr::launch_sum_parts(gpart, dgamma, D, lr::wgrad_nparts_used<E>(gr, false), ngp, s));
@@ -423,12 +426,13 @@ template <typename E>
 lr_status mlp_wgrad(lr::WgradArgs wa, const lr::WgradPlan& wp, int gr, float* gpart, int ngp, hipStream_t s) {
   const int ns = wp.nsplit;
   const bool reduced = wp.streamk || ns > 1;
-  const bool gamma_parts = wa.gamma && (!reduced || wp.split_tiles > 0);
+  const bool gamma_parts = wa.gamma && !reduced;
   wa.nsplit = ns;
   wa.part_stride = (int64_t)wa.n_up * wa.r * wa.dn + (int64_t)wa.d * gr;
   wa.part_offA = (int64_t)wa.n_up * wa.r * wa.dn;
   wa.streamk = wp.streamk; wa.sk_G = wp.G; wa.sk_Q = wp.Q; wa.sk_R = wp.R; wa.sk_KS = wp.KS;
   wa.sk_maxseg = wp.maxseg; wa.sk_S = wp.S; wa.sk_tiles = wp.tiles; wa.split_tiles = wp.split_tiles;
+  wa.gparts_used = lr::wgrad_nparts_used<E>(gr, false);
   {
     const int BK = lr::gemm_bk<E>();
     const int ksteps = (wa.T + BK - 1) / BK;

@@ -94,6 +94,7 @@ struct WgradArgs {
   float* dgamma;      // [d]: written by the reductions (launch_wgrad_reduce)
   float* gpart;       // [d, ngpart]: dgamma partials of an unsplit launch_wgrad
   int ngpart;
+  int gparts_used;    // split-tile plan with gamma: partials per row that k_wgrad_reduce_tiles sums into dgamma
   int T, d, r, g, n_up;     // d: width of x (rows of dA)
   int dn;                   // width of dy_i (columns of dB_i)
   int nsplit, ksplit;       // token splits and tokens per split (a multiple of the k step)
@@ -175,7 +176,8 @@ hipError_t launch_fold_fused(const void* A, const void* gamma, const void* const
 template <typename E> hipError_t launch_dz(const DzArgs& a, int n_up, hipStream_t s);
 template <typename E> hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 // sums the split partials (or stream-K slots) of launch_wgrad into dB and dA and
-// forms dgamma (nothing to do when nsplit == 1 without stream-K)
+// forms dgamma (nothing to do when nsplit == 1 without stream-K); with split
+// tiles it forms dgamma from gpart's first gparts_used partials of each row
 template <typename E> hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s);
 template <typename E> hipError_t launch_dx(const DxArgs& a, hipStream_t s);
 hipError_t launch_sum_parts(const float* parts, float* out, int n, int nparts, int stride, hipStream_t s);

@@ -839,10 +839,23 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(WgradArgs a) {
 
 // Sum of the two halves of each split tile (k_wgrad with split_tiles > 0): one
 // thread per 4 consecutive slot values, the halves added in order, written to
-// the tile's place in dB (split tiles are dB tiles).
+// the tile's place in dB (split tiles are dB tiles).  With gamma, the work-groups
+// past the tiles' also form dgamma_j from the row partials the whole dA tiles
+// left (one thread per row, the partials added in column order), so that no
+// separate launch sums them.
 template <class C>
 __global__ __launch_bounds__(256) void k_wgrad_reduce_tiles(WgradArgs a) {
   constexpr int TS = C::BM * C::BN;
+  const int64_t ntb = ((int64_t)a.split_tiles * TS / 4 + 255) / 256;
+  if ((int64_t)blockIdx.x >= ntb) {
+    const int j = (int)(((int64_t)blockIdx.x - ntb) * 256 + threadIdx.x);
+    if (j >= a.d) return;
+    const float* p = a.gpart + (int64_t)j * a.ngpart;
+    float s = 0.f;
+    for (int k = 0; k < a.gparts_used; ++k) s += p[k];
+    a.dgamma[j] = s;
+    return;
+  }
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (int64_t)a.split_tiles * TS) return;
   const int tile = (int)(i / TS), loc = (int)(i % TS);
@@ -1520,7 +1533,8 @@ hipError_t launch_wgrad_reduce(const WgradArgs& a, hipStream_t s) {
   if (a.split_tiles > 0) {
     using C = typename Cfgs<E>::Wgrad;
     const int64_t n4 = (int64_t)a.split_tiles * C::BM * C::BN / 4;
-    hipLaunchKernelGGL((k_wgrad_reduce_tiles<C>), dim3(cdiv(n4, 256)), dim3(256), 0, s, a);
+    const int64_t gblocks = a.gamma ? cdiv(a.d, 256) : 0;   // dgamma rows (see the kernel)
+    hipLaunchKernelGGL((k_wgrad_reduce_tiles<C>), dim3(cdiv(n4, 256) + gblocks), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_wgrad_reduce<E>, dim3(blocks), dim3(256), 0, s, a);
