@@ -517,7 +517,8 @@ def roofline(wl, dominant, dom, work, dtype):
     if os.path.exists(tpath):
         rec = json.load(open(tpath)).get(f"{wl.name}/{dominant}")
         if rec and rec.get("source_hash") == source_hash():
-            roof["traffic"] = rec["bytes_per_launch"]
+            # per step like `achieved` (per launch for a kernel launched once a step)
+            roof["traffic"] = rec.get("bytes_per_step", rec["bytes_per_launch"])
     return roof
 
 

@@ -16,6 +16,13 @@ HBM bytes per launch.  Each counter is scaled by the factor that makes the same
 counter read exactly right for the plain 256 MiB copy that
 `bench.py --copy-calibration` runs first (read 256 MiB, write 256 MiB), and the
 entry records a hash of the kernel sources so that stale figures are ignored.
+A kernel name launched n times a step (the per-projection MLP launches "up"
+five times, with different shapes) is summarised per launch position: the
+steps repeat one launch sequence, so position i of a step is every n-th
+dispatch of that name from the i-th on; each position's median over the
+steps is taken and the positions are added (bytes_per_step), and
+bytes_per_launch is that sum over n.  A name launched once a step reduces to
+the median over its dispatches.
 """
 from __future__ import annotations
 
@@ -63,11 +70,41 @@ def stats(csv_path: str, out: str, title: str, command: str) -> None:
 
 
 def _per_kernel(csv_path: str, counter: str):
-    vals = defaultdict(list)
+    """{kernel name: counter values in dispatch order}"""
+    rows = []
     for r in csv.DictReader(open(csv_path)):
         if r["Counter_Name"] == counter:
-            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    vals = defaultdict(list)
+    for _, k, v in sorted(rows):
+        vals[k].append(v)
     return vals
+
+
+def _per_short(vals):
+    """{short name: values in dispatch order} over this library's kernels"""
+    out = defaultdict(list)
+    for k, v in vals.items():
+        if short_name(k) != k:
+            out[short_name(k)].extend(v)
+    return out
+
+
+def _per_short_ordered(csv_path: str, counter: str):
+    rows = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and short_name(r["Kernel_Name"]) != r["Kernel_Name"]:
+            rows.append((int(r["Dispatch_Id"]), short_name(r["Kernel_Name"]), float(r["Counter_Value"])))
+    out = defaultdict(list)
+    for _, k, v in sorted(rows):
+        out[k].append(v)
+    return out
+
+
+def _per_step(values, steps: int) -> float:
+    """sum over launch positions of each position's median over the steps"""
+    n = max(1, len(values) // steps)
+    return sum(statistics.median(values[i::n]) for i in range(n)), n
 
 
 def traffic(fetch_csv: str, write_csv: str, workload: str, out: str, command: str) -> dict:
@@ -81,13 +118,14 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, out: str, command: st
     rec = json.load(open(out)) if os.path.exists(out) else {}
     h = source_hash()
     summary = {}
-    for k in fetch:
-        name = short_name(k)
-        if name == k:
-            continue
-        fb = statistics.median(fetch[k]) * 1024.0 * f_scale
-        wb = statistics.median(write.get(k, [0.0])) * 1024.0 * w_scale
-        rec[f"{workload}/{name}"] = {"bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+    sf, sw = _per_short_ordered(fetch_csv, "FETCH_SIZE"), _per_short_ordered(write_csv, "WRITE_SIZE")
+    steps = min(len(v) for v in sf.values())   # a name launched once a step sets the step count
+    for name in sf:
+        fpos, n = _per_step(sf[name], steps)
+        wpos, _ = _per_step(sw.get(name, [0.0] * len(sf[name])), steps)
+        fb, wb = fpos * 1024.0 * f_scale, wpos * 1024.0 * w_scale
+        rec[f"{workload}/{name}"] = {"bytes_per_launch": (fb + wb) / n, "bytes_per_step": fb + wb,
+                                     "launches_per_step": n, "fetch_bytes": fb / n, "write_bytes": wb / n,
                                      "fetch_scale": f_scale, "write_scale": w_scale, "source_hash": h,
                                      "command": command}
         summary[name] = (fb, wb)
