@@ -142,12 +142,17 @@ def mlp_kernel_work(wl, name: str):
                 e * (T * r + f * r + 4 * T * f) + e * (2 * T * r + 2 * d * r + (2 + res) * T * d) + 4 * T)
     if name == "fold_gamma":
         return 0.0, e * (2 * d * 2 * r + d)
-    if name == "wgrad_reduce":   # output layer's sums (no split tiles there), input layer's split tiles and dgamma
-        s_out = split_tiles(T, f, r, 1, 1, d, wl.dtype)
-        s_in = split_tiles(T, d, r, 2, 2, f, wl.dtype)
-        out_b = 4 * s_out * 256 * 256 if s_out else 4 * (r * d + f * r)
-        in_b = 4 * s_in * 256 * 256 + 4 * d * (-(-2 * r // 256) * 2 + 1) if s_in else 4 * (2 * r * f + d * 2 * r)
-        return 0.0, out_b + in_b
+    if name == "wgrad_reduce":   # each layer's reduction, where its plan has one
+        def red(dA_rows, g, n_up, dn, gamma):
+            cd = lambda a, b: -(-a // b)
+            tiles = n_up * cd(r, 256) * cd(dn, 256) + cd(dA_rows, 256) * cd(g * r, 256)
+            if tiles <= 256 and 8 * tiles >= 7 * 256:   # one token pass
+                return 0
+            st = split_tiles(T, dA_rows, r, g, n_up, dn, wl.dtype)
+            if st:
+                return 4 * st * 256 * 256 + (4 * dA_rows * (cd(g * r, 256) * 2 + 1) if gamma else 0)
+            return 4 * (n_up * r * dn + dA_rows * g * r)
+        return 0.0, red(f, 1, 1, d, False) + red(d, 2, 2, f, True)
     return 0.0, 0.0
 
 

@@ -1453,6 +1453,10 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up, int dn) {
   p.KS = cdiv(T, C::BK);
   const int64_t total = (int64_t)p.tiles * p.KS;
   p.nsplit = 1;
+  // Nearly one round of whole tiles (7/8 of the CUs or more): one token pass.
+  // Stream-K would spread the few idle CUs' share over every tile at the price
+  // of fp32 slots and a reduction (236 tiles: 578 + 35 us against ~450).
+  if (p.tiles <= kNumCu && 8 * p.tiles >= 7 * kNumCu) return p;
   if (Cfgs<E>::HAS_SKINNY && p.tiles < kNumCu && total >= 2 * kNumCu) {
     // stream-K: about one work-group per CU, at least 8 k steps each
     p.streamk = 1;
