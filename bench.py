@@ -68,7 +68,8 @@ def split_tiles(T, d, r, g, n_up, dn, dtype="bf16") -> int:
     tiles_b = n_up * cd(r, 256) * cd(dn, 256)
     tiles = tiles_b + cd(d, 256) * cd(g * r, 256)
     S = 512 - tiles
-    ok = tiles > 256 and 0 < S <= tiles_b and (tiles - S) % 8 == 0 and (2 * S) % 8 == 0 and cd(T, 64) >= 32
+    ok = (tiles > 256 and 0 < S <= tiles_b and tiles - S <= 256 and (tiles - S) % 8 == 0 and (2 * S) % 8 == 0
+          and cd(T, 64) >= 32)
     return S if ok else 0
 
 

@@ -1484,11 +1484,13 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up, int dn) {
   // Between one and two rounds of whole tiles: split just enough (dB) tiles in
   // two that the work-groups fill exactly two rounds, the whole tiles first
   // (one tile-time) and then the halves (half a tile-time), instead of
-  // splitting every tile and reducing all of dA and dB.
+  // splitting every tile and reducing all of dA and dB.  Only when the whole
+  // tiles fit in the first round (up to 1.5 rounds of tiles): beyond that the
+  // second round holds whole tiles too, and the split saves nothing.
   {
     const int S = 2 * kNumCu - p.tiles, U = p.tiles - S;
     const int tilesB = n_up * cdiv(r, C::BM) * cdiv(dn, C::BN);
-    if (Cfgs<E>::HAS_SKINNY && p.tiles > kNumCu && S > 0 && S <= tilesB && U % kNumXcd == 0 &&
+    if (Cfgs<E>::HAS_SKINNY && p.tiles > kNumCu && S > 0 && S <= tilesB && U <= kNumCu && U % kNumXcd == 0 &&
         (2 * S) % kNumXcd == 0 && p.KS >= 32) {
       p.nsplit = 2;
       p.split_tiles = S;
@@ -1497,9 +1499,12 @@ WgradPlan wgrad_plan(int T, int d, int r, int g, int n_up, int dn) {
     }
   }
   // token splits: aim for at least two waves of work-groups on 256 CUs, with
-  // >= 16 k steps per split
+  // >= 16 k steps per split, as long as doubling the splits shortens the
+  // schedule (rounds of work-groups times the split's share of a tile)
+  auto tile_times = [&](int sp) { return (double)cdiv((int64_t)p.tiles * sp, kNumCu) / sp; };
   int sp = 1;
-  while (p.tiles * sp < 2 * kNumCu && p.KS / (2 * sp) >= 16 && sp < 16) sp *= 2;
+  while (p.tiles * sp < 2 * kNumCu && p.KS / (2 * sp) >= 16 && sp < 16 && tile_times(2 * sp) < tile_times(sp))
+    sp *= 2;
   p.nsplit = sp;
   p.part_floats = sp > 1 ? (int64_t)sp * ((int64_t)n_up * r * dn + (int64_t)d * gr) : 0;
   return p;
