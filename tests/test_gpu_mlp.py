@@ -4,9 +4,9 @@ through the C ABI) with the CPU oracle (oracle/mlp.py).
 Small cases compare every output and gradient whole and span several tiles
 with ragged tails (T, and MLP widths f that leave a partial last column tile);
 the mid-size case has the full widths, so its weight gradients run the same
-plans as the full size (stream-K for the output layer, split tiles for the
-input layers); the full-size case compares sampled rows of out, the checkpoint
-and dx (rows are independent in all three).  Tolerances as for the block:
+plans as the full size (one token pass for the output layer's 236 tiles and
+the input layers' 472); the full-size case compares sampled rows of out, the
+checkpoint and dx (rows are independent in all three).  Tolerances as for the block:
 bf16 max|e| <= 1e-2 max|ref| and ||e||_F <= 5e-3 ||ref||_F; fp32 1e-5.
 """
 import sys
@@ -175,3 +175,32 @@ def test_mlp_full_size_sampled_rows():
     assert_close(host(g["dx"][ri]), rg["dx"], wl.dtype, "dx rows")
     for k in GRADS[1:]:
         assert np.all(np.isfinite(host(g[k]))), k
+
+
+def test_mlp_degenerate_rows():
+    """All-zero, constant and strongly scaled rows through the MLP, forward and
+    backward, against the oracle on the same bf16 values."""
+    from workloads import Tensor
+    wl = MlpWorkload("mlp_degenerate", T=260, d=256, f=448, r=64, dtype="bf16", residual=True)
+    _say("degenerate rows", wl)
+    inp = make_mlp_inputs(wl, seed=6)
+    xv = inp.x.v.copy()
+    xv[0] = 0.0
+    xv[100] = 2.0
+    xv[101:104] *= 1e3
+    xv[104:107] *= 1e-3
+    xv[-1] = 0.0
+    inp.x = Tensor(xv, wl.dtype)
+    dims = _dims(wl)
+    x = dev(inp.x)
+    w = _weights(inp)
+    out, h_in, h_out = rb.mlp_fwd(dims, x, *w, residual=x)
+    dout = dev(inp.dout)
+    g = rb.mlp_bwd(dims, x, *w, h_in, h_out, dout, dx_residual=dout)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_fwd(inp.x.v, *_wv(inp), wl.r, wl.eps, residual=inp.x.v)
+    assert_close(host(out), ref["out"], wl.dtype, "out")
+    assert_close(host(h_in), ref["h_in"], wl.dtype, "h_in")
+    rg = oracle.mlp_bwd(inp.x.v, *_wv(inp), inp.dout.v, wl.r, wl.eps, dx_residual=inp.dout.v)
+    for k in GRADS:
+        assert_close(host(g[k]), rg[k], wl.dtype, k)

@@ -591,3 +591,38 @@ def test_forward_up_many_tiles(wl):
     assert_close(host(h), ref["h"], wl.dtype, "h")
     for i, yi in enumerate(y):
         assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+
+
+def test_degenerate_rows():
+    """RMSNorm's degenerate rows through the whole block: all-zero rows (rstd =
+    eps^-1/2, h = 0), constant rows, rows scaled by 1e3 and 1e-3 (the statistic
+    spans 12 orders of magnitude), each against the oracle on the same bf16
+    values; forward and backward (a ragged T over several tiles)."""
+    from workloads import Tensor
+    wl = Workload("bf16_degenerate", 700, 512, 128, 3, "silu", "bf16")
+    _say("degenerate rows", wl)
+    inp = make_inputs(wl, seed=9)
+    xv = inp.x.v.copy()
+    xv[0] = 0.0
+    xv[5] = 0.0
+    xv[299] = 1.5
+    xv[300] = -0.25
+    xv[301:305] *= 1e3
+    xv[305:309] *= 1e-3
+    xv[-1] = 0.0
+    inp.x = Tensor(xv, wl.dtype)
+    dims, (x, gamma, A, B), y, h = _run_fwd(wl, inp)
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(h), ref["h"], wl.dtype, "h")
+    for i, yi in enumerate(y):
+        assert_close(host(yi), ref["y"][i], wl.dtype, f"y{i}")
+    g = rb.bwd(dims, x, gamma, A, B, h, [dev(t) for t in inp.dy])
+    torch.cuda.synchronize()
+    rb_ = oracle.block_bwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], [t.v for t in inp.dy],
+                           wl.r, wl.g, wl.act, wl.eps, wl.D)
+    for k in ("dx", "dgamma", "dA"):
+        assert_close(host(g[k]), rb_[k], wl.dtype, k)
+    for i in range(len(B)):
+        assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
+    # the zero rows' outputs: h = 0 exactly, y = SiLU(0) . B = 0 exactly
+    assert torch.count_nonzero(h[0]).item() == 0 and torch.count_nonzero(y[0][0]).item() == 0
