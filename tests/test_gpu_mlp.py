@@ -49,6 +49,8 @@ def _sample_rows(T, n=1024, seed=0):
 
 SMALL = [
     MlpWorkload("mlp_f32_tiny", T=130, d=128, f=192, r=64, dtype="f32"),
+    # fp32 over several 128 x 128 tiles in every GEMM, with the residual
+    MlpWorkload("mlp_f32_res", T=300, d=256, f=320, r=128, dtype="f32", residual=True),
     MlpWorkload("mlp_bf16_ragged", T=555, d=320, f=448, r=128, dtype="bf16"),
     MlpWorkload("mlp_bf16_res", T=300, d=256, f=704, r=64, dtype="bf16", residual=True),
     MlpWorkload("mlp_bf16_r192", T=777, d=512, f=576, r=192, dtype="bf16"),
