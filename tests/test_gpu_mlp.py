@@ -19,7 +19,7 @@ import oracle
 import rank_bottleneck_amd as rb
 from workloads import MLP_WORKLOADS, MlpWorkload, make_mlp_inputs
 
-from util import assert_close, dev, host
+from util import assert_close, dev, host, mlp_selection_case
 
 pytestmark = pytest.mark.gpu
 
@@ -206,3 +206,21 @@ def test_mlp_degenerate_rows():
     rg = oracle.mlp_bwd(inp.x.v, *_wv(inp), inp.dout.v, wl.r, wl.eps, dx_residual=inp.dout.v)
     for k in GRADS:
         assert_close(host(g[k]), rg[k], wl.dtype, k)
+
+
+def test_mlp_selection_case_exact():
+    """x in {+-1}, gamma = 1, eps = 0, selection weights (the oracle's
+    closed-form pin): every intermediate is a selection, so out equals
+    SiLU(+-1) * (+-1) rounded once to the storage type; exact in bf16, within
+    2 ulp of the device exp in fp32."""
+    T, d, f, r = 300, 256, 320, 64
+    x, gamma, A_in, B_g, B_u, A_o, B_o, *_ = mlp_selection_case(T, d, f, r, seed=3)
+    ref = oracle.mlp_fwd(x, gamma, A_in, B_g, B_u, A_o, B_o, r, 0.0)["out"]
+    for dtype, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        t = lambda a: torch.tensor(a, dtype=tdt, device="cuda").contiguous()
+        dims = rb.make_mlp_dims(T, d, f, r, dtype, 0.0)
+        out, _, _ = rb.mlp_fwd(dims, t(x), t(gamma), t(A_in), t(B_g), t(B_u), t(A_o), t(B_o))
+        torch.cuda.synchronize()
+        exp = torch.tensor(ref, dtype=tdt).double().numpy()
+        tol = 0.0 if dtype == "bf16" else 2.5e-7
+        assert np.max(np.abs(host(out) - exp)) <= tol, (dtype, np.max(np.abs(host(out) - exp)))

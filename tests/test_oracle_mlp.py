@@ -13,6 +13,8 @@ import torch
 import oracle
 from oracle import brute
 
+from util import mlp_selection_case
+
 EPS = 1e-6
 
 
@@ -189,3 +191,22 @@ def test_unmutated_mlp_oracle_passes_compact_pins():
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_mlp_pins_catch_planted_mistake(name):
     assert not _pins_hold(_load_mutant(name))
+
+
+def test_mlp_selection_closed_form():
+    """With selection weights every intermediate is a selection, so
+    out[t, sel_o[k]] = SiLU(x[t, sel_g[k]]) * x[t, sel_u[k]], which takes the
+    values e/(1+e), -e/(1+e), -1/(1+e), 1/(1+e) (SiLU(1) = e/(1+e), SiLU(-1) =
+    -1/(1+e)); every other entry of out is 0."""
+    import math
+    T, d, f, r = 5, 8, 6, 3
+    x, gamma, A_in, B_g, B_u, A_o, B_o, sel_g, sel_u, sel_o = mlp_selection_case(T, d, f, r)
+    silu = {1.0: math.e / (1.0 + math.e), -1.0: -1.0 / (1.0 + math.e)}
+    want = np.zeros((T, d))
+    for t in range(T):
+        for k in range(r):
+            want[t, sel_o[k]] = silu[x[t, sel_g[k]]] * x[t, sel_u[k]]
+    got = oracle.mlp_fwd(x, gamma, A_in, B_g, B_u, A_o, B_o, r, 0.0)["out"]
+    assert np.max(np.abs(got - want)) <= 2e-16     # exp() may differ by an ulp
+    assert set(np.round(np.abs(want[want != 0]), 12)) <= {round(math.e / (1 + math.e), 12),
+                                                          round(1 / (1 + math.e), 12)}

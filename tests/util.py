@@ -1,5 +1,6 @@
-"""Helpers shared by the tests: moving seeded inputs to the GPU and the
-tolerance check.  Holds none of the block's arithmetic."""
+"""Helpers shared by the tests: moving seeded inputs to the GPU, the
+tolerance check and the MLP's selection-case inputs.  Holds none of the
+method's arithmetic."""
 from __future__ import annotations
 
 import numpy as np
@@ -37,3 +38,25 @@ def assert_close(got, ref, dtype: str, what: str = ""):
     tmax, tfr = TOL[dtype]
     assert mx <= tmax and fr <= tfr, f"{what}: max rel {mx:.3e} (<= {tmax}), frob rel {fr:.3e} (<= {tfr})"
     return mx, fr
+
+
+def mlp_selection_case(T=5, d=8, f=6, r=3, seed=0):
+    """Inputs of the per-projection MLP's selection case (arrays only): x in
+    {+-1}, gamma = 1; one-hot A_in columns select coordinates sel_g (gate half)
+    and sel_u (up half); B_g = B_u = [I_r | 0]; A_o = [I_r ; 0]; B_o sends rank
+    index k to coordinate sel_o[k].  Returns (x, gamma, A_in, B_g, B_u, A_o,
+    B_o, sel_g, sel_u, sel_o)."""
+    rng = np.random.default_rng(seed)
+    x = np.where(rng.random((T, d)) < 0.5, -1.0, 1.0)
+    sel_g, sel_u, sel_o = rng.permutation(d)[:r], rng.permutation(d)[:r], rng.permutation(d)[:r]
+    A_in = np.zeros((d, 2 * r))
+    A_in[sel_g, np.arange(r)] = 1.0
+    A_in[sel_u, r + np.arange(r)] = 1.0
+    B_g = np.zeros((r, f))
+    B_g[np.arange(r), np.arange(r)] = 1.0
+    B_u = B_g.copy()
+    A_o = np.zeros((f, r))
+    A_o[np.arange(r), np.arange(r)] = 1.0
+    B_o = np.zeros((r, d))
+    B_o[np.arange(r), sel_o] = 1.0
+    return x, np.ones(d), A_in, B_g, B_u, A_o, B_o, sel_g, sel_u, sel_o
