@@ -5,7 +5,8 @@
            --workload W --out profiles/traffic.json --command C
     python -m rank_bottleneck_amd.profile_summary mfma <counter_collection.csv> <out.md> --title T --command C
 
-`mfma` summarises one `--pmc MfmaUtil MfmaFlopsBF16` pass per kernel: the MFMA
+`mfma` summarises one `--pmc MfmaUtil MfmaFlopsBF16` pass per kernel (per launch
+position within a step for a kernel launched several times a step): the MFMA
 busy fraction (MFMA busy cycles over active cycles times SIMDs), the bf16 MFMA
 FLOPs the hardware counted (MFMA ops x 512), the rate those FLOPs give over the
 dispatch's duration, and the shader clock that rate and busy fraction imply
@@ -134,17 +135,33 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, out: str, command: st
 
 
 def mfma(csv_path: str, out: str, title: str, command: str) -> None:
-    util, flops, dur = defaultdict(list), defaultdict(list), defaultdict(list)
+    # per short name, in dispatch order; a name launched n times a step is
+    # reported per launch position (name#1 .. name#n), as in `traffic`
+    rows = []
     for r in csv.DictReader(open(csv_path)):
         k = short_name(r["Kernel_Name"])
         if k == r["Kernel_Name"]:
             continue
-        v = float(r["Counter_Value"])
-        if r["Counter_Name"] == "MfmaUtil":
-            util[k].append(v)
-            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
-        elif r["Counter_Name"] == "MfmaFlopsBF16":
-            flops[k].append(v)
+        rows.append((int(r["Dispatch_Id"]), k, r["Counter_Name"], float(r["Counter_Value"]),
+                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9))
+    seq = defaultdict(list)   # name -> [(dispatch, {counter: value}, duration)]
+    by_disp = {}
+    for disp, k, cname, v, t in sorted(rows):
+        if disp not in by_disp:
+            by_disp[disp] = (k, {}, t)
+            seq[k].append(by_disp[disp])
+        by_disp[disp][1][cname] = v
+    steps = min(len(v) for v in seq.values()) if seq else 1
+    util, flops, dur = defaultdict(list), defaultdict(list), defaultdict(list)
+    for k, items in seq.items():
+        n = max(1, len(items) // steps)
+        for i, (_, vals, t) in enumerate(items):
+            key = k if n == 1 else f"{k}#{i % n + 1}"
+            if "MfmaUtil" in vals:
+                util[key].append(vals["MfmaUtil"])
+                dur[key].append(t)
+            if "MfmaFlopsBF16" in vals:
+                flops[key].append(vals["MfmaFlopsBF16"])
     with open(out, "w") as f:
         f.write(f"# {title}\n\nCommand (repository root, one MI355X):\n\n```\n{command}\n```\n\n")
         f.write("Medians over the profiled launches (kernels run one at a time under counter collection).\n\n")
