@@ -39,3 +39,19 @@ def test_recipe_moments():
     assert abs((inp.gamma.v - 1.0).std() - np.sqrt(0.1)) < 0.03
     assert inp.x.store.dtype == np.uint16 and len(inp.B) == 3 and len(inp.dy) == 3
     assert WORKLOADS["swiglu_mlp"].n_up == 1
+
+
+def test_mlp_inputs_deterministic_and_recipe():
+    from workloads import MLP_WORKLOADS, make_mlp_inputs
+    wl = MLP_WORKLOADS["lowrank_mlp"].replace(T=256, d=512, f=1024, r=128)
+    a, b, c = make_mlp_inputs(wl, 0), make_mlp_inputs(wl, 0), make_mlp_inputs(wl, 0, rows=33)
+    for k in ("x", "gamma", "A_in", "B_g", "B_u", "A_o", "B_o", "dout"):
+        assert np.array_equal(getattr(a, k).v, getattr(b, k).v), k
+    assert np.array_equal(a.x.v[:33], c.x.v) and np.array_equal(a.dout.v[:33], c.dout.v)
+    assert np.array_equal(a.A_o.v, c.A_o.v)
+    assert a.A_in.shape == (512, 256) and a.B_g.shape == (128, 1024) and a.A_o.shape == (1024, 128)
+    assert a.B_o.shape == (128, 512) and a.x.store.dtype == np.uint16
+    assert abs(a.A_in.v.std() * np.sqrt(512) - 1.0) < 0.02
+    assert abs(a.A_o.v.std() * np.sqrt(1024) - 1.0) < 0.02
+    assert abs(a.B_g.v.std() * np.sqrt(128) - 1.0) < 0.02
+    assert not np.array_equal(make_mlp_inputs(wl, 1).x.v, a.x.v)
