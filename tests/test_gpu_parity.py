@@ -626,3 +626,53 @@ def test_degenerate_rows():
         assert_close(host(g["dB"][i]), rb_["dB"][i], wl.dtype, f"dB{i}")
     # the zero rows' outputs: h = 0 exactly, y = SiLU(0) . B = 0 exactly
     assert torch.count_nonzero(h[0]).item() == 0 and torch.count_nonzero(y[0][0]).item() == 0
+
+
+def test_graph_capture_replays_match_eager():
+    """The library allocates nothing and records no memsets, so its launches can
+    be captured in a HIP graph: one fwd+bwd step (the benchmark's calls, with
+    the allocation-free forward) captured once and replayed four times, with
+    eager work and synchronisation between the replays; every replay equals the
+    eager step bit for bit (same kernels, same order)."""
+    wl = Workload("bf16_graph", 1100, 512, 256, 3, "silu", "bf16")
+    _say("graph capture", wl)
+    inp = make_inputs(wl, seed=12)
+    dims = _dims(wl)
+    x, gamma, A = dev(inp.x), dev(inp.gamma), dev(inp.A)
+    B = [dev(b) for b in inp.B]
+    dy = [dev(t) for t in inp.dy]
+    dt = torch.bfloat16
+    y = [torch.empty(wl.T, wl.d, dtype=dt, device="cuda") for _ in range(3)]
+    h = torch.empty(wl.T, wl.g * wl.r, dtype=dt, device="cuda")
+    rstd = torch.empty(wl.T, dtype=torch.float32, device="cuda")
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    dgamma = torch.empty(wl.d, dtype=torch.float32, device="cuda")
+    dA = torch.empty(wl.d, wl.g * wl.r, dtype=torch.float32, device="cuda")
+    dB = [torch.empty(wl.r, wl.d, dtype=torch.float32, device="cuda") for _ in range(3)]
+    wsb = rb.workspace(dims, True)
+
+    def step():
+        rb.lr_block_fwd_noalloc(dims, x, gamma, A, B, y, h, rstd)
+        rb.lr_block_bwd_rstd(dims, x, gamma, A, B, h, rstd, dy, dx, dgamma, dA, dB, wsb)
+
+    outs = lambda: [t.clone() for t in [*y, h, rstd, dx, dgamma, dA, *dB]]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                      # the first call looks the scratch address up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = outs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in [*y, h, rstd, dx, dgamma, dA, *dB]:
+            t.fill_(float("nan"))   # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), eager):
+            assert torch.equal(a, b), f"replay {i}"
+    ref = oracle.block_fwd(inp.x.v, inp.gamma.v, inp.A.v, [b.v for b in inp.B], wl.r, wl.g, wl.act, wl.eps, wl.D)
+    assert_close(host(y[0]), ref["y"][0], wl.dtype, "y0 (graph)")
